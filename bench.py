@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Routed tokens/s of one OmniMoE routed atomic-expert layer (forward) on one
+MI355X, with the executor's HBM roofline fraction and the CPU oracle's rate.
+
+A step is one pass of the whole path on one batch: router logits ->
+product top-K + gates -> expert-centric schedule -> expert-centric execute,
+all four C-ABI calls enqueued back to back on one stream, inputs resident in
+HBM, every output buffer allocated before timing.
+
+    python bench.py [--steps 50] [--warmup 5] [--workload large]
+
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/sec per atomic-expert layer at 1 GPU; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+EXEC_SRC = os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", "execute.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def exec_src_hash():
+    with open(EXEC_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """Counter-derived HBM bytes per executor launch, if taken on this kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m = re.search(r"traffic_record:\s*(\{.*\})", txt)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != workload or rec.get("execute_hip_sha256_16") != exec_src_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, target_s):
+    """The oracle, untuned, on the first S tokens of the workload."""
+    from oracle import omni_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([1] + [p.get("num_threads", 1) for p in threadpool_info()])
+    except Exception:  # pragma: no cover
+        cores = 1
+
+    def run(S):
+        xs = inp["x"][:S]
+        t0 = time.perf_counter()
+        a, b = O.router_logp(xs, inp["wr"], inp["wc"], inp["row_bias"], inp["col_bias"])
+        idx, score, gate, _, _ = O.product_topk(a, b, wl.kprime, wl.K)
+        O.build_schedule(idx, gate, wl.N, wl.B)
+        O.atomic_forward(xs, inp["w"], inp["v"], idx, gate)
+        return time.perf_counter() - t0
+
+    s0 = min(wl.L, 16)
+    t0 = run(s0)
+    S = int(max(s0, min(wl.L, s0 * target_s / max(t0, 1e-3))))
+    t = run(S)
+    return {"value": S / t, "unit": "routed tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of {wl.L} tokens of the {wl.name} workload, whole path "
+                      f"(router, top-K + gates, schedule, token-centric y) in {t:.1f}s; "
+                      f"numpy float64, BLAS threads={cores}, the rest single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the layer's multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from cartesian_routed_atomic_amd import binding as B
+    from synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    say(f"[bench] workload {wl.name}: L={wl.L} d={wl.d} N={wl.N} ({wl.Nr}x{wl.Nc}) "
+        f"k'={wl.kprime} K={wl.K} B={wl.B} {wl.dtype}")
+    t0 = time.time()
+    inp = make_inputs(wl)
+    say(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    t = {k: to_dev(v) for k, v in inp.items()}
+    x, wr, wc, w, v = t["x"], t["wr"], t["wc"], t["w"], t["v"]
+    rb, cb = t["row_bias"], t["col_bias"]
+    L, K = wl.L, wl.K
+    dev = "cuda"
+    a = torch.empty((L, wl.Nr), dtype=torch.float32, device=dev)
+    b = torch.empty((L, wl.Nc), dtype=torch.float32, device=dev)
+    sel = {"expert_idx": torch.empty((L, K), dtype=torch.int32, device=dev),
+           "score": torch.empty((L, K), dtype=torch.float32, device=dev),
+           "gate": torch.empty((L, K), dtype=torch.float32, device=dev)}
+    sched = B.alloc_schedule(L, K, wl.N, wl.B, dev, with_index=False)
+    y = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
+    y2 = torch.zeros_like(y)
+
+    def stage_router():
+        B.router_logits(x, wr, wc, rb, cb, row_logp=a, col_logp=b)
+
+    def stage_topk():
+        B.product_topk(a, b, wl.kprime, K, want_sel=False, out=sel)
+
+    def stage_schedule():
+        B.schedule_tasks(sel["expert_idx"], sel["gate"], wl.N, wl.B, sched=sched)
+
+    def stage_execute():
+        B.atomic_forward(x, w, v, sched, y=y)
+
+    def step():
+        stage_router()
+        stage_topk()
+        stage_schedule()
+        stage_execute()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    ms = 1e3 * elapsed / args.steps
+    say(f"[bench] {args.steps} steps in {elapsed:.3f}s: {ms:.3f} ms/step")
+
+    # per-stage times (HIP events on the stream the kernels run on)
+    def ev_time(fn, reps=10):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / reps
+
+    stages = {"router": ev_time(stage_router), "topk": ev_time(stage_topk),
+              "schedule": ev_time(stage_schedule), "execute": ev_time(stage_execute)}
+    # the executor kernel alone: accumulate mode skips the y clear
+    exec_ms = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y2, accumulate=True), reps=20)
+    counts = sched.counts.cpu().tolist()
+    n_active, n_groups = int(counts[0]), int(counts[1])
+    s = wl.elem_bytes
+    M = L * K
+    bytes_alg = 2 * wl.d * s * n_active + L * wl.d * s + 4 * L * wl.d + 12 * M
+    achieved = bytes_alg / (exec_ms * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+    router_flop = 2.0 * L * wl.d * (wl.Nr + wl.Nc)
+    router_tflops = router_flop / (stages["router"] * 1e-3) / 1e12
+    say(f"[bench] stages ms {json.dumps({k: round(v4, 4) for k, v4 in stages.items()})}; "
+        f"executor kernel {exec_ms:.4f} ms, {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of HBM); n_active={n_active} "
+        f"n_groups={n_groups}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        say("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+        say(f"[bench] oracle {cpu['value']:.1f} tokens/s ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": L / (ms * 1e-3),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded Gaussian x ~ N(0,1), W, V, Wr, Wc ~ N(0,1/d), bf16",
+        "config": {"workload": wl.name, "L": L, "d": wl.d, "N": wl.N,
+                   "grid": [wl.Nr, wl.Nc], "kprime": wl.kprime, "K": K, "B": wl.B,
+                   "zipf_s": wl.zipf_s},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "atomic_forward_kernel", "bytes_alg": bytes_alg,
+                     "kernel_ms": exec_ms},
+        "router_mfma": {"achieved": router_tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": router_tflops / MFMA_BF16_TFLOPS,
+                        "note": "router call = MFMA GEMM + log-softmax kernel"},
+        "stages_ms": stages,
+        "n_active": n_active,
+        "expert_usage": n_active / wl.N,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,257 @@
+"""Thin Python binding of libomni.so (ctypes).
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is missing the import fails; there is no other execution path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
+
+OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
+OMNI_F32, OMNI_BF16 = 0, 1
+
+# Every symbol the header declares (checked by the CPU test suite).
+EXPORTS = (
+    "omni_abi_version", "omni_status_string", "omni_router_logits",
+    "omni_product_topk_workspace", "omni_product_topk", "omni_schedule_max_groups",
+    "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_workspace",
+    "omni_atomic_forward",
+)
+
+
+class OmniError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed: {msg} (status {code})")
+        self.code = code
+
+
+class ScheduleStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("counts", "active", "group_offsets", "task_token", "task_expert",
+                 "task_gate", "task_index")]
+
+
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "omni_abi_version": (_i, []),
+    "omni_status_string": (ctypes.c_char_p, [_i]),
+    "omni_router_logits": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "omni_product_topk_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "omni_product_topk": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _sz, _vp]),
+    "omni_schedule_max_groups": (_i, [_i, _i, _i, _i]),
+    "omni_schedule_workspace": (_sz, [_i, _i, _i, _i]),
+    "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),
+                                 _vp, _sz, _vp]),
+    "omni_atomic_forward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "omni_atomic_forward": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                                 ctypes.POINTER(ScheduleStruct), _vp, _i, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libomni.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with "
+                              f"`python -m cartesian_routed_atomic_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(fn, code):
+    if code != OMNI_OK:
+        msg = lib().omni_status_string(code).decode()
+        raise OmniError(fn, code, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return OMNI_BF16
+    if t.dtype == torch.float32:
+        return OMNI_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _req(t, name, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ------------------------------------------------------------------ calls
+
+
+def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None, row_logp=None,
+                  col_logp=None, stream=None):
+    """omni_router_logits: returns (row_logp [L,Nr], col_logp [L,Nc]) float32."""
+    L, d = x.shape
+    Nr, Nc = wr_t.shape[0], wc_t.shape[0]
+    _req(x, "x")
+    _req(wr_t, "wr_t", x.dtype, (Nr, d))
+    _req(wc_t, "wc_t", x.dtype, (Nc, d))
+    for b, n, nm in ((row_bias, Nr, "row_bias"), (col_bias, Nc, "col_bias")):
+        if b is not None:
+            _req(b, nm, torch.float32, (n,))
+    if row_logp is None:
+        row_logp = torch.empty((L, Nr), dtype=torch.float32, device=x.device)
+    if col_logp is None:
+        col_logp = torch.empty((L, Nc), dtype=torch.float32, device=x.device)
+    _req(row_logp, "row_logp", torch.float32, (L, Nr))
+    _req(col_logp, "col_logp", torch.float32, (L, Nc))
+    _check("omni_router_logits", lib().omni_router_logits(
+        _dtype_code(x), L, d, Nr, Nc, _ptr(x), _ptr(wr_t), _ptr(wc_t), _ptr(row_bias),
+        _ptr(col_bias), _ptr(row_logp), _ptr(col_logp), _stream(stream)))
+    return row_logp, col_logp
+
+
+def product_topk(row_logp, col_logp, kprime, K, want_sel=True, out=None, stream=None):
+    """omni_product_topk: returns dict expert_idx, score, gate (+ row_sel, col_sel)."""
+    L, Nr = row_logp.shape
+    Nc = col_logp.shape[1]
+    _req(row_logp, "row_logp", torch.float32)
+    _req(col_logp, "col_logp", torch.float32, (L, Nc))
+    dev = row_logp.device
+    o = out or {}
+    idx = o.get("expert_idx")
+    if idx is None:
+        idx = torch.empty((L, K), dtype=torch.int32, device=dev)
+    score = o.get("score")
+    if score is None:
+        score = torch.empty((L, K), dtype=torch.float32, device=dev)
+    gate = o.get("gate")
+    if gate is None:
+        gate = torch.empty((L, K), dtype=torch.float32, device=dev)
+    rsel = csel = None
+    if want_sel:
+        rsel = o.get("row_sel")
+        if rsel is None:
+            rsel = torch.empty((L, kprime), dtype=torch.int32, device=dev)
+        csel = o.get("col_sel")
+        if csel is None:
+            csel = torch.empty((L, kprime), dtype=torch.int32, device=dev)
+    nws = lib().omni_product_topk_workspace(L, Nr, Nc, kprime, K)
+    ws = o.get("workspace")
+    if nws and (ws is None or ws.numel() < nws):
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check("omni_product_topk", lib().omni_product_topk(
+        L, Nr, Nc, kprime, K, _ptr(row_logp), _ptr(col_logp), _ptr(idx), _ptr(score),
+        _ptr(gate), _ptr(rsel), _ptr(csel), _ptr(ws), nws, _stream(stream)))
+    return {"expert_idx": idx, "score": score, "gate": gate, "row_sel": rsel, "col_sel": csel,
+            "workspace": ws}
+
+
+@dataclass
+class Schedule:
+    L: int
+    K: int
+    N: int
+    B: int
+    counts: torch.Tensor
+    active: torch.Tensor
+    group_offsets: torch.Tensor
+    task_token: torch.Tensor
+    task_expert: torch.Tensor
+    task_gate: torch.Tensor
+    task_index: torch.Tensor | None
+    workspace: torch.Tensor | None
+
+    def struct(self):
+        return ScheduleStruct(*(None if t is None else t.data_ptr() for t in (
+            self.counts, self.active, self.group_offsets, self.task_token, self.task_expert,
+            self.task_gate, self.task_index)))
+
+
+def max_groups(L, K, N, B):
+    return lib().omni_schedule_max_groups(L, K, N, B)
+
+
+def alloc_schedule(L, K, N, B, device, with_index=True):
+    """Device buffers for a schedule of L*K tasks (and its workspace)."""
+    M = L * K
+    G = max_groups(L, K, N, B)
+    nws = lib().omni_schedule_workspace(L, K, N, B)
+    i32 = dict(dtype=torch.int32, device=device)
+    return Schedule(L, K, N, B,
+                    counts=torch.zeros(2, **i32),
+                    active=torch.empty(max(1, min(N, M)), **i32),
+                    group_offsets=torch.empty(G + 1, **i32),
+                    task_token=torch.empty(max(1, M), **i32),
+                    task_expert=torch.empty(max(1, M), **i32),
+                    task_gate=torch.empty(max(1, M), dtype=torch.float32, device=device),
+                    task_index=torch.empty(max(1, M), **i32) if with_index else None,
+                    workspace=torch.empty(max(1, nws), dtype=torch.uint8, device=device))
+
+
+def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None):
+    """omni_schedule_tasks: returns a Schedule of device tensors."""
+    L, K = expert_idx.shape
+    _req(expert_idx, "expert_idx", torch.int32)
+    _req(gate, "gate", torch.float32, (L, K))
+    if sched is None:
+        sched = alloc_schedule(L, K, N, B, expert_idx.device)
+    st = sched.struct()
+    ws = sched.workspace
+    _check("omni_schedule_tasks", lib().omni_schedule_tasks(
+        L, K, N, B, _ptr(expert_idx), _ptr(gate), ctypes.byref(st), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
+    return sched
+
+
+def atomic_forward(x, w, v, sched, y=None, accumulate=False, stream=None):
+    """omni_atomic_forward: returns y [L, d] float32 (y += routed if accumulate)."""
+    L, d = x.shape
+    N = w.shape[0]
+    _req(x, "x")
+    _req(w, "w", x.dtype, (N, d))
+    _req(v, "v", x.dtype, (N, d))
+    if y is None:
+        y = torch.empty((L, d), dtype=torch.float32, device=x.device)
+    _req(y, "y", torch.float32, (L, d))
+    st = sched.struct()
+    nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B)
+    ws = torch.empty(nws, dtype=torch.uint8, device=x.device) if nws else None
+    _check("omni_atomic_forward", lib().omni_atomic_forward(
+        _dtype_code(x), L, d, N, sched.K, sched.B, _ptr(x), _ptr(w), _ptr(v),
+        ctypes.byref(st), _ptr(y), int(bool(accumulate)), _ptr(ws), nws, _stream(stream)))
+    return y
+
+
+def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, stream=None):
+    """The four calls back to back on one stream; returns every intermediate."""
+    a, b = router_logits(x, wr_t, wc_t, row_bias, col_bias, stream=stream)
+    sel = product_topk(a, b, kprime, K, stream=stream)
+    N = wr_t.shape[0] * wc_t.shape[0]
+    sched = schedule_tasks(sel["expert_idx"], sel["gate"], N, B, stream=stream)
+    y = atomic_forward(x, w, v, sched, stream=stream)
+    return {"row_logp": a, "col_logp": b, **sel, "schedule": sched, "y": y}

@@ -1,0 +1,168 @@
+// C ABI of the routed atomic-expert layer: argument validation, workspace
+// sizing and dispatch to the gfx950 kernels.  Every check runs on the host
+// before anything is enqueued; nothing here allocates or synchronises.
+#include <stdint.h>
+
+#include "../../include/omni.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+bool fits_i32(long long v) { return v >= 0 && v < (1ll << 31); }
+
+omni_status hip_status(hipError_t e) { return e == hipSuccess ? OMNI_OK : OMNI_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int omni_abi_version(void) { return kAbiVersion; }
+
+const char* omni_status_string(omni_status s) {
+  switch (s) {
+    case OMNI_OK: return "ok";
+    case OMNI_ERR_INVALID_ARG: return "invalid argument";
+    case OMNI_ERR_WORKSPACE: return "workspace missing or too small";
+    case OMNI_ERR_UNSUPPORTED: return "shape or type not covered by the kernels";
+    case OMNI_ERR_HIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc, const void* x,
+                               const void* wr_t, const void* wc_t, const float* row_bias,
+                               const float* col_bias, float* row_logp, float* col_logp,
+                               hipStream_t stream) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
+  if (L < 0 || d < 1 || Nr < 1 || Nc < 1) return OMNI_ERR_INVALID_ARG;
+  if (!wr_t || !wc_t) return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && (!x || !row_logp || !col_logp)) return OMNI_ERR_INVALID_ARG;
+  if (!fits_i32(static_cast<long long>(L) * d) || !fits_i32(static_cast<long long>(L) * Nr) ||
+      !fits_i32(static_cast<long long>(L) * Nc) ||
+      !fits_i32(static_cast<long long>(Nr + static_cast<long long>(Nc)) * d) ||
+      !fits_i32(2ll * L))
+    return OMNI_ERR_UNSUPPORTED;
+  if ((L > 0 && !aligned16(x)) || !aligned16(wr_t) || !aligned16(wc_t))
+    return OMNI_ERR_INVALID_ARG;
+  if (dt == OMNI_BF16 && d % 8 != 0) return OMNI_ERR_UNSUPPORTED;
+  if (dt == OMNI_F32 && d % 4 != 0) return OMNI_ERR_UNSUPPORTED;
+  if (L == 0) return OMNI_OK;
+  hipError_t e;
+  if (dt == OMNI_BF16)
+    e = omni::launch_router_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr_t),
+                                 static_cast<const uint16_t*>(wc_t), row_bias, col_bias, row_logp,
+                                 col_logp, L, d, Nr, Nc, stream);
+  else
+    e = omni::launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(wr_t),
+                                static_cast<const float*>(wc_t), row_bias, col_bias, row_logp,
+                                col_logp, L, d, Nr, Nc, stream);
+  if (e != hipSuccess) return OMNI_ERR_HIP;
+  return hip_status(omni::launch_log_softmax(row_logp, col_logp, L, Nr, Nc, stream));
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace of omni_product_topk: a tie flag per token, then room for the
+// per-axis lists when the caller does not ask for them.
+size_t omni_product_topk_workspace(int L, int Nr, int Nc, int kprime, int K) {
+  (void)Nr; (void)Nc; (void)K;
+  if (L <= 0 || kprime < 1) return 0;
+  return align256(static_cast<size_t>(L) * 4) +
+         2 * align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
+}
+
+omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const float* row_logp,
+                              const float* col_logp, int32_t* expert_idx, float* score,
+                              float* gate, int32_t* row_sel, int32_t* col_sel, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (L < 0 || Nr < 1 || Nc < 1) return OMNI_ERR_INVALID_ARG;
+  if (kprime < 1 || kprime > Nr || kprime > Nc) return OMNI_ERR_INVALID_ARG;
+  if (K < 1 || static_cast<long long>(K) > static_cast<long long>(kprime) * kprime)
+    return OMNI_ERR_INVALID_ARG;
+  if (!fits_i32(static_cast<long long>(Nr) * Nc)) return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && (!row_logp || !col_logp || !expert_idx || !score || !gate))
+    return OMNI_ERR_INVALID_ARG;
+  if (kprime > 64 || K > 64 || Nr > 4096 || Nc > 4096) return OMNI_ERR_UNSUPPORTED;
+  if (!fits_i32(static_cast<long long>(L) * Nr) || !fits_i32(static_cast<long long>(L) * Nc) ||
+      !fits_i32(static_cast<long long>(L) * K) || !fits_i32(static_cast<long long>(L) * kprime))
+    return OMNI_ERR_UNSUPPORTED;
+  if (L == 0) return OMNI_OK;
+  const size_t need = omni_product_topk_workspace(L, Nr, Nc, kprime, K);
+  if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  int32_t* flags = reinterpret_cast<int32_t*>(base);
+  const size_t o1 = align256(static_cast<size_t>(L) * 4);
+  const size_t o2 = o1 + align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
+  int32_t* rsel = row_sel ? row_sel : reinterpret_cast<int32_t*>(base + o1);
+  int32_t* csel = col_sel ? col_sel : reinterpret_cast<int32_t*>(base + o2);
+  return hip_status(omni::launch_product_topk(row_logp, col_logp, L, Nr, Nc, kprime, K,
+                                              expert_idx, score, gate, rsel, csel, flags,
+                                              stream));
+}
+
+int omni_schedule_max_groups(int L, int K, int N, int B) {
+  if (L < 0 || K < 1 || N < 1 || B < 1) return 0;
+  const long long M = static_cast<long long>(L) * K;
+  const long long mn = M < N ? M : N;
+  return static_cast<int>((mn + B - 1) / B);
+}
+
+static bool schedule_args_ok(int L, int K, int N, int B) {
+  return L >= 0 && K >= 1 && N >= 1 && B >= 1 && fits_i32(static_cast<long long>(L) * K);
+}
+
+size_t omni_schedule_workspace(int L, int K, int N, int B) {
+  if (!schedule_args_ok(L, K, N, B)) return 0;
+  return omni::schedule_ws_layout(L, K, N, B).bytes;
+}
+
+omni_status omni_schedule_tasks(int L, int K, int N, int B, const int32_t* expert_idx,
+                                const float* gate, const omni_schedule* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (!schedule_args_ok(L, K, N, B)) return OMNI_ERR_INVALID_ARG;
+  if (!out || !out->counts || !out->group_offsets) return OMNI_ERR_INVALID_ARG;
+  const long long M = static_cast<long long>(L) * K;
+  if (M > 0 && (!expert_idx || !gate || !out->active || !out->task_token || !out->task_expert ||
+                !out->task_gate))
+    return OMNI_ERR_INVALID_ARG;
+  const size_t need = omni_schedule_workspace(L, K, N, B);
+  if (M > 0 && (!ws || ws_bytes < need)) return OMNI_ERR_WORKSPACE;
+  if (M > 0 && !aligned256(ws)) return OMNI_ERR_WORKSPACE;
+  return hip_status(omni::launch_schedule(L, K, N, B, expert_idx, gate, out->counts, out->active,
+                                          out->group_offsets, out->task_token, out->task_expert,
+                                          out->task_gate, out->task_index, ws, stream));
+}
+
+size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B) {
+  (void)dt; (void)L; (void)d; (void)N; (void)K; (void)B;
+  return 0;
+}
+
+omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B, const void* x,
+                                const void* w, const void* v, const omni_schedule* sched,
+                                float* y, int accumulate, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
+  if (!schedule_args_ok(L, K, N, B) || d < 1) return OMNI_ERR_INVALID_ARG;
+  if (!w || !v || !sched) return OMNI_ERR_INVALID_ARG;
+  const long long M = static_cast<long long>(L) * K;
+  if (L > 0 && (!x || !y)) return OMNI_ERR_INVALID_ARG;
+  if (M > 0 && (!sched->task_token || !sched->task_expert || !sched->task_gate))
+    return OMNI_ERR_INVALID_ARG;
+  if (d < 64 || d > 4096 || (d & (d - 1)) != 0) return OMNI_ERR_UNSUPPORTED;
+  if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(v)) return OMNI_ERR_INVALID_ARG;
+  if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;
+  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
+  if (need > 0 && (!ws || ws_bytes < need)) return OMNI_ERR_WORKSPACE;
+  (void)ws;
+  if (L == 0) return OMNI_OK;
+  return hip_status(omni::launch_atomic_forward(dt == OMNI_BF16, L, d, N, static_cast<int>(M), x, w,
+                                                v, sched->task_token, sched->task_expert,
+                                                sched->task_gate, y, accumulate != 0, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal host-side launch interface between the C ABI (api.hip) and the
+// kernel files.  Every function enqueues on `s` and returns the launch error.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace omni {
+
+// router.hip
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
+                              const float* rb, const float* cb, float* zr, float* zc,
+                              int L, int d, int Nr, int Nc, hipStream_t s);
+hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
+                             const float* rb, const float* cb, float* zr, float* zc,
+                             int L, int d, int Nr, int Nc, hipStream_t s);
+hipError_t launch_log_softmax(float* zr, float* zc, int L, int Nr, int Nc, hipStream_t s);
+
+// topk.hip
+hipError_t launch_product_topk(const float* a, const float* b, int L, int Nr, int Nc, int kp,
+                               int K, int32_t* expert_idx, float* score, float* gate,
+                               int32_t* row_sel, int32_t* col_sel, int32_t* tie_flag,
+                               hipStream_t s);
+
+// schedule.hip
+struct ScheduleWs {
+  size_t bytes;
+  size_t flags, tile_cnt, rank, key0, val0, key1, val1, hist;  // byte offsets
+  int n_ftiles, n_ttiles, passes, max_groups;
+};
+ScheduleWs schedule_ws_layout(int L, int K, int N, int B);
+hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx,
+                           const float* gate, int32_t* counts, int32_t* active,
+                           int32_t* group_offsets, int32_t* task_token, int32_t* task_expert,
+                           float* task_gate, int32_t* task_index, void* ws, hipStream_t s);
+
+// execute.hip
+hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int M, const void* x, const void* w,
+                                 const void* v, const int32_t* task_token,
+                                 const int32_t* task_expert, const float* task_gate, float* y,
+                                 bool accumulate, hipStream_t s);
+
+}  // namespace omni

@@ -1,0 +1,200 @@
+// Cartesian Product Router, part 1: row / column logits and their
+// log-softmax.  Pages: gist.science explainer §2.2 "Cartesian Product
+// Router" (two small projections give row and column logits over the
+// Nr x Nc grid) and the interactive explainer "Cartesian Product Router"
+// (the scores are combined in log space).
+//
+// The projection is one dense contraction z = x . [Wr | Wc] of shape
+// L x d x (Nr + Nc), so the bf16 path runs it on the gfx950 matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A second kernel turns each
+// row of z into log-probabilities in place.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace omni {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Block tile 128 tokens x 128 grid lines x 64 features; 4 waves in 2 x 2,
+// each wave owns a 64 x 64 sub-tile = 4 x 4 MFMA 16x16 tiles.  LDS rows are
+// padded by 8 bf16 (16 bytes) to spread the 16-byte fragment reads over banks.
+constexpr int RBM = 128, RBN = 128, RBK = 64, RLD = RBK + 8;
+
+__global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ wc, const float* __restrict__ rb,
+    const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[RBM * RLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[RBN * RLD];
+
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  // Workgroup b runs on XCD b % 8.  Give every XCD a contiguous run of
+  // logical tiles so one token tile is reused from that XCD's L2 across all
+  // of its grid-line tiles.
+  const int nblk = n_mt * n_nt;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int logical = xcd * per + min(xcd, rem) + loc;
+  const int mt = logical / n_nt, nt = logical - mt * n_nt;
+  const int m0 = mt * RBM, n0 = nt * RBN;
+  const int NT = Nr + Nc;
+
+  // global -> register staging: 4 x 16 B of A and of B per thread
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+  int ach[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, row = c >> 3;
+    ach[i] = (c & 7) * 8;
+    const int t = m0 + row;
+    arow[i] = (t < L) ? x + static_cast<size_t>(t) * d : nullptr;
+    const int n = n0 + row;
+    brow[i] = (n < Nr) ? wr + static_cast<size_t>(n) * d
+                       : ((n < NT) ? wc + static_cast<size_t>(n - Nr) * d : nullptr);
+  }
+  uint4 ra[4], rbv[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + ach[i];
+      ra[i] = (arow[i] && k < d) ? *reinterpret_cast<const uint4*>(arow[i] + k) : make_uint4(0, 0, 0, 0);
+      rbv[i] = (brow[i] && k < d) ? *reinterpret_cast<const uint4*>(brow[i] + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wm = wv >> 1, wn = wv & 1;
+  const int fr = l & 15, fk = (l >> 4) * 8;
+
+  gload(0);
+  for (int k0 = 0; k0 < d; k0 += RBK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3;
+      *reinterpret_cast<uint4*>(&sA[row * RLD + ach[i]]) = ra[i];
+      *reinterpret_cast<uint4*>(&sB[row * RLD + ach[i]]) = rbv[i];
+    }
+    __syncthreads();
+    if (k0 + RBK < d) gload(k0 + RBK);
+#pragma unroll
+    for (int kk = 0; kk < RBK; kk += 32) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 64 + i * 16 + fr) * RLD + kk + fk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[(wn * 64 + j * 16 + fr) * RLD + kk + fk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Accumulator lane layout (16x16 output tile): column = lane % 16,
+  // rows 4 * (lane / 16) + q, q = 0..3.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 64 + j * 16 + fr;
+    if (n >= NT) continue;
+    const bool is_row = n < Nr;
+    const float bias = is_row ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + q;
+        if (t >= L) continue;
+        const float val = acc[i][j][q] + bias;
+        if (is_row) zr[static_cast<size_t>(t) * Nr + n] = val;
+        else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = val;
+      }
+    }
+  }
+}
+
+// fp32 path (small shapes): one thread per (token, grid line), features in
+// ascending order, float4 loads.
+__global__ __launch_bounds__(256) void router_gemm_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ wc,
+    const float* __restrict__ rb, const float* __restrict__ cb, float* __restrict__ zr,
+    float* __restrict__ zc, int L, int d, int Nr, int Nc) {
+  const int NT = Nr + Nc;
+  const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= static_cast<size_t>(L) * NT) return;
+  const int t = static_cast<int>(id / NT), n = static_cast<int>(id - static_cast<size_t>(t) * NT);
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * d);
+  const float4* wrow = reinterpret_cast<const float4*>(
+      n < Nr ? wr + static_cast<size_t>(n) * d : wc + static_cast<size_t>(n - Nr) * d);
+  float s = 0.f;
+  for (int c = 0; c < d / 4; ++c) {
+    const float4 a = xr[c], b = wrow[c];
+    s = fmaf(a.x, b.x, s);
+    s = fmaf(a.y, b.y, s);
+    s = fmaf(a.z, b.z, s);
+    s = fmaf(a.w, b.w, s);
+  }
+  if (n < Nr) zr[static_cast<size_t>(t) * Nr + n] = s + (rb ? rb[n] : 0.f);
+  else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = s + (cb ? cb[n - Nr] : 0.f);
+}
+
+// In-place log-softmax of each row of zr [L, Nr] and zc [L, Nc]: one wave
+// per row, a = z - (m + ln sum exp(z - m)).
+__global__ __launch_bounds__(256) void log_softmax_kernel(float* __restrict__ zr,
+                                                          float* __restrict__ zc, int L, int Nr,
+                                                          int Nc) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= 2 * L) return;
+  const int l = lane();
+  float* z;
+  int n;
+  if (row < L) { z = zr + static_cast<size_t>(row) * Nr; n = Nr; }
+  else { z = zc + static_cast<size_t>(row - L) * Nc; n = Nc; }
+  float m = -INFINITY;
+  for (int i = l; i < n; i += 64) m = fmaxf(m, z[i]);
+  m = wave_max(m);
+  float s = 0.f;
+  for (int i = l; i < n; i += 64) s += expf(z[i] - m);
+  s = wave_sum(s);
+  const float lse = m + logf(s);
+  for (int i = l; i < n; i += 64) z[i] = z[i] - lse;
+}
+
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
+                              const float* rb, const float* cb, float* zr, float* zc, int L,
+                              int d, int Nr, int Nc, hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  const int n_mt = (L + RBM - 1) / RBM, n_nt = (Nr + Nc + RBN - 1) / RBN;
+  router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc,
+                                                      n_mt, n_nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_f32(const float* x, const float* wr, const float* wc, const float* rb,
+                             const float* cb, float* zr, float* zc, int L, int d, int Nr, int Nc,
+                             hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  const size_t n = static_cast<size_t>(L) * (Nr + Nc);
+  router_gemm_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+      x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc);
+  return hipGetLastError();
+}
+
+hipError_t launch_log_softmax(float* zr, float* zc, int L, int Nr, int Nc, hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  log_softmax_kernel<<<(2 * L + 3) / 4, 256, 0, s>>>(zr, zc, L, Nr, Nc);
+  return hipGetLastError();
+}
+
+}  // namespace omni

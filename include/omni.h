@@ -1,0 +1,202 @@
+/*
+ * omni.h — C ABI of the MI355X (gfx950) OmniMoE routed atomic-expert layer,
+ * forward pass.
+ *
+ * The layer (pages: "OmniMoE: An Efficient MoE by Orchestrating Atomic
+ * Experts at Scale", gist.science explainer §2.1-§2.2, and the OmniMoE
+ * interactive explainer, sections "Atomic Expert / DEA", "Cartesian Product
+ * Router", "Expert-Centric Scheduling"):
+ *
+ *   1. omni_router_logits   row / column log-probabilities of the Cartesian
+ *                           Product Router over an Nr x Nc expert grid;
+ *   2. omni_product_topk    per-axis top-k', then top-K over the k' x k'
+ *                           product cells with S = log p_r[i] + log p_c[j],
+ *                           plus the gates (softmax over the K selected S);
+ *   3. omni_schedule_tasks  Expert-Centric Scheduling: flatten the L*K
+ *                           (token, expert, gate) tasks, group the unique
+ *                           active experts B at a time, order the tasks by
+ *                           (group, token);
+ *   4. omni_atomic_forward  expert-centric execution of the schedule:
+ *                           y_t = sum_k g_tk * silu(x_t . W[e_tk]) * V[e_tk].
+ *
+ * Conventions shared by every call
+ *   - All pointers except the `omni_schedule` descriptor itself are DEVICE
+ *     pointers owned by the caller.  The library never allocates, frees or
+ *     synchronises; every call only enqueues kernels on `stream` and returns.
+ *   - Matrices are dense row-major.  bf16 data is raw bfloat16 bits.
+ *   - Shapes and pointers are validated on the host before anything is
+ *     enqueued; a failed check returns a non-OK status and enqueues nothing.
+ *     A failed launch returns OMNI_ERR_HIP.  Faults during execution surface
+ *     at the caller's next synchronisation.
+ *   - Inputs must be finite; NaN / Inf inputs give unspecified results.
+ *   - Expert ids: grid cell (i, j) is expert e = i * Nc + j (row-major).
+ *   - Tie rule everywhere: larger value first, then lower index; values are
+ *     compared as float32 numbers (-0 == +0).
+ *   - L == 0 is accepted and enqueues only what writes the (empty) outputs.
+ */
+#ifndef OMNI_H
+#define OMNI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum omni_status {
+  OMNI_OK = 0,
+  OMNI_ERR_INVALID_ARG = 1,   /* bad shape, null or misaligned pointer      */
+  OMNI_ERR_WORKSPACE = 2,     /* workspace pointer null or smaller than asked */
+  OMNI_ERR_UNSUPPORTED = 3,   /* valid request outside what the kernels cover */
+  OMNI_ERR_HIP = 4            /* a kernel launch failed                      */
+} omni_status;
+
+typedef enum omni_dtype {
+  OMNI_F32 = 0,               /* float32 x, weights                          */
+  OMNI_BF16 = 1               /* bfloat16 x, weights; float32 accumulation   */
+} omni_dtype;
+
+/* ABI revision of this header. */
+int omni_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* omni_status_string(omni_status s);
+
+/*
+ * omni_router_logits — Cartesian Product Router, row and column scores.
+ * Pages: gist.science explainer §2.2 "Cartesian Product Router" (two small
+ * projections give independent low-dimensional row and column logits) and
+ * the interactive explainer, "Cartesian Product Router" (p(i,j|x) is taken as
+ * p_r(i|x) p_c(j|x); scores are combined in log space).
+ *
+ *   row_logp[t, i] = log_softmax_i( x[t,:] . Wr[:, i] + row_bias[i] )
+ *   col_logp[t, j] = log_softmax_j( x[t,:] . Wc[:, j] + col_bias[j] )
+ *
+ * dt        OMNI_BF16 (MFMA path) or OMNI_F32.
+ * x         [L, d] of dt.
+ * wr_t      [Nr, d] of dt: row i holds the d weights that score grid row i
+ *           (Wr of the pages, Wr in R^{d x Nr}, stored transposed).
+ * wc_t      [Nc, d] of dt, likewise for grid columns.
+ * row_bias  [Nr] float32 or NULL;  col_bias [Nc] float32 or NULL.
+ * row_logp  [L, Nr] float32 out;   col_logp [L, Nc] float32 out.
+ * Requires L >= 0, d >= 1, Nr >= 1, Nc >= 1; for bf16 d % 8 == 0 and
+ * x, wr_t, wc_t 16-byte aligned; for f32 d % 4 == 0 and 16-byte aligned.
+ */
+omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc,
+                               const void* x, const void* wr_t, const void* wc_t,
+                               const float* row_bias, const float* col_bias,
+                               float* row_logp, float* col_logp,
+                               hipStream_t stream);
+
+/*
+ * omni_product_topk — top-K over the product grid, and the gates.
+ * Pages: interactive explainer, "Cartesian Product Router" (rows and
+ * columns are searched separately; the joint score S_ij = log p_r[i] +
+ * log p_c[j] is additive in log space and the N-entry score matrix is never
+ * formed) and "Expert-Centric Scheduling" (each routing decision carries a
+ * weight).
+ *
+ * Per token t: R = the k' best rows of row_logp[t] (value desc, index asc),
+ * C = the k' best columns of col_logp[t]; over the k' x k' cells
+ * S = fl32(row_logp[t,R_r] + col_logp[t,C_c]), e = R_r * Nc + C_c, keep the
+ * K best by (S desc, e asc) in rank order.
+ *
+ * expert_idx [L, K] int32 out (rank order); score [L, K] float32 out (S);
+ * gate [L, K] float32 out: g_k = exp(S_k - S_0) / sum_j exp(S_j - S_0).
+ * row_sel, col_sel: [L, k'] int32 out (R and C in rank order), each may be
+ * NULL.
+ * ws / ws_bytes: workspace of at least omni_product_topk_workspace(...)
+ * bytes, 256-byte aligned (a tie flag per token and, for NULL row_sel /
+ * col_sel, the per-axis lists).
+ * Requires 1 <= k' <= min(Nr, Nc), 1 <= K <= k'^2, Nr * Nc < 2^31.
+ * Kernels cover k' <= 64, K <= 64 and Nr, Nc <= 4096 (else UNSUPPORTED).
+ * Selection and scores are exact functions of the float32 inputs; gates are
+ * float32 (expf, wave-order sum).
+ */
+size_t omni_product_topk_workspace(int L, int Nr, int Nc, int kprime, int K);
+omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K,
+                              const float* row_logp, const float* col_logp,
+                              int32_t* expert_idx, float* score, float* gate,
+                              int32_t* row_sel, int32_t* col_sel,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Schedule produced by omni_schedule_tasks (all members device pointers).
+ * G = omni_schedule_max_groups(L, K, N, B) = ceil(min(N, L*K) / B).
+ *   counts        [2]      int32: n_active, n_groups.
+ *   active        [min(N, L*K)] int32: the active expert ids ascending
+ *                          (entries >= n_active unspecified).
+ *   group_offsets [G + 1]  int32: tasks of group g are [off[g], off[g+1]);
+ *                          every entry past n_groups equals L*K.
+ *   task_token, task_expert [L*K] int32, task_gate [L*K] float32: the tasks
+ *                          sorted by (group, token), ties in flatten order.
+ *   task_index    [L*K] int32: flat id m = t*K + k of each sorted task, or
+ *                          NULL if not wanted.
+ */
+typedef struct omni_schedule {
+  int32_t* counts;
+  int32_t* active;
+  int32_t* group_offsets;
+  int32_t* task_token;
+  int32_t* task_expert;
+  float* task_gate;
+  int32_t* task_index;
+} omni_schedule;
+
+/* ceil(min(N, L*K) / B): the number of groups the schedule can hold. */
+int omni_schedule_max_groups(int L, int K, int N, int B);
+
+/*
+ * omni_schedule_tasks — Expert-Centric Scheduling.
+ * Pages: interactive explainer, "Expert-Centric Scheduling" (flatten all
+ * (token, expert, weight) triples into M = L x K tasks; collect the unique
+ * active experts, sort them by id, B per group; order by group id, then
+ * token id) and gist.science explainer §2.2 (task collection, grouping and
+ * sorting, grouped execution).
+ *
+ * expert_idx [L, K] int32 in (each id in [0, N)); gate [L, K] float32 in.
+ * out: host pointer to a descriptor whose members point to device buffers
+ * of the sizes listed above.  ws / ws_bytes: workspace of at least
+ * omni_schedule_workspace(...) bytes, 256-byte aligned.
+ * Requires N >= 1, K >= 1, B >= 1, L*K < 2^31.  Ids outside [0, N) give
+ * unspecified results (the ids are produced on the device and not checked).
+ * Bit-exact: the result is a pure function of the inputs.
+ */
+size_t omni_schedule_workspace(int L, int K, int N, int B);
+omni_status omni_schedule_tasks(int L, int K, int N, int B,
+                                const int32_t* expert_idx, const float* gate,
+                                const omni_schedule* out,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * omni_atomic_forward — expert-centric execution of a schedule.
+ * Pages: gist.science explainer §2.1 (atomic expert E_i(x) = sigma(x w_in^T)
+ * w_out; all N experts live in two global matrices W, V in R^{N x d}; per
+ * token the selected rows are assembled into one block) and interactive
+ * explainer "Expert-Centric Scheduling" (each group's parameters are loaded
+ * once and reused for all tokens assigned to it; traffic 2d*|E_active|
+ * instead of 2d*L*K).  sigma = SiLU.
+ *
+ *   y[t, :] = sum over scheduled tasks (t, e, g): g * silu(x[t,:] . W[e,:]) * V[e,:]
+ *
+ * x [L, d], w [N, d], v [N, d] of dt; sched: a schedule produced by
+ * omni_schedule_tasks for the same L, K, N, B; y [L, d] float32 out.
+ * accumulate = 0: y is overwritten with the routed output; accumulate != 0:
+ * the routed output is added to y as it stands (e.g. onto the output of a
+ * shared dense branch).  ws / ws_bytes: at least omni_atomic_forward_workspace(...)
+ * bytes.  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
+ * 16-byte aligned x, w, v.  y is accumulated with float32 atomics, so its
+ * low bits depend on the order tasks finish.
+ */
+size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B);
+omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B,
+                                const void* x, const void* w, const void* v,
+                                const omni_schedule* sched, float* y, int accumulate,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OMNI_H */

@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol include/omni.h declares, and
+rejects bad arguments on the host (these calls return before any HIP call, so
+they need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "omni.h")
+
+B = pytest.importorskip("cartesian_routed_atomic_amd.binding")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(omni_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail(f"{B.LIB_PATH} missing: run __graft_entry__.build() first")
+    return B.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    d = _declared()
+    for name in ("omni_router_logits", "omni_product_topk", "omni_schedule_tasks",
+                 "omni_atomic_forward"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(B.EXPORTS)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.omni_abi_version() == 1
+    for code in range(5):
+        assert lib.omni_status_string(code)
+    assert lib.omni_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced (checks fail first)
+MIS = ctypes.c_void_p((1 << 20) + 2)  # misaligned
+
+
+def test_router_argument_checks(lib):
+    f = lib.omni_router_logits
+    ok_args = dict(dt=B.OMNI_BF16, L=4, d=64, Nr=8, Nc=8)
+
+    def call(dt=1, L=4, d=64, Nr=8, Nc=8, x=FAKE, wr=FAKE, wc=FAKE, rl=FAKE, cl=FAKE):
+        return f(dt, L, d, Nr, Nc, x, wr, wc, None, None, rl, cl, None)
+    assert ok_args
+    assert call(dt=7) == B.OMNI_ERR_INVALID_ARG
+    assert call(L=-1) == B.OMNI_ERR_INVALID_ARG
+    assert call(Nr=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(x=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(rl=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(x=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(d=60) == B.OMNI_ERR_UNSUPPORTED          # bf16 needs d % 8 == 0
+    assert call(dt=0, d=66) == B.OMNI_ERR_UNSUPPORTED    # f32 needs d % 4 == 0
+    assert call(L=1 << 30, d=64) == B.OMNI_ERR_UNSUPPORTED
+    assert call(L=0) == B.OMNI_OK                        # empty batch: nothing enqueued
+
+
+def test_product_topk_argument_checks(lib):
+    f = lib.omni_product_topk
+
+    def call(L=4, Nr=16, Nc=16, kp=4, K=4, ws=None, nws=0):
+        return f(L, Nr, Nc, kp, K, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, ws, nws, None)
+    assert call(kp=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(kp=17) == B.OMNI_ERR_INVALID_ARG         # k' > Nr
+    assert call(kp=4, K=17) == B.OMNI_ERR_INVALID_ARG    # K > k'^2
+    assert call(K=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(Nr=1 << 16, Nc=1 << 16, kp=4) == B.OMNI_ERR_INVALID_ARG  # N >= 2^31
+    assert call(Nr=128, Nc=128, kp=65, K=8) == B.OMNI_ERR_UNSUPPORTED
+    assert call(Nr=128, Nc=128, kp=64, K=65) == B.OMNI_ERR_UNSUPPORTED
+    assert call(Nr=8192, Nc=16, kp=4, K=4) == B.OMNI_ERR_UNSUPPORTED
+    assert call(L=0) == B.OMNI_OK
+    nws = lib.omni_product_topk_workspace(8192, 1024, 1024, 64, 64)
+    assert nws >= 8192 * 4 + 2 * 8192 * 64 * 4
+    assert call(ws=None, nws=nws) == B.OMNI_ERR_WORKSPACE
+    assert call(ws=FAKE, nws=1) == B.OMNI_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 8), nws=1 << 20) == B.OMNI_ERR_WORKSPACE
+
+
+def test_schedule_argument_checks(lib):
+    L, K, N, Bg = 64, 8, 1024, 16
+    assert lib.omni_schedule_max_groups(L, K, N, Bg) == 32
+    assert lib.omni_schedule_max_groups(8192, 64, 1 << 20, 256) == 2048
+    assert lib.omni_schedule_max_groups(256, 64, 1 << 20, 64) == 256
+    nws = lib.omni_schedule_workspace(L, K, N, Bg)
+    assert nws > 0
+    st = B.ScheduleStruct(*([1 << 20] * 7))
+    f = lib.omni_schedule_tasks
+
+    def call(L=L, K=K, N=N, Bg=Bg, ws=FAKE, n=nws, s=st):
+        return f(L, K, N, Bg, FAKE, FAKE, ctypes.byref(s) if s is not None else None, ws, n, None)
+    assert call(K=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(Bg=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(N=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(L=1 << 28, K=64) == B.OMNI_ERR_INVALID_ARG   # L*K >= 2^31
+    assert call(s=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
+    assert call(ws=None) == B.OMNI_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE  # not 256-aligned
+    bad = B.ScheduleStruct(*([1 << 20] * 3 + [0] + [1 << 20] * 3))
+    assert call(s=bad) == B.OMNI_ERR_INVALID_ARG
+
+
+def test_atomic_forward_argument_checks(lib):
+    st = B.ScheduleStruct(*([1 << 20] * 7))
+    f = lib.omni_atomic_forward
+
+    def call(dt=1, L=4, d=128, N=64, K=2, Bg=4, x=FAKE, w=FAKE, v=FAKE, y=FAKE, s=st):
+        return f(dt, L, d, N, K, Bg, x, w, v, ctypes.byref(s) if s is not None else None,
+                 y, 0, None, 0, None)
+    assert call(dt=3) == B.OMNI_ERR_INVALID_ARG
+    assert call(s=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(y=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(w=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=8192) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=32) == B.OMNI_ERR_UNSUPPORTED
+    assert call(L=0) == B.OMNI_OK

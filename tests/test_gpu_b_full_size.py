@@ -1,0 +1,43 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (binding.forward on one stream).  The oracle checks the whole
+router output and the whole schedule, and samples tokens for the top-K and
+for y (each sampled token is computed independently by the oracle)."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import omni_oracle as O
+from synth import WORKLOADS, make_inputs
+from tests.gpu_helpers import dev, host, log
+from tests.test_gpu_a_parity import check_router, check_schedule, check_topk, check_y
+
+pytestmark = pytest.mark.gpu
+
+B = pytest.importorskip("cartesian_routed_atomic_amd.binding")
+
+
+@pytest.mark.parametrize("name", ["mid", "large", "decode"])
+def test_full_size_parity(name):
+    wl = WORKLOADS[name]
+    log(f"[full] {name}: L={wl.L} d={wl.d} N={wl.N} K={wl.K} B={wl.B}")
+    t0 = time.time()
+    inp = make_inputs(wl)
+    log(f"  inputs generated in {time.time() - t0:.1f}s")
+    t = {k: dev(v) for k, v in inp.items()}
+    out = B.forward(t["x"], t["wr"], t["wc"], t["w"], t["v"], wl.kprime, wl.K, wl.B,
+                    t["row_bias"], t["col_bias"])
+    torch.cuda.synchronize()
+    del t
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    check_router(inp, out["row_logp"], out["col_logp"])
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(wl.L, size=min(wl.L, 512), replace=False))
+    check_topk(out["row_logp"], out["col_logp"], out, wl.kprime, wl.K, tokens=toks)
+    want = check_schedule(out, out["schedule"], wl.N, wl.B)
+    log(f"  expert usage {want['n_active'] / wl.N:.4f}; traffic "
+        f"{O.traffic_elements(wl.d, wl.L, wl.K, want['n_active'])}")
+    ytoks = np.sort(rng.choice(wl.L, size=min(wl.L, 96), replace=False))
+    check_y(inp, out, out["y"], wl.dtype, tokens=ytoks)
+    log(f"  done in {time.time() - t0:.1f}s")
