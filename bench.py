@@ -123,7 +123,13 @@ def main():
     sel = {"expert_idx": torch.empty((L, K), dtype=torch.int32, device=dev),
            "score": torch.empty((L, K), dtype=torch.float32, device=dev),
            "gate": torch.empty((L, K), dtype=torch.float32, device=dev)}
-    sched = B.alloc_schedule(L, K, wl.N, wl.B, dev, with_index=False)
+    sel["workspace"] = torch.empty(
+        max(1, B.lib().omni_product_topk_workspace(L, wl.Nr, wl.Nc, wl.kprime, K)),
+        dtype=torch.uint8, device=dev)
+    sched = B.alloc_schedule(L, K, wl.N, wl.B, dev)
+    exec_ws = torch.empty(
+        max(1, B.lib().omni_atomic_forward_workspace(1, L, wl.d, wl.N, K, wl.B)),
+        dtype=torch.uint8, device=dev)
     y = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
     y2 = torch.zeros_like(y)
 
@@ -137,7 +143,7 @@ def main():
         B.schedule_tasks(sel["expert_idx"], sel["gate"], wl.N, wl.B, sched=sched)
 
     def stage_execute():
-        B.atomic_forward(x, w, v, sched, y=y)
+        B.atomic_forward(x, w, v, sched, y=y, workspace=exec_ws)
 
     def step():
         stage_router()
@@ -170,7 +176,8 @@ def main():
     stages = {"router": ev_time(stage_router), "topk": ev_time(stage_topk),
               "schedule": ev_time(stage_schedule), "execute": ev_time(stage_execute)}
     # the executor kernel alone: accumulate mode skips the y clear
-    exec_ms = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y2, accumulate=True), reps=20)
+    exec_ms = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y2, accumulate=True,
+                                               workspace=exec_ws), reps=20)
     counts = sched.counts.cpu().tolist()
     n_active, n_groups = int(counts[0]), int(counts[1])
     s = wl.elem_bytes

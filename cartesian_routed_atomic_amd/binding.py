@@ -228,22 +228,27 @@ def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None):
     return sched
 
 
-def atomic_forward(x, w, v, sched, y=None, accumulate=False, stream=None):
+def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, stream=None):
     """omni_atomic_forward: returns y [L, d] float32 (y += routed if accumulate)."""
     L, d = x.shape
     N = w.shape[0]
     _req(x, "x")
     _req(w, "w", x.dtype, (N, d))
     _req(v, "v", x.dtype, (N, d))
+    if sched.task_index is None:
+        raise ValueError("the schedule must carry task_index")
     if y is None:
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
     _req(y, "y", torch.float32, (L, d))
     st = sched.struct()
     nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B)
-    ws = torch.empty(nws, dtype=torch.uint8, device=x.device) if nws else None
+    ws = workspace
+    if nws and (ws is None or ws.numel() < nws):
+        ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
     _check("omni_atomic_forward", lib().omni_atomic_forward(
         _dtype_code(x), L, d, N, sched.K, sched.B, _ptr(x), _ptr(w), _ptr(v),
-        ctypes.byref(st), _ptr(y), int(bool(accumulate)), _ptr(ws), nws, _stream(stream)))
+        ctypes.byref(st), _ptr(y), int(bool(accumulate)), _ptr(ws), nws if ws is not None else 0,
+        _stream(stream)))
     return y
 
 

@@ -138,8 +138,9 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, const int32_t* exper
 }
 
 size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B) {
-  (void)dt; (void)L; (void)d; (void)N; (void)K; (void)B;
-  return 0;
+  (void)dt; (void)d; (void)N; (void)B;
+  if (L <= 0 || K < 1 || !fits_i32(static_cast<long long>(L) * K)) return 0;
+  return omni::atomic_forward_ws_bytes(L, K);
 }
 
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B, const void* x,
@@ -151,18 +152,20 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
   if (!w || !v || !sched) return OMNI_ERR_INVALID_ARG;
   const long long M = static_cast<long long>(L) * K;
   if (L > 0 && (!x || !y)) return OMNI_ERR_INVALID_ARG;
-  if (M > 0 && (!sched->task_token || !sched->task_expert || !sched->task_gate))
+  if (M > 0 && (!sched->task_token || !sched->task_expert || !sched->task_gate ||
+                !sched->task_index))
     return OMNI_ERR_INVALID_ARG;
   if (d < 64 || d > 4096 || (d & (d - 1)) != 0) return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(v)) return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && !aligned16(y)) return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;
-  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
-  if (need > 0 && (!ws || ws_bytes < need)) return OMNI_ERR_WORKSPACE;
-  (void)ws;
   if (L == 0) return OMNI_OK;
-  return hip_status(omni::launch_atomic_forward(dt == OMNI_BF16, L, d, N, static_cast<int>(M), x, w,
-                                                v, sched->task_token, sched->task_expert,
-                                                sched->task_gate, y, accumulate != 0, stream));
+  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
+  return hip_status(omni::launch_atomic_forward(dt == OMNI_BF16, L, d, N, K, x, w, v,
+                                                sched->task_token, sched->task_expert,
+                                                sched->task_gate, sched->task_index, y,
+                                                accumulate != 0, ws, stream));
 }
 
 }  // extern "C"

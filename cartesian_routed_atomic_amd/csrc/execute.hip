@@ -5,20 +5,27 @@
 // reused for every token assigned to the group; parameter traffic
 // 2d * |E_active| instead of 2d * L * K).
 //
-// The kernel walks the task list in its (group, token) order.  Each wave
-// owns a contiguous run of tasks; per task it streams W[e] and V[e] from HBM
-// with 16-byte loads (the next task's rows are in flight while the current
-// one is computed), forms h = x_t . W[e] with a wave reduction, and adds
-// g * silu(h) * V[e] into a per-token register accumulator.  When the token
-// changes (the end of a (group, token) run) the accumulator is added into
-// y[t] with float32 atomics, 256 contiguous bytes per instruction after a
-// small LDS transpose.  Workgroups are laid out XCD by XCD over the task
-// list, so one group's tasks run on one XCD and an expert used by several
-// tokens of the group is re-read from that XCD's L2, not from HBM.
+// Two kernels, no atomics:
+//   phase 1 (expert-centric, in the schedule's (group, token) order): per
+//     task h = x_t . W[e], coef = g * silu(h), written at the task's flat id
+//     m = t*K + k together with e.  Each wave walks a contiguous run of the
+//     sorted tasks with three tasks' rows in flight; x_t is fetched once per
+//     (group, token) run.  Workgroups are laid out XCD by XCD over the task
+//     list, so a group's tasks run on one XCD and an expert used by several
+//     tokens of the group is re-read from that XCD's L2, not from HBM.  The
+//     bf16 dot product runs on v_dot2_f32_bf16 (two products per instruction,
+//     float32 accumulation).
+//   phase 2 (token-centric gather): y_t = sum_k coef[t,k] * V[e_tk], one wave
+//     (or a few, splitting d) per token, y written once with plain stores.
+// Scattering the V contributions in expert-centric order instead needs a
+// float32 atomic add into y per (group, token) run, which measured about
+// twice as slow on MI355X as reading the few repeated V rows again.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace omni {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // A row fragment of one lane: EPL elements held raw (as loaded) so a load
 // can stay in flight until the first use; element q = c * VEC + j maps to
@@ -62,112 +69,219 @@ template <int EPL> struct RowFrag<float, EPL> {
   __device__ __forceinline__ float get(int q) const { return f[q]; }
 };
 
+// Partial dot product of this lane's fragment elements.
+template <int EPL>
+__device__ __forceinline__ float frag_dot(const RowFrag<uint16_t, EPL>& a,
+                                          const RowFrag<uint16_t, EPL>& b) {
+  float p = 0.f;
+  if constexpr (EPL == 1) {
+    p = a.get(0) * b.get(0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RowFrag<uint16_t, EPL>::NW; ++i)
+      p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w[i]),
+                                          __builtin_bit_cast(bf16x2, b.w[i]), p, false);
+  }
+  return p;
+}
+template <int EPL>
+__device__ __forceinline__ float frag_dot(const RowFrag<float, EPL>& a,
+                                          const RowFrag<float, EPL>& b) {
+  float p = 0.f;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) p = fmaf(a.f[q], b.f[q], p);
+  return p;
+}
+
 __device__ __forceinline__ int rdlane(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
 __device__ __forceinline__ float rdlane(float v, int i) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
 }
 
-constexpr int kExecWaves = 4;  // waves per workgroup
+constexpr int kRing = 4;  // task slots per wave: three in flight, one computed
+
+// Phase 1.  Issue the loads of task i into ring slot S.
+template <typename T, int EPL>
+__device__ __forceinline__ void coef_issue(int i, int n, const T* __restrict__ x,
+                                           const T* __restrict__ W, int d, int my_t, int my_e,
+                                           RowFrag<T, EPL>& wslot, RowFrag<T, EPL>& xslot) {
+  if (i >= n) return;
+  wslot.load(W + static_cast<size_t>(rdlane(my_e, i)) * d, lane());
+  const int t = rdlane(my_t, i);
+  const int tp = i ? rdlane(my_t, i - 1) : -1;
+  if (t != tp) xslot.load(x + static_cast<size_t>(t) * d, lane());  // first task of a run
+}
 
 template <typename T, int EPL>
-__global__ __launch_bounds__(256) void atomic_forward_kernel(
-    const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ V,
-    const int32_t* __restrict__ ttok, const int32_t* __restrict__ texp,
-    const float* __restrict__ tgate, int M, int d, int L, int N, int chunk, int nblk,
-    float* __restrict__ y) {
+__global__ __launch_bounds__(256) void coef_kernel(
+    const T* __restrict__ x, const T* __restrict__ W, const int32_t* __restrict__ ttok,
+    const int32_t* __restrict__ texp, const float* __restrict__ tgate,
+    const int32_t* __restrict__ tidx, int M, int d, int L, int N, int chunk, int nblk,
+    float* __restrict__ coef, int32_t* __restrict__ eflat) {
   using Frag = RowFrag<T, EPL>;
-  constexpr int VEC = Frag::VEC, NCH = Frag::NCH;
-  __shared__ float tr[kExecWaves][64 * VEC];
-
   const int wv = threadIdx.x >> 6, l = lane();
   // XCD-contiguous workgroup order (workgroup b runs on XCD b % 8)
   const int per = nblk >> 3, rem = nblk & 7;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
   const int logical = xcd * per + min(xcd, rem) + loc;
-  const long long m0ll = (static_cast<long long>(logical) * kExecWaves + wv) * chunk;
+  const long long m0ll = (static_cast<long long>(logical) * 4 + wv) * chunk;
   if (m0ll >= M) return;
   const int m0 = static_cast<int>(m0ll);
   const int n = min(chunk, M - m0);
 
-  // task metadata of the run, one task per lane (chunk <= 64)
-  // ids outside [0, L) / [0, N) (only from a corrupted schedule) are mapped
-  // to 0 so every access stays in bounds
+  // task metadata, one task per lane (chunk <= 64).  Ids outside their range
+  // (only from a corrupted schedule) are mapped to 0 so every access stays
+  // in bounds.
   int my_t = (l < n) ? ttok[m0 + l] : 0;
   int my_e = (l < n) ? texp[m0 + l] : 0;
+  int my_i = (l < n) ? tidx[m0 + l] : 0;
+  const float my_g = (l < n) ? tgate[m0 + l] : 0.f;
   my_t = static_cast<unsigned>(my_t) < static_cast<unsigned>(L) ? my_t : 0;
   my_e = static_cast<unsigned>(my_e) < static_cast<unsigned>(N) ? my_e : 0;
-  const float my_g = (l < n) ? tgate[m0 + l] : 0.f;
+  const bool idx_ok = static_cast<unsigned>(my_i) < static_cast<unsigned>(M);
 
+  Frag wr[kRing], xr[kRing], xc;
+  int cur = -1;
+  float my_c = 0.f;
+#pragma unroll
+  for (int s = 0; s < kRing - 1; ++s) coef_issue<T, EPL>(s, n, x, W, d, my_t, my_e, wr[s], xr[s]);
+  for (int i = 0; i < n; i += kRing) {
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int ii = i + s;
+      if (ii >= n) break;
+      coef_issue<T, EPL>(ii + kRing - 1, n, x, W, d, my_t, my_e, wr[(s + kRing - 1) % kRing],
+                         xr[(s + kRing - 1) % kRing]);
+      const int t = rdlane(my_t, ii);
+      if (t != cur) {
+        xc = xr[s];
+        cur = t;
+      }
+      const float h = wave_sum(frag_dot<EPL>(xc, wr[s]));
+      const float c = rdlane(my_g, ii) * (h / (1.f + __expf(-h)));
+      if (l == ii) my_c = c;
+    }
+  }
+  if (l < n && idx_ok) {
+    coef[my_i] = my_c;
+    eflat[my_i] = my_e;
+  }
+}
+
+// Phase 2.  Wave g serves token g / split, columns [s * 64 * EPL, +64 * EPL).
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void gather_kernel(
+    const T* __restrict__ V, const float* __restrict__ coef, const int32_t* __restrict__ eflat,
+    int L, int K, int d, int N, int split, float* __restrict__ y, int accumulate) {
+  using Frag = RowFrag<T, EPL>;
+  constexpr int VEC = Frag::VEC, NCH = Frag::NCH;
+  const long long g = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int l = lane();
+  if (g >= static_cast<long long>(L) * split) return;
+  const int t = static_cast<int>(g / split);
+  const int col0 = static_cast<int>(g - static_cast<long long>(t) * split) * 64 * EPL;
   float acc[EPL];
-  float xf[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
-  int cur = rdlane(my_t, 0);
-  {
-    Frag xr;
-    xr.load(x + static_cast<size_t>(cur) * d, l);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int n = min(64, K - k0);
+    const size_t base = static_cast<size_t>(t) * K + k0;
+    int my_e = (l < n) ? eflat[base + l] : 0;
+    my_e = static_cast<unsigned>(my_e) < static_cast<unsigned>(N) ? my_e : 0;
+    const float my_c = (l < n) ? coef[base + l] : 0.f;
+    Frag f[kRing];
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) xf[q] = xr.get(q);
+    for (int s = 0; s < kRing - 1; ++s)
+      if (s < n) f[s].load(V + static_cast<size_t>(rdlane(my_e, s)) * d + col0, l);
+    for (int i = 0; i < n; i += kRing) {
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        const int ii = i + s;
+        if (ii >= n) break;
+        if (ii + kRing - 1 < n)
+          f[(s + kRing - 1) % kRing].load(
+              V + static_cast<size_t>(rdlane(my_e, ii + kRing - 1)) * d + col0, l);
+        const float c = rdlane(my_c, ii);
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
+      }
+    }
   }
-
-  auto flush = [&](int t) {
-    float* yt = y + static_cast<size_t>(t) * d;
+  float* yt = y + static_cast<size_t>(t) * d + col0;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+  for (int c = 0; c < NCH; ++c) {
+    float* p = yt + c * 64 * VEC + l * VEC;
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) tr[wv][l * VEC + j] = acc[c * VEC + j];
-      wave_lds_fence();
+    for (int j = 0; j < VEC; j += (VEC >= 4 ? 4 : VEC)) {
+      if constexpr (VEC >= 4) {
+        float4 v = make_float4(acc[c * VEC + j], acc[c * VEC + j + 1], acc[c * VEC + j + 2],
+                               acc[c * VEC + j + 3]);
+        if (accumulate) {
+          const float4 o = *reinterpret_cast<const float4*>(p + j);
+          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        }
+        *reinterpret_cast<float4*>(p + j) = v;
+      } else {
 #pragma unroll
-      for (int q = 0; q < VEC; ++q)
-        unsafeAtomicAdd(yt + c * 64 * VEC + q * 64 + l, tr[wv][q * 64 + l]);
-      wave_lds_fence();
+        for (int q = 0; q < VEC; ++q) p[q] = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
+      }
     }
-  };
-
-  auto process = [&](int i, const Frag& wf, const Frag& vf) {
-    const int t = rdlane(my_t, i);
-    if (t != cur) {
-      flush(cur);
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
-      cur = t;
-      Frag xr;
-      xr.load(x + static_cast<size_t>(cur) * d, l);
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) xf[q] = xr.get(q);
-    }
-    float p = 0.f;
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) p = fmaf(xf[q], wf.get(q), p);
-    const float h = wave_sum(p);
-    const float c = rdlane(my_g, i) * (h / (1.f + __expf(-h)));
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, vf.get(q), acc[q]);
-  };
-
-  // two tasks in flight: while one is computed the other's rows load
-  Frag wa, va, wb, vb;
-  {
-    const int e = rdlane(my_e, 0);
-    wa.load(W + static_cast<size_t>(e) * d, l);
-    va.load(V + static_cast<size_t>(e) * d, l);
   }
-  for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) {
-      const int e = rdlane(my_e, i + 1);
-      wb.load(W + static_cast<size_t>(e) * d, l);
-      vb.load(V + static_cast<size_t>(e) * d, l);
-    }
-    process(i, wa, va);
-    if (i + 1 >= n) break;
-    if (i + 2 < n) {
-      const int e = rdlane(my_e, i + 2);
-      wa.load(W + static_cast<size_t>(e) * d, l);
-      va.load(V + static_cast<size_t>(e) * d, l);
-    }
-    process(i + 1, wb, vb);
+}
+
+static inline int clampi(long long v, int lo, int hi) {
+  return static_cast<int>(v < lo ? lo : (v > hi ? hi : v));
+}
+
+template <typename T, int EPL>
+static void launch_coef_t(const T* x, const T* w, const int32_t* tt, const int32_t* te,
+                          const float* tg, const int32_t* ti, int M, int d, int L, int N,
+                          float* coef, int32_t* eflat, hipStream_t s) {
+  // ~16 waves per CU over 256 CUs at full size, at most 64 tasks per wave
+  const int chunk = clampi(M / (256 * 16), 1, 64);
+  const long long waves = (static_cast<long long>(M) + chunk - 1) / chunk;
+  const int nblk = static_cast<int>((waves + 3) / 4);
+  coef_kernel<T, EPL><<<nblk, 256, 0, s>>>(x, w, tt, te, tg, ti, M, d, L, N, chunk, nblk, coef,
+                                           eflat);
+}
+
+template <typename T, int EPL>
+static void launch_gather_t(const T* v, const float* coef, const int32_t* eflat, int L, int K,
+                            int d, int N, int split, float* y, int accumulate, hipStream_t s) {
+  const long long waves = static_cast<long long>(L) * split;
+  gather_kernel<T, EPL><<<static_cast<unsigned>((waves + 3) / 4), 256, 0, s>>>(
+      v, coef, eflat, L, K, d, N, split, y, accumulate);
+}
+
+// Phase-2 column split: enough waves to cover the chip when L is small,
+// never fewer than 512 columns (1 KiB of bf16) per wave and row.
+static int gather_split(int L, int d) {
+  int split = 1;
+  while (static_cast<long long>(L) * split < 256 * 8 && d / (split * 2) >= 512) split *= 2;
+  return split;
+}
+
+template <typename T>
+static bool dispatch_exec(const T* x, const T* w, const T* v, const int32_t* tt,
+                          const int32_t* te, const float* tg, const int32_t* ti, int M, int d,
+                          int L, int K, int N, float* coef, int32_t* eflat, float* y,
+                          int accumulate, hipStream_t s) {
+  switch (d) {
+#define OMNI_COEF(D_, EPL_) case D_: launch_coef_t<T, EPL_>(x, w, tt, te, tg, ti, M, d, L, N, coef, eflat, s); break;
+    OMNI_COEF(64, 1) OMNI_COEF(128, 2) OMNI_COEF(256, 4) OMNI_COEF(512, 8)
+    OMNI_COEF(1024, 16) OMNI_COEF(2048, 32) OMNI_COEF(4096, 64)
+#undef OMNI_COEF
+    default: return false;
   }
-  flush(cur);
+  const int split = gather_split(L, d);
+  switch (d / split) {
+#define OMNI_GATHER(D_, EPL_) case D_: launch_gather_t<T, EPL_>(v, coef, eflat, L, K, d, N, split, y, accumulate, s); break;
+    OMNI_GATHER(64, 1) OMNI_GATHER(128, 2) OMNI_GATHER(256, 4) OMNI_GATHER(512, 8)
+    OMNI_GATHER(1024, 16) OMNI_GATHER(2048, 32) OMNI_GATHER(4096, 64)
+#undef OMNI_GATHER
+    default: return false;
+  }
+  return true;
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, size_t n4) {
@@ -175,55 +289,38 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, s
   if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <typename T, int EPL>
-static void launch_exec_t(const T* x, const T* w, const T* v, const int32_t* tt,
-                          const int32_t* te, const float* tg, int M, int d, int L, int N,
-                          float* y, hipStream_t s) {
-  // ~16 waves per CU over 256 CUs at full size, at most 64 tasks per wave
-  int chunk = M / (256 * 16);
-  chunk = chunk < 1 ? 1 : (chunk > 64 ? 64 : chunk);
-  const long long waves = (static_cast<long long>(M) + chunk - 1) / chunk;
-  const int nblk = static_cast<int>((waves + kExecWaves - 1) / kExecWaves);
-  atomic_forward_kernel<T, EPL><<<nblk, 64 * kExecWaves, 0, s>>>(x, w, v, tt, te, tg, M, d, L,
-                                                                 N, chunk, nblk, y);
+size_t atomic_forward_ws_bytes(int L, int K) {
+  const size_t m = static_cast<size_t>(L) * static_cast<size_t>(K) * 4;
+  return 2 * ((m + 255) & ~static_cast<size_t>(255));
 }
 
-template <typename T>
-static bool dispatch_exec(const T* x, const T* w, const T* v, const int32_t* tt,
-                          const int32_t* te, const float* tg, int M, int d, int L, int N,
-                          float* y, hipStream_t s) {
-  switch (d) {
-    case 64: launch_exec_t<T, 1>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    case 128: launch_exec_t<T, 2>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    case 256: launch_exec_t<T, 4>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    case 512: launch_exec_t<T, 8>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    case 1024: launch_exec_t<T, 16>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    case 2048: launch_exec_t<T, 32>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    case 4096: launch_exec_t<T, 64>(x, w, v, tt, te, tg, M, d, L, N, y, s); return true;
-    default: return false;
-  }
-}
-
-hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int M, const void* x, const void* w,
-                                 const void* v, const int32_t* task_token,
-                                 const int32_t* task_expert, const float* task_gate, float* y,
-                                 bool accumulate, hipStream_t s) {
+hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int K, const void* x,
+                                 const void* w, const void* v, const int32_t* task_token,
+                                 const int32_t* task_expert, const float* task_gate,
+                                 const int32_t* task_index, float* y, bool accumulate, void* ws,
+                                 hipStream_t s) {
   if (L == 0) return hipSuccess;
-  if (!accumulate) {
-    const size_t n4 = static_cast<size_t>(L) * d / 4;
-    zero_f32_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(
-        reinterpret_cast<float4*>(y), n4);
+  const int M = L * K;
+  if (M == 0) {  // no tasks: the routed output is zero
+    if (!accumulate) {
+      const size_t n4 = static_cast<size_t>(L) * d / 4;
+      zero_f32_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(
+          reinterpret_cast<float4*>(y), n4);
+    }
+    return hipGetLastError();
   }
-  if (M == 0) return hipGetLastError();
+  float* coef = static_cast<float*>(ws);
+  int32_t* eflat = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + atomic_forward_ws_bytes(L, K) / 2);
   bool ok;
   if (bf16)
     ok = dispatch_exec<uint16_t>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                                  static_cast<const uint16_t*>(v), task_token, task_expert,
-                                 task_gate, M, d, L, N, y, s);
+                                 task_gate, task_index, M, d, L, K, N, coef, eflat, y,
+                                 accumulate ? 1 : 0, s);
   else
     ok = dispatch_exec<float>(static_cast<const float*>(x), static_cast<const float*>(w),
                               static_cast<const float*>(v), task_token, task_expert, task_gate,
-                              M, d, L, N, y, s);
+                              task_index, M, d, L, K, N, coef, eflat, y, accumulate ? 1 : 0, s);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -35,9 +35,11 @@ hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx
                            float* task_gate, int32_t* task_index, void* ws, hipStream_t s);
 
 // execute.hip
-hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int M, const void* x, const void* w,
-                                 const void* v, const int32_t* task_token,
-                                 const int32_t* task_expert, const float* task_gate, float* y,
-                                 bool accumulate, hipStream_t s);
+size_t atomic_forward_ws_bytes(int L, int K);
+hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int K, const void* x,
+                                 const void* w, const void* v, const int32_t* task_token,
+                                 const int32_t* task_expert, const float* task_gate,
+                                 const int32_t* task_index, float* y, bool accumulate, void* ws,
+                                 hipStream_t s);
 
 }  // namespace omni

@@ -171,7 +171,7 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * omni_atomic_forward — expert-centric execution of a schedule.
+ * omni_atomic_forward — execution of a schedule.
  * Pages: gist.science explainer §2.1 (atomic expert E_i(x) = sigma(x w_in^T)
  * w_out; all N experts live in two global matrices W, V in R^{N x d}; per
  * token the selected rows are assembled into one block) and interactive
@@ -181,14 +181,19 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B,
  *
  *   y[t, :] = sum over scheduled tasks (t, e, g): g * silu(x[t,:] . W[e,:]) * V[e,:]
  *
+ * Two kernels: the first walks the tasks in the schedule's (group, token)
+ * order and computes c = g * silu(x_t . W[e]) per task; the second gathers
+ * y_t = sum_k c_tk V[e_tk] per token, so y is written once, without atomics.
+ *
  * x [L, d], w [N, d], v [N, d] of dt; sched: a schedule produced by
- * omni_schedule_tasks for the same L, K, N, B; y [L, d] float32 out.
- * accumulate = 0: y is overwritten with the routed output; accumulate != 0:
- * the routed output is added to y as it stands (e.g. onto the output of a
- * shared dense branch).  ws / ws_bytes: at least omni_atomic_forward_workspace(...)
- * bytes.  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
- * 16-byte aligned x, w, v.  y is accumulated with float32 atomics, so its
- * low bits depend on the order tasks finish.
+ * omni_schedule_tasks for the same L, K, N, B, with task_index present;
+ * y [L, d] float32 out, 16-byte aligned.  accumulate = 0: y is overwritten
+ * with the routed output; accumulate != 0: the routed output is added to y as
+ * it stands (e.g. onto the output of a shared dense branch).
+ * ws / ws_bytes: at least omni_atomic_forward_workspace(...) bytes, 256-byte
+ * aligned (a coefficient and an expert id per task).  Requires
+ * d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED); 16-byte aligned x,
+ * w, v.  Deterministic: every y element is summed in a fixed order.
  */
 size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B);
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B,

@@ -130,3 +130,7 @@ def test_atomic_forward_argument_checks(lib):
     assert call(d=8192) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=32) == B.OMNI_ERR_UNSUPPORTED
     assert call(L=0) == B.OMNI_OK
+    assert call() == B.OMNI_ERR_WORKSPACE                  # L*K tasks need a workspace
+    noidx = B.ScheduleStruct(*([1 << 20] * 6 + [0]))
+    assert call(s=noidx) == B.OMNI_ERR_INVALID_ARG          # task_index is required
+    assert lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256) >= 8 * 8192 * 64
