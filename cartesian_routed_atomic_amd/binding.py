@@ -46,7 +46,7 @@ _SIGS = {
     "omni_router_logits": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "omni_product_topk_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "omni_product_topk": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                               _sz, _vp]),
+                               _vp, _vp, _sz, _vp]),
     "omni_schedule_max_groups": (_i, [_i, _i, _i, _i]),
     "omni_schedule_workspace": (_sz, [_i, _i, _i, _i]),
     "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),
@@ -112,9 +112,9 @@ def _req(t, name, dtype=None, shape=None):
 # ------------------------------------------------------------------ calls
 
 
-def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None, row_logp=None,
-                  col_logp=None, stream=None):
-    """omni_router_logits: returns (row_logp [L,Nr], col_logp [L,Nc]) float32."""
+def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None, row_logits=None,
+                  col_logits=None, stream=None):
+    """omni_router_logits: returns (row_logits [L,Nr], col_logits [L,Nc]) float32."""
     L, d = x.shape
     Nr, Nc = wr_t.shape[0], wc_t.shape[0]
     _req(x, "x")
@@ -123,52 +123,52 @@ def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None, row_logp=None,
     for b, n, nm in ((row_bias, Nr, "row_bias"), (col_bias, Nc, "col_bias")):
         if b is not None:
             _req(b, nm, torch.float32, (n,))
-    if row_logp is None:
-        row_logp = torch.empty((L, Nr), dtype=torch.float32, device=x.device)
-    if col_logp is None:
-        col_logp = torch.empty((L, Nc), dtype=torch.float32, device=x.device)
-    _req(row_logp, "row_logp", torch.float32, (L, Nr))
-    _req(col_logp, "col_logp", torch.float32, (L, Nc))
+    if row_logits is None:
+        row_logits = torch.empty((L, Nr), dtype=torch.float32, device=x.device)
+    if col_logits is None:
+        col_logits = torch.empty((L, Nc), dtype=torch.float32, device=x.device)
+    _req(row_logits, "row_logits", torch.float32, (L, Nr))
+    _req(col_logits, "col_logits", torch.float32, (L, Nc))
     _check("omni_router_logits", lib().omni_router_logits(
         _dtype_code(x), L, d, Nr, Nc, _ptr(x), _ptr(wr_t), _ptr(wc_t), _ptr(row_bias),
-        _ptr(col_bias), _ptr(row_logp), _ptr(col_logp), _stream(stream)))
-    return row_logp, col_logp
+        _ptr(col_bias), _ptr(row_logits), _ptr(col_logits), _stream(stream)))
+    return row_logits, col_logits
 
 
-def product_topk(row_logp, col_logp, kprime, K, want_sel=True, out=None, stream=None):
-    """omni_product_topk: returns dict expert_idx, score, gate (+ row_sel, col_sel)."""
-    L, Nr = row_logp.shape
-    Nc = col_logp.shape[1]
-    _req(row_logp, "row_logp", torch.float32)
-    _req(col_logp, "col_logp", torch.float32, (L, Nc))
-    dev = row_logp.device
-    o = out or {}
-    idx = o.get("expert_idx")
-    if idx is None:
-        idx = torch.empty((L, K), dtype=torch.int32, device=dev)
-    score = o.get("score")
-    if score is None:
-        score = torch.empty((L, K), dtype=torch.float32, device=dev)
-    gate = o.get("gate")
-    if gate is None:
-        gate = torch.empty((L, K), dtype=torch.float32, device=dev)
-    rsel = csel = None
-    if want_sel:
-        rsel = o.get("row_sel")
-        if rsel is None:
-            rsel = torch.empty((L, kprime), dtype=torch.int32, device=dev)
-        csel = o.get("col_sel")
-        if csel is None:
-            csel = torch.empty((L, kprime), dtype=torch.int32, device=dev)
+def product_topk(row_logits, col_logits, kprime, K, want_sel=True, want_logp=True, out=None,
+                 stream=None):
+    """omni_product_topk: returns dict expert_idx, score, gate, row_logp, col_logp,
+    row_sel, col_sel (the last four None unless asked for)."""
+    L, Nr = row_logits.shape
+    Nc = col_logits.shape[1]
+    _req(row_logits, "row_logits", torch.float32)
+    _req(col_logits, "col_logits", torch.float32, (L, Nc))
+    dev = row_logits.device
+    o = dict(out or {})
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+        _req(t, name, dtype, shape)
+        return t
+    idx = get("expert_idx", (L, K), torch.int32)
+    score = get("score", (L, K), torch.float32)
+    gate = get("gate", (L, K), torch.float32)
+    rlp = get("row_logp", (L, Nr), torch.float32) if want_logp else None
+    clp = get("col_logp", (L, Nc), torch.float32) if want_logp else None
+    rsel = get("row_sel", (L, kprime), torch.int32) if want_sel else None
+    csel = get("col_sel", (L, kprime), torch.int32) if want_sel else None
     nws = lib().omni_product_topk_workspace(L, Nr, Nc, kprime, K)
     ws = o.get("workspace")
     if nws and (ws is None or ws.numel() < nws):
         ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     _check("omni_product_topk", lib().omni_product_topk(
-        L, Nr, Nc, kprime, K, _ptr(row_logp), _ptr(col_logp), _ptr(idx), _ptr(score),
-        _ptr(gate), _ptr(rsel), _ptr(csel), _ptr(ws), nws, _stream(stream)))
-    return {"expert_idx": idx, "score": score, "gate": gate, "row_sel": rsel, "col_sel": csel,
-            "workspace": ws}
+        L, Nr, Nc, kprime, K, _ptr(row_logits), _ptr(col_logits), _ptr(idx), _ptr(score),
+        _ptr(gate), _ptr(rlp), _ptr(clp), _ptr(rsel), _ptr(csel), _ptr(ws),
+        nws if ws is not None else 0, _stream(stream)))
+    return {"expert_idx": idx, "score": score, "gate": gate, "row_logp": rlp, "col_logp": clp,
+            "row_sel": rsel, "col_sel": csel, "workspace": ws}
 
 
 @dataclass
@@ -254,9 +254,9 @@ def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, str
 
 def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, stream=None):
     """The four calls back to back on one stream; returns every intermediate."""
-    a, b = router_logits(x, wr_t, wc_t, row_bias, col_bias, stream=stream)
-    sel = product_topk(a, b, kprime, K, stream=stream)
+    zr, zc = router_logits(x, wr_t, wc_t, row_bias, col_bias, stream=stream)
+    sel = product_topk(zr, zc, kprime, K, stream=stream)
     N = wr_t.shape[0] * wc_t.shape[0]
     sched = schedule_tasks(sel["expert_idx"], sel["gate"], N, B, stream=stream)
     y = atomic_forward(x, w, v, sched, stream=stream)
-    return {"row_logp": a, "col_logp": b, **sel, "schedule": sched, "y": y}
+    return {"row_logits": zr, "col_logits": zc, **sel, "schedule": sched, "y": y}

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -35,16 +35,15 @@ const char* omni_status_string(omni_status s) {
 
 omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc, const void* x,
                                const void* wr_t, const void* wc_t, const float* row_bias,
-                               const float* col_bias, float* row_logp, float* col_logp,
+                               const float* col_bias, float* row_logits, float* col_logits,
                                hipStream_t stream) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
   if (L < 0 || d < 1 || Nr < 1 || Nc < 1) return OMNI_ERR_INVALID_ARG;
   if (!wr_t || !wc_t) return OMNI_ERR_INVALID_ARG;
-  if (L > 0 && (!x || !row_logp || !col_logp)) return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && (!x || !row_logits || !col_logits)) return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(L) * d) || !fits_i32(static_cast<long long>(L) * Nr) ||
       !fits_i32(static_cast<long long>(L) * Nc) ||
-      !fits_i32(static_cast<long long>(Nr + static_cast<long long>(Nc)) * d) ||
-      !fits_i32(2ll * L))
+      !fits_i32(static_cast<long long>(Nr + static_cast<long long>(Nc)) * d))
     return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(wr_t) || !aligned16(wc_t))
     return OMNI_ERR_INVALID_ARG;
@@ -54,39 +53,43 @@ omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc, cons
   hipError_t e;
   if (dt == OMNI_BF16)
     e = omni::launch_router_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr_t),
-                                 static_cast<const uint16_t*>(wc_t), row_bias, col_bias, row_logp,
-                                 col_logp, L, d, Nr, Nc, stream);
+                                 static_cast<const uint16_t*>(wc_t), row_bias, col_bias,
+                                 row_logits, col_logits, L, d, Nr, Nc, stream);
   else
     e = omni::launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(wr_t),
-                                static_cast<const float*>(wc_t), row_bias, col_bias, row_logp,
-                                col_logp, L, d, Nr, Nc, stream);
-  if (e != hipSuccess) return OMNI_ERR_HIP;
-  return hip_status(omni::launch_log_softmax(row_logp, col_logp, L, Nr, Nc, stream));
+                                static_cast<const float*>(wc_t), row_bias, col_bias, row_logits,
+                                col_logits, L, d, Nr, Nc, stream);
+  return hip_status(e);
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Workspace of omni_product_topk: a tie flag per token, then room for the
-// per-axis lists when the caller does not ask for them.
+// Workspace of omni_product_topk: a tie flag and the two float32 normalisers
+// per token, then room for the per-axis lists when the caller does not ask
+// for them.
+static size_t topk_ws_lists_offset(int L) {
+  return align256(static_cast<size_t>(L) * 4) + align256(static_cast<size_t>(L) * 8);
+}
+
 size_t omni_product_topk_workspace(int L, int Nr, int Nc, int kprime, int K) {
   (void)Nr; (void)Nc; (void)K;
   if (L <= 0 || kprime < 1) return 0;
-  return align256(static_cast<size_t>(L) * 4) +
+  return topk_ws_lists_offset(L) +
          2 * align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
 }
 
-omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const float* row_logp,
-                              const float* col_logp, int32_t* expert_idx, float* score,
-                              float* gate, int32_t* row_sel, int32_t* col_sel, void* ws,
-                              size_t ws_bytes, hipStream_t stream) {
+omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const float* row_logits,
+                              const float* col_logits, int32_t* expert_idx, float* score,
+                              float* gate, float* row_logp, float* col_logp, int32_t* row_sel,
+                              int32_t* col_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (L < 0 || Nr < 1 || Nc < 1) return OMNI_ERR_INVALID_ARG;
   if (kprime < 1 || kprime > Nr || kprime > Nc) return OMNI_ERR_INVALID_ARG;
   if (K < 1 || static_cast<long long>(K) > static_cast<long long>(kprime) * kprime)
     return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(Nr) * Nc)) return OMNI_ERR_INVALID_ARG;
-  if (L > 0 && (!row_logp || !col_logp || !expert_idx || !score || !gate))
+  if (L > 0 && (!row_logits || !col_logits || !expert_idx || !score || !gate))
     return OMNI_ERR_INVALID_ARG;
-  if (kprime > 64 || K > 64 || Nr > 4096 || Nc > 4096) return OMNI_ERR_UNSUPPORTED;
+  if (kprime > 64 || K > 64 || Nr > 2048 || Nc > 2048) return OMNI_ERR_UNSUPPORTED;
   if (!fits_i32(static_cast<long long>(L) * Nr) || !fits_i32(static_cast<long long>(L) * Nc) ||
       !fits_i32(static_cast<long long>(L) * K) || !fits_i32(static_cast<long long>(L) * kprime))
     return OMNI_ERR_UNSUPPORTED;
@@ -95,13 +98,14 @@ omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const fl
   if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
   int32_t* flags = reinterpret_cast<int32_t*>(base);
-  const size_t o1 = align256(static_cast<size_t>(L) * 4);
+  float* lse = reinterpret_cast<float*>(base + align256(static_cast<size_t>(L) * 4));
+  const size_t o1 = topk_ws_lists_offset(L);
   const size_t o2 = o1 + align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
   int32_t* rsel = row_sel ? row_sel : reinterpret_cast<int32_t*>(base + o1);
   int32_t* csel = col_sel ? col_sel : reinterpret_cast<int32_t*>(base + o2);
-  return hip_status(omni::launch_product_topk(row_logp, col_logp, L, Nr, Nc, kprime, K,
-                                              expert_idx, score, gate, rsel, csel, flags,
-                                              stream));
+  return hip_status(omni::launch_product_topk(row_logits, col_logits, L, Nr, Nc, kprime, K,
+                                              expert_idx, score, gate, row_logp, col_logp, rsel,
+                                              csel, flags, lse, stream));
 }
 
 int omni_schedule_max_groups(int L, int K, int N, int B) {

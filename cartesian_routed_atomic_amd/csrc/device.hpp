@@ -14,45 +14,85 @@ __device__ __forceinline__ int lane() { return static_cast<int>(__lane_id()); }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// DPP helpers: v from the lane selected by `ctrl` (lanes without a source,
+// or in rows left out by `row_mask`, get `old`).
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, old), __builtin_bit_cast(int, v), ctrl, row_mask, 0xf, false));
+}
+// Wave-wide sum with DPP: row_shr 1, 2, 4, 8 builds each 16-lane row's total
+// in its lane 15; row_bcast:15 and row_bcast:31 carry the row totals up to
+// lane 63, which is then broadcast.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<0x111, 0xf>(0.f, v);  // row_shr:1
+  v += dpp_f<0x112, 0xf>(0.f, v);  // row_shr:2
+  v += dpp_f<0x114, 0xf>(0.f, v);  // row_shr:4
+  v += dpp_f<0x118, 0xf>(0.f, v);  // row_shr:8
+  v += dpp_f<0x142, 0xa>(0.f, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xc>(0.f, v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<0x111, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<0x112, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<0x114, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<0x118, 0xf>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<0x142, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<0x143, 0xc>(-INFINITY, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+template <int ctrl, int row_mask>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old), static_cast<int>(v), ctrl, row_mask, 0xf, false));
+}
+__device__ __forceinline__ uint32_t wave_and32(uint32_t v) {
+  v &= dpp_u<0x111, 0xf>(~0u, v);
+  v &= dpp_u<0x112, 0xf>(~0u, v);
+  v &= dpp_u<0x114, 0xf>(~0u, v);
+  v &= dpp_u<0x118, 0xf>(~0u, v);
+  v &= dpp_u<0x142, 0xa>(~0u, v);
+  v &= dpp_u<0x143, 0xc>(~0u, v);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ uint32_t wave_or32(uint32_t v) {
+  v |= dpp_u<0x111, 0xf>(0u, v);
+  v |= dpp_u<0x112, 0xf>(0u, v);
+  v |= dpp_u<0x114, 0xf>(0u, v);
+  v |= dpp_u<0x118, 0xf>(0u, v);
+  v |= dpp_u<0x142, 0xa>(0u, v);
+  v |= dpp_u<0x143, 0xc>(0u, v);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 __device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v &= __shfl_xor(v, o);
-  return v;
+  return (static_cast<uint64_t>(wave_and32(static_cast<uint32_t>(v >> 32))) << 32) |
+         wave_and32(static_cast<uint32_t>(v));
 }
 __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+  return (static_cast<uint64_t>(wave_or32(static_cast<uint32_t>(v >> 32))) << 32) |
+         wave_or32(static_cast<uint32_t>(v));
+}
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside each 16-lane
+// row, then the row totals carried up with row_bcast).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += dpp_u<0x111, 0xf>(0u, v);
+  v += dpp_u<0x112, 0xf>(0u, v);
+  v += dpp_u<0x114, 0xf>(0u, v);
+  v += dpp_u<0x118, 0xf>(0u, v);
+  v += dpp_u<0x142, 0xa>(0u, v);
+  v += dpp_u<0x143, 0xc>(0u, v);
   return v;
 }
 // Inclusive suffix sum over lanes: sum of v over lanes >= this lane.
 __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
-  const int l = lane();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t u = __shfl_down(v, o);
-    if (l + o < 64) v += u;
-  }
-  return v;
+  const uint32_t p = wave_inclusive_scan(v);
+  const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(p), 63));
+  return total - p + v;
 }
 // Inclusive prefix sum over lanes.
 __device__ __forceinline__ int wave_prefix_sum(int v) {
-  const int l = lane();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(v, o);
-    if (l >= o) v += u;
-  }
-  return v;
+  return static_cast<int>(wave_inclusive_scan(static_cast<uint32_t>(v)));
 }
 // Number of set bits of m in lanes below this lane.
 __device__ __forceinline__ int mbcnt(uint64_t m) {

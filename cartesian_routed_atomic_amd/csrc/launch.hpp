@@ -14,12 +14,12 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
 hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
                              const float* rb, const float* cb, float* zr, float* zc,
                              int L, int d, int Nr, int Nc, hipStream_t s);
-hipError_t launch_log_softmax(float* zr, float* zc, int L, int Nr, int Nc, hipStream_t s);
 
 // topk.hip
-hipError_t launch_product_topk(const float* a, const float* b, int L, int Nr, int Nc, int kp,
+hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, int Nc, int kp,
                                int K, int32_t* expert_idx, float* score, float* gate,
-                               int32_t* row_sel, int32_t* col_sel, int32_t* tie_flag,
+                               float* row_logp, float* col_logp, int32_t* row_sel,
+                               int32_t* col_sel, int32_t* tie_flag, float* lse,
                                hipStream_t s);
 
 // schedule.hip

@@ -1,13 +1,11 @@
-// Cartesian Product Router, part 1: row / column logits and their
-// log-softmax.  Pages: gist.science explainer §2.2 "Cartesian Product
-// Router" (two small projections give row and column logits over the
-// Nr x Nc grid) and the interactive explainer "Cartesian Product Router"
-// (the scores are combined in log space).
+// Cartesian Product Router, part 1: row / column logits.  Pages: gist.science
+// explainer §2.2 "Cartesian Product Router" (two small projections give row
+// and column logits over the Nr x Nc grid).
 //
 // The projection is one dense contraction z = x . [Wr | Wc] of shape
 // L x d x (Nr + Nc), so the bf16 path runs it on the gfx950 matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A second kernel turns each
-// row of z into log-probabilities in place.
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  The per-axis log-softmax
+// is fused into the selection kernel, which reads each row once anyway.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -149,28 +147,6 @@ __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
   else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = s + (cb ? cb[n - Nr] : 0.f);
 }
 
-// In-place log-softmax of each row of zr [L, Nr] and zc [L, Nc]: one wave
-// per row, a = z - (m + ln sum exp(z - m)).
-__global__ __launch_bounds__(256) void log_softmax_kernel(float* __restrict__ zr,
-                                                          float* __restrict__ zc, int L, int Nr,
-                                                          int Nc) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= 2 * L) return;
-  const int l = lane();
-  float* z;
-  int n;
-  if (row < L) { z = zr + static_cast<size_t>(row) * Nr; n = Nr; }
-  else { z = zc + static_cast<size_t>(row - L) * Nc; n = Nc; }
-  float m = -INFINITY;
-  for (int i = l; i < n; i += 64) m = fmaxf(m, z[i]);
-  m = wave_max(m);
-  float s = 0.f;
-  for (int i = l; i < n; i += 64) s += expf(z[i] - m);
-  s = wave_sum(s);
-  const float lse = m + logf(s);
-  for (int i = l; i < n; i += 64) z[i] = z[i] - lse;
-}
-
 hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
                               const float* rb, const float* cb, float* zr, float* zc, int L,
                               int d, int Nr, int Nc, hipStream_t s) {
@@ -188,12 +164,6 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc, c
   const size_t n = static_cast<size_t>(L) * (Nr + Nc);
   router_gemm_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
       x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc);
-  return hipGetLastError();
-}
-
-hipError_t launch_log_softmax(float* zr, float* zc, int L, int Nr, int Nc, hipStream_t s) {
-  if (L == 0) return hipSuccess;
-  log_softmax_kernel<<<(2 * L + 3) / 4, 256, 0, s>>>(zr, zc, L, Nr, Nc);
   return hipGetLastError();
 }
 

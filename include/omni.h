@@ -7,11 +7,12 @@
  * interactive explainer, sections "Atomic Expert / DEA", "Cartesian Product
  * Router", "Expert-Centric Scheduling"):
  *
- *   1. omni_router_logits   row / column log-probabilities of the Cartesian
- *                           Product Router over an Nr x Nc expert grid;
- *   2. omni_product_topk    per-axis top-k', then top-K over the k' x k'
- *                           product cells with S = log p_r[i] + log p_c[j],
- *                           plus the gates (softmax over the K selected S);
+ *   1. omni_router_logits   row / column logits of the Cartesian Product
+ *                           Router over an Nr x Nc expert grid;
+ *   2. omni_product_topk    per-axis log-softmax and top-k', then top-K over
+ *                           the k' x k' product cells with
+ *                           S = log p_r[i] + log p_c[j], plus the gates
+ *                           (softmax over the K selected S);
  *   3. omni_schedule_tasks  Expert-Centric Scheduling: flatten the L*K
  *                           (token, expert, gate) tasks, group the unique
  *                           active experts B at a time, order the tasks by
@@ -59,66 +60,70 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);
+int omni_abi_version(void);  /* 2 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
 
 /*
- * omni_router_logits — Cartesian Product Router, row and column scores.
+ * omni_router_logits — Cartesian Product Router, row and column logits.
  * Pages: gist.science explainer §2.2 "Cartesian Product Router" (two small
- * projections give independent low-dimensional row and column logits) and
- * the interactive explainer, "Cartesian Product Router" (p(i,j|x) is taken as
- * p_r(i|x) p_c(j|x); scores are combined in log space).
+ * projections give independent low-dimensional row and column logits over
+ * the Nr x Nc grid).
  *
- *   row_logp[t, i] = log_softmax_i( x[t,:] . Wr[:, i] + row_bias[i] )
- *   col_logp[t, j] = log_softmax_j( x[t,:] . Wc[:, j] + col_bias[j] )
+ *   row_logits[t, i] = x[t,:] . Wr[:, i] + row_bias[i]
+ *   col_logits[t, j] = x[t,:] . Wc[:, j] + col_bias[j]
  *
- * dt        OMNI_BF16 (MFMA path) or OMNI_F32.
- * x         [L, d] of dt.
- * wr_t      [Nr, d] of dt: row i holds the d weights that score grid row i
- *           (Wr of the pages, Wr in R^{d x Nr}, stored transposed).
- * wc_t      [Nc, d] of dt, likewise for grid columns.
- * row_bias  [Nr] float32 or NULL;  col_bias [Nc] float32 or NULL.
- * row_logp  [L, Nr] float32 out;   col_logp [L, Nc] float32 out.
+ * dt          OMNI_BF16 (MFMA path, float32 accumulation) or OMNI_F32.
+ * x           [L, d] of dt.
+ * wr_t        [Nr, d] of dt: row i holds the d weights that score grid row i
+ *             (Wr of the pages, Wr in R^{d x Nr}, stored transposed).
+ * wc_t        [Nc, d] of dt, likewise for grid columns.
+ * row_bias    [Nr] float32 or NULL;  col_bias [Nc] float32 or NULL.
+ * row_logits  [L, Nr] float32 out;   col_logits [L, Nc] float32 out.
  * Requires L >= 0, d >= 1, Nr >= 1, Nc >= 1; for bf16 d % 8 == 0 and
  * x, wr_t, wc_t 16-byte aligned; for f32 d % 4 == 0 and 16-byte aligned.
  */
 omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc,
                                const void* x, const void* wr_t, const void* wc_t,
                                const float* row_bias, const float* col_bias,
-                               float* row_logp, float* col_logp,
+                               float* row_logits, float* col_logits,
                                hipStream_t stream);
 
 /*
- * omni_product_topk — top-K over the product grid, and the gates.
- * Pages: interactive explainer, "Cartesian Product Router" (rows and
- * columns are searched separately; the joint score S_ij = log p_r[i] +
- * log p_c[j] is additive in log space and the N-entry score matrix is never
- * formed) and "Expert-Centric Scheduling" (each routing decision carries a
- * weight).
+ * omni_product_topk — per-axis log-probabilities, top-K over the product
+ * grid, and the gates.
+ * Pages: interactive explainer, "Cartesian Product Router" (p(i,j|x) is
+ * taken as p_r(i|x) p_c(j|x); rows and columns are searched separately; the
+ * joint score S_ij = log p_r[i] + log p_c[j] is additive in log space and the
+ * N-entry score matrix is never formed) and "Expert-Centric Scheduling"
+ * (each routing decision carries a weight).
  *
- * Per token t: R = the k' best rows of row_logp[t] (value desc, index asc),
- * C = the k' best columns of col_logp[t]; over the k' x k' cells
- * S = fl32(row_logp[t,R_r] + col_logp[t,C_c]), e = R_r * Nc + C_c, keep the
- * K best by (S desc, e asc) in rank order.
+ * Per token t: a = row_logits[t] - LSE(row_logits[t]) and b likewise for the
+ * columns (float32, LSE = m + ln sum exp(z - m)); R = the k' best rows of a
+ * (value desc, index asc), C = the k' best columns of b; over the k' x k'
+ * cells S = fl32(a[R_r] + b[C_c]), e = R_r * Nc + C_c, keep the K best by
+ * (S desc, e asc) in rank order.
  *
  * expert_idx [L, K] int32 out (rank order); score [L, K] float32 out (S);
  * gate [L, K] float32 out: g_k = exp(S_k - S_0) / sum_j exp(S_j - S_0).
+ * row_logp [L, Nr], col_logp [L, Nc] float32 out (a and b), each may be NULL.
  * row_sel, col_sel: [L, k'] int32 out (R and C in rank order), each may be
  * NULL.
  * ws / ws_bytes: workspace of at least omni_product_topk_workspace(...)
- * bytes, 256-byte aligned (a tie flag per token and, for NULL row_sel /
- * col_sel, the per-axis lists).
+ * bytes, 256-byte aligned (a tie flag and two normalisers per token and, for
+ * NULL row_sel / col_sel, the per-axis lists).
  * Requires 1 <= k' <= min(Nr, Nc), 1 <= K <= k'^2, Nr * Nc < 2^31.
- * Kernels cover k' <= 64, K <= 64 and Nr, Nc <= 4096 (else UNSUPPORTED).
- * Selection and scores are exact functions of the float32 inputs; gates are
- * float32 (expf, wave-order sum).
+ * Kernels cover k' <= 64, K <= 64 and Nr, Nc <= 2048 (else UNSUPPORTED).
+ * Given a and b, selection and scores are exact functions of them (the same
+ * a and b are written to row_logp / col_logp); gates are float32 (expf,
+ * wave-order sum).
  */
 size_t omni_product_topk_workspace(int L, int Nr, int Nc, int kprime, int K);
 omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K,
-                              const float* row_logp, const float* col_logp,
+                              const float* row_logits, const float* col_logits,
                               int32_t* expert_idx, float* score, float* gate,
+                              float* row_logp, float* col_logp,
                               int32_t* row_sel, int32_t* col_sel,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -88,8 +88,18 @@ def router_logp(x, wr_t, wc_t, row_bias=None, col_bias=None):
     return log_softmax_rows(zr).astype(np.float32), log_softmax_rows(zc).astype(np.float32)
 
 
+def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None):
+    """Row and column router logits z_r [L, Nr], z_c [L, Nc], float64 -> float32.
+
+    [GS-NL §2.2, Cartesian Product Router]: two small projections Wr, Wc give
+    independent row and column logits.  z_r = x . Wr (+ row_bias).
+    """
+    zr, zc = router_logits_f64(x, wr_t, wc_t, row_bias, col_bias)
+    return zr.astype(np.float32), zc.astype(np.float32)
+
+
 def router_logits_f64(x, wr_t, wc_t, row_bias=None, col_bias=None):
-    """The raw logits z_r, z_c of router_logp, in float64 (for diagnostics)."""
+    """The raw logits z_r, z_c of router_logp, in float64."""
     xf = widen(x)
     zr = xf @ widen(wr_t).T
     zc = xf @ widen(wc_t).T

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 1
+    assert lib.omni_abi_version() == 2
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -74,7 +74,8 @@ def test_product_topk_argument_checks(lib):
     f = lib.omni_product_topk
 
     def call(L=4, Nr=16, Nc=16, kp=4, K=4, ws=None, nws=0):
-        return f(L, Nr, Nc, kp, K, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, ws, nws, None)
+        return f(L, Nr, Nc, kp, K, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, ws, nws,
+                 None)
     assert call(kp=0) == B.OMNI_ERR_INVALID_ARG
     assert call(kp=17) == B.OMNI_ERR_INVALID_ARG         # k' > Nr
     assert call(kp=4, K=17) == B.OMNI_ERR_INVALID_ARG    # K > k'^2
@@ -82,7 +83,7 @@ def test_product_topk_argument_checks(lib):
     assert call(Nr=1 << 16, Nc=1 << 16, kp=4) == B.OMNI_ERR_INVALID_ARG  # N >= 2^31
     assert call(Nr=128, Nc=128, kp=65, K=8) == B.OMNI_ERR_UNSUPPORTED
     assert call(Nr=128, Nc=128, kp=64, K=65) == B.OMNI_ERR_UNSUPPORTED
-    assert call(Nr=8192, Nc=16, kp=4, K=4) == B.OMNI_ERR_UNSUPPORTED
+    assert call(Nr=4096, Nc=16, kp=4, K=4) == B.OMNI_ERR_UNSUPPORTED
     assert call(L=0) == B.OMNI_OK
     nws = lib.omni_product_topk_workspace(8192, 1024, 1024, 64, 64)
     assert nws >= 8192 * 4 + 2 * 8192 * 64 * 4

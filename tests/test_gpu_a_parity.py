@@ -24,12 +24,19 @@ B = pytest.importorskip("cartesian_routed_atomic_amd.binding")
 TOL_Y = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def check_router(inp, a, b):
+def check_router(inp, out):
+    """Logits vs the oracle's router; log-probabilities vs the oracle's
+    log-softmax of the GPU's own logits and vs the oracle end to end."""
+    zr, zc = O.router_logits(inp["x"], inp["wr"], inp["wc"], inp["row_bias"], inp["col_bias"])
+    gzr, gzc = host(out["row_logits"]), host(out["col_logits"])
+    dz = max(float(np.abs(gzr - zr).max()), float(np.abs(gzc - zc).max()))
+    ga, gb = host(out["row_logp"]), host(out["col_logp"])
+    dl = max(float(np.abs(ga - O.log_softmax_rows(gzr)).max()),
+             float(np.abs(gb - O.log_softmax_rows(gzc)).max()))
     ea, eb = O.router_logp(inp["x"], inp["wr"], inp["wc"], inp["row_bias"], inp["col_bias"])
-    da = float(np.abs(host(a) - ea).max())
-    db = float(np.abs(host(b) - eb).max())
-    log(f"  router max|d| rows {da:.2e} cols {db:.2e}")
-    assert da <= 1e-4 and db <= 1e-4
+    de = max(float(np.abs(ga - ea).max()), float(np.abs(gb - eb).max()))
+    log(f"  router logits max|d| {dz:.2e}; log-softmax of own logits {dl:.2e}; end to end {de:.2e}")
+    assert dz <= 1e-4 and dl <= 1e-5 and de <= 1e-4
 
 
 def check_topk(a, b, sel, kp, K, tokens=None):
@@ -115,7 +122,7 @@ def test_stage_parity(name):
         f"K={wl.K} B={wl.B} {wl.dtype}")
     inp = make_inputs(wl)
     out = run_pipeline(wl, inp)
-    check_router(inp, out["row_logp"], out["col_logp"])
+    check_router(inp, out)
     check_topk(out["row_logp"], out["col_logp"], out, wl.kprime, wl.K)
     check_schedule(out, out["schedule"], wl.N, wl.B)
     check_y(inp, out, out["y"], wl.dtype)
@@ -154,13 +161,16 @@ def test_topk_with_ties_is_bit_exact(Nr, Nc, kp, K, step):
     # Quantised inputs produce many equal values, so ties decide the order and
     # the merge's exact fallback (a tie at the staircase threshold) runs.
     L = 97
-    a = _tied_logp(L, Nr, step, Nr)
-    b = _tied_logp(L, Nc, step, Nc + 1)
-    a[0, :3] = [0.0, -0.0, 0.0]           # -0 and +0 compare equal
-    b[0, :2] = [-0.0, 0.0]
-    sel = B.product_topk(dev(a), dev(b), kp, K)
+    za = _tied_logp(L, Nr, step, Nr)
+    zb = _tied_logp(L, Nc, step, Nc + 1)
+    za[0, :3] = [0.0, -0.0, 0.0]
+    zb[0, :2] = [-0.0, 0.0]
+    sel = B.product_topk(dev(za), dev(zb), kp, K)
     torch.cuda.synchronize()
-    check_topk(dev(a), dev(b), sel, kp, K)
+    # equal logits stay equal after the float32 normalisation: ties persist
+    check_topk(sel["row_logp"], sel["col_logp"], sel, kp, K)
+    dl = float(np.abs(host(sel["row_logp"]) - O.log_softmax_rows(za)).max())
+    assert dl <= 1e-5
 
 
 def _zipf_ids(L, K, N, s, seed):

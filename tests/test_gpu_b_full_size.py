@@ -31,7 +31,7 @@ def test_full_size_parity(name):
     torch.cuda.synchronize()
     del t
     log(f"  gpu done {time.time() - t0:.1f}s")
-    check_router(inp, out["row_logp"], out["col_logp"])
+    check_router(inp, out)
     rng = np.random.default_rng(0)
     toks = np.sort(rng.choice(wl.L, size=min(wl.L, 512), replace=False))
     check_topk(out["row_logp"], out["col_logp"], out, wl.kprime, wl.K, tokens=toks)
