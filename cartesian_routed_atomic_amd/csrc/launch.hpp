@@ -25,7 +25,7 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
 // schedule.hip
 struct ScheduleWs {
   size_t bytes;
-  size_t flags, tile_cnt, rank, key0, val0, key1, val1, hist;  // byte offsets
+  size_t flags, tile_cnt, rank, key0, val0, key1, val1, hist, dtot;  // byte offsets
   int n_ftiles, n_ttiles, passes, max_groups;
 };
 ScheduleWs schedule_ws_layout(int L, int K, int N, int B);

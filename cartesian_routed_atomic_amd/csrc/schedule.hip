@@ -11,19 +11,22 @@
 //   2. count flags per 4096-expert tile; each tile sums the counts of the
 //      tiles before it, scans its own flags and writes rank[e] (position
 //      among active experts) and the ascending active list;
-//   3. key[m] = rank[e_m] / B, the group of task m;
-//   4. stable LSD radix sort of the tasks by group, 8 bits per pass.  Tasks
-//      enter in flatten order m = t*K + k, which is already token-major, so a
-//      stable sort by group alone yields (group, token) order with ties in
-//      flatten order.  Each pass: per-tile digit histograms, one exclusive
-//      scan, then a stable scatter ranked with 8 ballots per element;
-//   5. CSR group offsets from the group boundaries of the sorted keys.
+//   3. stable LSD radix sort of the tasks by group g = rank[e] / B, 8 bits
+//      per pass.  Tasks enter in flatten order m = t*K + k, which is already
+//      token-major, so a stable sort by group alone yields (group, token)
+//      order with ties in flatten order.  Each pass: per-tile digit
+//      histograms (the first pass computes the group keys on the way), a
+//      parallel scan of each digit's row of tile counts, then a stable
+//      scatter ranked with 8 ballots per element.  Passes beyond the digits
+//      that n_groups actually needs return at once;
+//   4. CSR group offsets from the group boundaries of the sorted keys.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace omni {
 
-constexpr int kTile = 4096;  // elements per workgroup tile (256 threads x 16)
+constexpr int kTile = 4096;   // experts per flag tile (256 threads x 16)
+constexpr int kSTile = 2048;  // tasks per sort tile (512 threads x 4)
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -31,12 +34,13 @@ ScheduleWs schedule_ws_layout(int L, int K, int N, int B) {
   ScheduleWs w{};
   const long long M = static_cast<long long>(L) * K;
   w.n_ftiles = static_cast<int>((static_cast<long long>(N) + kTile - 1) / kTile);
-  w.n_ttiles = static_cast<int>((M + kTile - 1) / kTile);
+  w.n_ttiles = static_cast<int>((M + kSTile - 1) / kSTile);
   const long long mn = M < N ? M : N;
   w.max_groups = static_cast<int>((mn + B - 1) / B);
   int bits = 0;
   while (bits < 31 && (1ll << bits) < w.max_groups) ++bits;  // groups are < max_groups
   w.passes = bits <= 8 ? 1 : (bits + 7) / 8;
+  const size_t nt = static_cast<size_t>(w.n_ttiles > 0 ? w.n_ttiles : 1);
   size_t o = 0;
   w.flags = o;    o = align256(o + static_cast<size_t>(w.n_ftiles) * kTile);
   w.tile_cnt = o; o = align256(o + static_cast<size_t>(w.n_ftiles) * 4);
@@ -45,9 +49,21 @@ ScheduleWs schedule_ws_layout(int L, int K, int N, int B) {
   w.val0 = o;     o = align256(o + static_cast<size_t>(M) * 4);
   w.key1 = o;     o = align256(o + static_cast<size_t>(M) * 4);
   w.val1 = o;     o = align256(o + static_cast<size_t>(M) * 4);
-  w.hist = o;     o = align256(o + static_cast<size_t>(256) * (w.n_ttiles > 0 ? w.n_ttiles : 1) * 4);
+  w.hist = o;     o = align256(o + 256 * nt * 4);
+  w.dtot = o;     o = align256(o + 256 * 4);
   w.bytes = o;
   return w;
+}
+
+// Passes that n_groups actually needs: max group id n_groups - 1 < 256^eff.
+__device__ __forceinline__ int effective_passes(int n_groups) {
+  int eff = 1;
+  long long lim = 256;
+  while (static_cast<long long>(n_groups) > lim && eff < 4) {
+    ++eff;
+    lim <<= 8;
+  }
+  return eff;
 }
 
 __global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, size_t n16) {
@@ -124,88 +140,98 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ f
   (void)N;
 }
 
-__global__ __launch_bounds__(256) void group_key_kernel(const int32_t* __restrict__ idx,
-                                                        const int* __restrict__ rank, int M, int N,
-                                                        int B, int* __restrict__ key) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= M) return;
-  const int e = idx[m];
-  key[m] = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? rank[e] / B : 0;
-}
-
-__global__ __launch_bounds__(256) void radix_up_kernel(const int* __restrict__ key, int M,
-                                                       int shift, int n_tt,
-                                                       int* __restrict__ hist) {
+// Per-tile digit histogram, digit-major: hist[d * n_tt + tile].  The first
+// pass computes the group key of each task (kout) on the way.
+__global__ __launch_bounds__(512) void radix_up_kernel(
+    const int* __restrict__ kin, const int32_t* __restrict__ idx, const int* __restrict__ rank,
+    int* __restrict__ kout, int M, int N, int B, int pass, int n_tt,
+    const int* __restrict__ counts, int* __restrict__ hist) {
+  if (pass >= effective_passes(counts[1])) return;
   __shared__ uint32_t h[256];
-  h[threadIdx.x] = 0;
+  if (threadIdx.x < 256) h[threadIdx.x] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kTile;
-#pragma unroll 4
-  for (int r = 0; r < 16; ++r) {
-    const int i = base + r * 256 + threadIdx.x;
-    if (i < M) atomicAdd(&h[(static_cast<uint32_t>(key[i]) >> shift) & 255], 1u);
+  const int shift = 8 * pass;
+  const int base = blockIdx.x * kSTile;
+#pragma unroll
+  for (int r = 0; r < kSTile / 512; ++r) {
+    const int i = base + r * 512 + threadIdx.x;
+    if (i >= M) continue;
+    int key;
+    if (pass == 0) {
+      const int e = idx[i];
+      key = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? rank[e] / B : 0;
+      kout[i] = key;
+    } else {
+      key = kin[i];
+    }
+    atomicAdd(&h[(static_cast<uint32_t>(key) >> shift) & 255], 1u);
   }
   __syncthreads();
-  hist[threadIdx.x * n_tt + blockIdx.x] = static_cast<int>(h[threadIdx.x]);
+  if (threadIdx.x < 256) hist[threadIdx.x * n_tt + blockIdx.x] = static_cast<int>(h[threadIdx.x]);
 }
 
-// Exclusive scan of n ints in place, one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ a, int n) {
-  __shared__ int wpre[16];
-  __shared__ int total_s;
-  const int tid = threadIdx.x, w = tid >> 6, l = lane();
-  int carry = 0;
-  for (int base = 0; base < n; base += 4096) {
-    int v[4];
-    int s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = base + tid * 4 + q;
-      v[q] = i < n ? a[i] : 0;
-      s += v[q];
-    }
-    const int inc = wave_prefix_sum(s);
-    if (l == 63) wpre[w] = inc;
-    __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int q = 0; q < 16; ++q) { const int t = wpre[q]; wpre[q] = acc; acc += t; }
-      total_s = acc;
-    }
-    __syncthreads();
-    int run = carry + wpre[w] + inc - s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = base + tid * 4 + q;
-      if (i < n) a[i] = run;
-      run += v[q];
-    }
-    carry += total_s;
-    __syncthreads();
+// Exclusive scan of each digit's row of tile counts; the row total goes to
+// dtot[d].  One wave per digit.
+__global__ __launch_bounds__(64) void radix_rowscan_kernel(int* __restrict__ hist, int n_tt,
+                                                           int pass,
+                                                           const int* __restrict__ counts,
+                                                           int* __restrict__ dtot) {
+  if (pass >= effective_passes(counts[1])) return;
+  int* row = hist + static_cast<size_t>(blockIdx.x) * n_tt;
+  const int l = lane();
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < n_tt; b0 += 64) {
+    const int b = b0 + l;
+    const uint32_t v = b < n_tt ? static_cast<uint32_t>(row[b]) : 0u;
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (b < n_tt) row[b] = static_cast<int>(carry + inc - v);
+    carry += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
   }
+  if (l == 0) dtot[blockIdx.x] = static_cast<int>(carry);
 }
 
-// Stable scatter of one radix pass.  Wave w of a tile ranks its 1024
-// consecutive elements 64 at a time: lanes with the same digit find each
-// other with 8 ballots, the lowest of them bumps the wave's running count.
-__global__ __launch_bounds__(256) void radix_down_kernel(
-    const int* __restrict__ kin, const int* __restrict__ vin, int M, int shift, int n_tt,
-    const int* __restrict__ hscan, int* __restrict__ kout, int* __restrict__ vout, int K,
+// Stable scatter of one pass.  Wave w of a tile ranks its 256 consecutive
+// elements 64 at a time: lanes with the same digit find each other with 8
+// ballots, the lowest of them bumps the wave's running count.  The last
+// effective pass also writes the task arrays.
+__global__ __launch_bounds__(512) void radix_down_kernel(
+    const int* __restrict__ kin, const int* __restrict__ vin, int M, int pass, int n_tt,
+    const int* __restrict__ hist, const int* __restrict__ dtot, const int* __restrict__ counts,
+    int* __restrict__ kout, int* __restrict__ vout, int K,
     const int32_t* __restrict__ expert_idx, const float* __restrict__ gate,
     int32_t* __restrict__ task_token, int32_t* __restrict__ task_expert,
     float* __restrict__ task_gate, int32_t* __restrict__ task_index) {
-  __shared__ uint32_t wh[4][256];
+  const int eff = effective_passes(counts[1]);
+  if (pass >= eff) return;
+  const bool last = pass == eff - 1;
+  constexpr int kW = 8, kR = kSTile / (kW * 64);
+  __shared__ uint32_t wh[kW][256];
   __shared__ uint32_t goff[256];
+  __shared__ uint32_t red[4];
   const int tid = threadIdx.x, w = tid >> 6, l = lane();
-  wh[0][tid] = 0; wh[1][tid] = 0; wh[2][tid] = 0; wh[3][tid] = 0;
-  goff[tid] = static_cast<uint32_t>(hscan[tid * n_tt + blockIdx.x]);
+  for (int q = 0; q < kW; ++q)
+    if (tid < 256) wh[q][tid] = 0;
+  // digit base: exclusive scan of the digit totals (first 4 waves, 64 each)
+  if (tid < 256) {
+    const uint32_t v = static_cast<uint32_t>(dtot[tid]);
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (l == 63) red[w] = inc;
+    goff[tid] = inc - v;
+  }
   __syncthreads();
-  const int base = blockIdx.x * kTile + w * 1024;
+  if (tid < 256) {
+    uint32_t add = 0;
+    for (int q = 0; q < w; ++q) add += red[q];
+    goff[tid] += add + static_cast<uint32_t>(hist[tid * n_tt + blockIdx.x]);
+  }
+  __syncthreads();
+  const int shift = 8 * pass;
+  const int base = blockIdx.x * kSTile + w * (kR * 64);
   const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  uint32_t dg[16], lr[16];
-  int kv[16], vv[16];
+  uint32_t dg[kR], lr[kR];
+  int kv[kR], vv[kR];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 0; r < kR; ++r) {
     const int i = base + r * 64 + l;
     const bool valid = i < M;
     const int k = valid ? kin[i] : 0;
@@ -229,23 +255,25 @@ __global__ __launch_bounds__(256) void radix_down_kernel(
     vv[r] = v;
   }
   __syncthreads();
-  {
-    const uint32_t c0 = wh[0][tid], c1 = wh[1][tid], c2 = wh[2][tid];
-    wh[0][tid] = 0;
-    wh[1][tid] = c0;
-    wh[2][tid] = c0 + c1;
-    wh[3][tid] = c0 + c1 + c2;
+  if (tid < 256) {  // exclusive prefix of the per-wave counts of each digit
+    uint32_t run = 0;
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      const uint32_t c = wh[q][tid];
+      wh[q][tid] = run;
+      run += c;
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 0; r < kR; ++r) {
     const int i = base + r * 64 + l;
     if (i >= M) continue;
     const uint32_t pos = goff[dg[r]] + wh[w][dg[r]] + lr[r];
     if (pos >= static_cast<uint32_t>(M)) continue;  // unreachable when counts agree
     kout[pos] = kv[r];
     vout[pos] = vv[r];
-    if (task_token) {
+    if (last) {
       const int m = vv[r];
       task_token[pos] = m / K;
       task_expert[pos] = expert_idx[m];
@@ -256,11 +284,15 @@ __global__ __launch_bounds__(256) void radix_down_kernel(
 }
 
 // CSR offsets: off[g] = first sorted position of group g (groups are never
-// empty); entries from n_groups to G hold M.
-__global__ __launch_bounds__(256) void offsets_kernel(const int* __restrict__ skey, int M, int G,
-                                                      const int* __restrict__ counts,
+// empty); entries from n_groups to G hold M.  The sorted keys are those of
+// the last effective pass.
+__global__ __launch_bounds__(256) void offsets_kernel(const int* __restrict__ skey_even,
+                                                      const int* __restrict__ skey_odd, int M,
+                                                      int G, const int* __restrict__ counts,
                                                       int* __restrict__ off) {
   const int i = blockIdx.x * 256 + threadIdx.x;
+  const int eff = effective_passes(counts[1]);
+  const int* skey = ((eff - 1) & 1) ? skey_odd : skey_even;
   if (i < M) {
     const int g = min(skey[i], G - 1);
     const int gp = i ? min(skey[i - 1], G - 1) : -1;
@@ -298,6 +330,7 @@ hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx
   int* key1 = reinterpret_cast<int*>(base + lay.key1);
   int* val1 = reinterpret_cast<int*>(base + lay.val1);
   int* hist = reinterpret_cast<int*>(base + lay.hist);
+  int* dtot = reinterpret_cast<int*>(base + lay.dtot);
 
   const size_t n16 = static_cast<size_t>(lay.n_ftiles) * kTile / 16;
   zero16_kernel<<<blocks_for(static_cast<long long>(n16), 256), 256, 0, s>>>(
@@ -306,27 +339,23 @@ hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx
   tile_count_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, tile_cnt);
   rank_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, N, tile_cnt, lay.n_ftiles, B, rank, active,
                                            counts);
-  group_key_kernel<<<blocks_for(M, 256), 256, 0, s>>>(expert_idx, rank, M, N, B, key0);
-
-  int* kin = key0;
-  int* vin = nullptr;  // identity payload on the first pass
-  int* kbuf[2] = {key1, key0};
-  int* vbuf[2] = {val1, val0};
+  // pass p reads (key, val) from buffer p & 1 and writes buffer (p + 1) & 1;
+  // pass 0 reads the group keys it computes itself (key0) and identity values
+  int* kb[2] = {key0, key1};
+  int* vb[2] = {val0, val1};
   for (int p = 0; p < lay.passes; ++p) {
-    const int shift = 8 * p;
-    const bool last = p == lay.passes - 1;
-    int* ko = kbuf[p & 1];
-    int* vo = vbuf[p & 1];
-    radix_up_kernel<<<lay.n_ttiles, 256, 0, s>>>(kin, M, shift, lay.n_ttiles, hist);
-    scan_kernel<<<1, 1024, 0, s>>>(hist, 256 * lay.n_ttiles);
-    radix_down_kernel<<<lay.n_ttiles, 256, 0, s>>>(
-        kin, vin, M, shift, lay.n_ttiles, hist, ko, vo, K, expert_idx, gate,
-        last ? task_token : nullptr, task_expert, task_gate, task_index);
-    kin = ko;
-    vin = vo;
+    int* kin = kb[p & 1];
+    const int* vin = p == 0 ? nullptr : vb[p & 1];
+    radix_up_kernel<<<lay.n_ttiles, 512, 0, s>>>(kin, expert_idx, rank, key0, M, N, B, p,
+                                                 lay.n_ttiles, counts, hist);
+    radix_rowscan_kernel<<<256, 64, 0, s>>>(hist, lay.n_ttiles, p, counts, dtot);
+    radix_down_kernel<<<lay.n_ttiles, 512, 0, s>>>(
+        kin, vin, M, p, lay.n_ttiles, hist, dtot, counts, kb[(p + 1) & 1], vb[(p + 1) & 1], K,
+        expert_idx, gate, task_token, task_expert, task_gate, task_index);
   }
+  // the last effective pass p leaves its sorted keys in kb[(p + 1) & 1]
   const long long nthr = M > lay.max_groups + 1 ? M : lay.max_groups + 1;
-  offsets_kernel<<<blocks_for(nthr, 256), 256, 0, s>>>(kin, M, lay.max_groups, counts,
+  offsets_kernel<<<blocks_for(nthr, 256), 256, 0, s>>>(key1, key0, M, lay.max_groups, counts,
                                                        group_offsets);
   return hipGetLastError();
 }
