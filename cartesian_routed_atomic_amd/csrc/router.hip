@@ -122,6 +122,131 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   }
 }
 
+// Large-shape path (d % 32 == 0): block tile 256 tokens x 256 grid lines,
+// K step 32, 8 waves in 2 x 4, each wave a 128 x 64 sub-tile = 8 x 4 MFMA
+// 16x16x32 tiles (128 float32 accumulators per lane).  Operands go straight
+// from global memory into a 4-stage LDS ring with global_load_lds_dwordx4
+// (three K steps in flight, no register staging).  An LDS row holds 32 bf16
+// (64 B = four 16-B chunks); chunk c of row r is stored at position
+// c ^ ((r >> 2) & 3), so the 16 rows a fragment read touches fall on
+// distinct banks.
+constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4;
+constexpr int GSTAGE_BYTES = (GBM + GBN) * GBK * 2;  // 32 KiB
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ wc, const float* __restrict__ rb,
+    const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[GSTAGES * GSTAGE_BYTES];
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int nblk = n_mt * n_nt;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int logical = xcd * per + min(xcd, rem) + loc;
+  const int mt = logical / n_nt, nt = logical - mt * n_nt;
+  const int m0 = mt * GBM, n0 = nt * GBN;
+  const int NT = Nr + Nc;
+
+  // Direct loads: each wave fills 2 KiB of A (32 rows) and 2 KiB of B per
+  // stage with two 1-KiB instructions each; lane i of an instruction lands
+  // on row r = base + i / 4, stored chunk i % 4, so it fetches logical chunk
+  // (i % 4) ^ ((r >> 2) & 3).  Rows past the end re-read a valid row (their
+  // results are never stored).
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = (wv * 2 + u) * 16 + (l >> 2);
+    const int c = (l & 3) ^ ((r >> 2) & 3);
+    const int t = min(m0 + r, L - 1);
+    asrc[u] = x + static_cast<size_t>(t) * d + c * 8;
+    const int n = min(n0 + r, NT - 1);
+    bsrc[u] = (n < Nr ? wr + static_cast<size_t>(n) * d : wc + static_cast<size_t>(n - Nr) * d) +
+              c * 8;
+  }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % GSTAGES) * GSTAGE_BYTES;
+    const int k0 = kt * GBK;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wv * 2 + u) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + GBM * 64 + (wv * 2 + u) * 1024, 16, 0,
+                                       0);
+    }
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wm = wv >> 2, wn = wv & 3;  // 2 x 4 waves
+  const int fr = l & 15, fc = l >> 4;
+  const int nk = d / GBK;
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = nk - 1 - kt;  // stages issued after this one (at most 2)
+    if (ahead >= 2) wait_vmcnt<8>();
+    else if (ahead == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    // Every wave's loads for stage kt have landed (the wait above) and every
+    // wave is done reading stage kt-1, whose slot the next issue reuses.  A
+    // bare barrier: a fenced one would also wait for the stages still in
+    // flight.
+    __builtin_amdgcn_s_barrier();
+    if (kt + 3 < nk) issue(kt + 3);
+    const uint8_t* st = smem + (kt % GSTAGES) * GSTAGE_BYTES;
+    bf16x8 af[8], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(st + swz(wm * 128 + i * 16 + fr, fc));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(st + GBM * 64 + swz(wn * 64 + j * 16 + fr, fc));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+
+  // Accumulator lane layout (16x16 output tile): column = lane % 16,
+  // rows 4 * (lane / 16) + q, q = 0..3.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 64 + j * 16 + fr;
+    if (n >= NT) continue;
+    const bool is_row = n < Nr;
+    const float bias = is_row ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
+        if (t >= L) continue;
+        const float val = acc[i][j][q] + bias;
+        if (is_row) zr[static_cast<size_t>(t) * Nr + n] = val;
+        else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = val;
+      }
+    }
+  }
+}
+
 // fp32 path (small shapes): one thread per (token, grid line), features in
 // ascending order, float4 loads.
 __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
@@ -151,6 +276,12 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
                               const float* rb, const float* cb, float* zr, float* zc, int L,
                               int d, int Nr, int Nc, hipStream_t s) {
   if (L == 0) return hipSuccess;
+  if (d % GBK == 0) {
+    const int n_mt = (L + GBM - 1) / GBM, n_nt = (Nr + Nc + GBN - 1) / GBN;
+    router_gemm_bf16_big_kernel<<<n_mt * n_nt, 512, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr,
+                                                            Nc, n_mt, n_nt);
+    return hipGetLastError();
+  }
   const int n_mt = (L + RBM - 1) / RBM, n_nt = (Nr + Nc + RBN - 1) / RBN;
   router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc,
                                                       n_mt, n_nt);

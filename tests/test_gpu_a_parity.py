@@ -250,3 +250,18 @@ def test_accumulate_adds_onto_y():
     B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], y=y, accumulate=True)
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(y), host(base) + host(out["y"]), rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("L,d,Nr,Nc", [(77, 40, 24, 40), (300, 200, 96, 33), (513, 2048, 300, 260)])
+def test_router_logits_ragged_shapes(L, d, Nr, Nc):
+    # Token and grid-line counts that leave partial tiles, and feature widths
+    # on both bf16 GEMM paths (d % 32 != 0 and d % 32 == 0).
+    wl = custom(L=L, d=d, Nr=Nr, Nc=Nc, kprime=4, K=4, B=4, dtype="bf16", index=300 + d)
+    inp = make_inputs(wl, ("x", "wr", "wc"))
+    rb = (np.arange(Nr, dtype=np.float32) * 0.01).astype(np.float32)
+    zr, zc = B.router_logits(dev(inp["x"]), dev(inp["wr"]), dev(inp["wc"]), dev(rb), None)
+    torch.cuda.synchronize()
+    er, ec = O.router_logits(inp["x"], inp["wr"], inp["wc"], rb, None)
+    dz = max(float(np.abs(host(zr) - er).max()), float(np.abs(host(zc) - ec).max()))
+    log(f"[router] L={L} d={d} grid={Nr}x{Nc}: max|d| {dz:.2e}")
+    assert dz <= 1e-4
