@@ -3,9 +3,10 @@
 MI355X, with the executor's HBM roofline fraction and the CPU oracle's rate.
 
 A step is one pass of the whole path on one batch: router logits ->
-product top-K + gates -> expert-centric schedule -> expert-centric execute,
-all four C-ABI calls enqueued back to back on one stream, inputs resident in
-HBM, every output buffer allocated before timing.
+product top-K + gates -> expert-centric schedule -> execution of the schedule
+(in the form the library's auto mode picks for the shape; the other form is
+timed beside it), all four C-ABI calls enqueued back to back on one stream,
+inputs resident in HBM, every output buffer allocated before timing.
 
     python bench.py [--steps 50] [--warmup 5] [--workload large]
 
@@ -27,6 +28,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 EXEC_SRC = os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", "execute.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
+EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
+    "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
+    "token": "omni_atomic_forward, token-centric: unpermute_kernel + token_kernel",
+}
 
 
 def say(msg):
@@ -131,7 +136,7 @@ def main():
         max(1, B.lib().omni_atomic_forward_workspace(1, L, wl.d, wl.N, K, wl.B)),
         dtype=torch.uint8, device=dev)
     y = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
-    y2 = torch.zeros_like(y)
+    form = B.atomic_forward_mode(x.dtype, L, wl.d, wl.N, K, wl.B)
 
     def stage_router():
         B.router_logits(x, wr, wc, rb, cb, row_logits=a, col_logits=b)
@@ -175,9 +180,16 @@ def main():
 
     stages = {"router": ev_time(stage_router), "topk": ev_time(stage_topk),
               "schedule": ev_time(stage_schedule), "execute": ev_time(stage_execute)}
-    # the executor kernel alone: accumulate mode skips the y clear
-    exec_ms = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y2, accumulate=True,
-                                               workspace=exec_ws), reps=20)
+    # the executor call alone, in each form (the step runs `form`)
+    forms_ms = {}
+    for f in ("expert", "token"):
+        try:
+            forms_ms[f] = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y,
+                                                           workspace=exec_ws, mode=f), reps=20)
+        except B.OmniError:
+            forms_ms[f] = None
+    exec_ms = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y, workspace=exec_ws),
+                      reps=20)
     counts = sched.counts.cpu().tolist()
     n_active, n_groups = int(counts[0]), int(counts[1])
     s = wl.elem_bytes
@@ -188,9 +200,9 @@ def main():
     router_flop = 2.0 * L * wl.d * (wl.Nr + wl.Nc)
     router_tflops = router_flop / (stages["router"] * 1e-3) / 1e12
     say(f"[bench] stages ms {json.dumps({k: round(v4, 4) for k, v4 in stages.items()})}; "
-        f"executor kernel {exec_ms:.4f} ms, {achieved:.0f} GB/s "
+        f"executor ({form}-centric) {exec_ms:.4f} ms, {achieved:.0f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of HBM); n_active={n_active} "
-        f"n_groups={n_groups}")
+        f"n_groups={n_groups}; forms ms {forms_ms}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -216,8 +228,10 @@ def main():
                    "zipf_s": wl.zipf_s},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "atomic_forward_kernel", "bytes_alg": bytes_alg,
+                     "kernel": EXEC_KERNELS[form], "bytes_alg": bytes_alg,
                      "kernel_ms": exec_ms},
+        "executor_form": form,
+        "executor_forms_ms": forms_ms,
         "router_mfma": {"achieved": router_tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": router_tflops / MFMA_BF16_TFLOPS,
                         "note": "router call = one MFMA GEMM kernel (bias fused)"},

@@ -17,13 +17,15 @@ LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
+EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
+ABI_VERSION = 3
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
     "omni_abi_version", "omni_status_string", "omni_router_logits",
     "omni_product_topk_workspace", "omni_product_topk", "omni_schedule_max_groups",
-    "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_workspace",
-    "omni_atomic_forward",
+    "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_mode",
+    "omni_atomic_forward_workspace", "omni_atomic_forward",
 )
 
 
@@ -51,9 +53,10 @@ _SIGS = {
     "omni_schedule_workspace": (_sz, [_i, _i, _i, _i]),
     "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),
                                  _vp, _sz, _vp]),
+    "omni_atomic_forward_mode": (_i, [_i, _i, _i, _i, _i, _i]),
     "omni_atomic_forward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "omni_atomic_forward": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
-                                 ctypes.POINTER(ScheduleStruct), _vp, _i, _vp, _sz, _vp]),
+                                 ctypes.POINTER(ScheduleStruct), _vp, _i, _i, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -71,6 +74,9 @@ def lib():
             f = getattr(h, name)
             f.restype = res
             f.argtypes = args
+        if h.omni_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {h.omni_abi_version()}, this binding "
+                              f"expects {ABI_VERSION}: rebuild the library")
         _lib = h
     return _lib
 
@@ -228,8 +234,26 @@ def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None):
     return sched
 
 
-def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, stream=None):
-    """omni_atomic_forward: returns y [L, d] float32 (y += routed if accumulate)."""
+def _exec_mode(mode):
+    if mode not in EXEC_MODES:
+        raise ValueError(f"mode must be one of {sorted(EXEC_MODES)}, got {mode!r}")
+    return EXEC_MODES[mode]
+
+
+def atomic_forward_mode(dtype, L, d, N, K, B):
+    """omni_atomic_forward_mode: the form mode="auto" runs ("expert" / "token")."""
+    code = torch.bfloat16 if dtype == torch.bfloat16 else torch.float32
+    m = lib().omni_atomic_forward_mode(OMNI_BF16 if code == torch.bfloat16 else OMNI_F32,
+                                       L, d, N, K, B)
+    if m == 0:
+        raise ValueError("invalid shape for omni_atomic_forward_mode")
+    return {1: "expert", 2: "token"}[m]
+
+
+def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, stream=None,
+                   mode="auto"):
+    """omni_atomic_forward: returns y [L, d] float32 (y += routed if accumulate).
+    mode: "auto", "expert" (expert-centric) or "token" (token-centric)."""
     L, d = x.shape
     N = w.shape[0]
     _req(x, "x")
@@ -237,6 +261,7 @@ def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, str
     _req(v, "v", x.dtype, (N, d))
     if sched.task_index is None:
         raise ValueError("the schedule must carry task_index")
+    code = _exec_mode(mode)
     if y is None:
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
     _req(y, "y", torch.float32, (L, d))
@@ -247,16 +272,17 @@ def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, str
         ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
     _check("omni_atomic_forward", lib().omni_atomic_forward(
         _dtype_code(x), L, d, N, sched.K, sched.B, _ptr(x), _ptr(w), _ptr(v),
-        ctypes.byref(st), _ptr(y), int(bool(accumulate)), _ptr(ws), nws if ws is not None else 0,
-        _stream(stream)))
+        ctypes.byref(st), _ptr(y), int(bool(accumulate)), code, _ptr(ws),
+        nws if ws is not None else 0, _stream(stream)))
     return y
 
 
-def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, stream=None):
+def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, stream=None,
+            mode="auto"):
     """The four calls back to back on one stream; returns every intermediate."""
     zr, zc = router_logits(x, wr_t, wc_t, row_bias, col_bias, stream=stream)
     sel = product_topk(zr, zc, kprime, K, stream=stream)
     N = wr_t.shape[0] * wc_t.shape[0]
     sched = schedule_tasks(sel["expert_idx"], sel["gate"], N, B, stream=stream)
-    y = atomic_forward(x, w, v, sched, stream=stream)
+    y = atomic_forward(x, w, v, sched, stream=stream, mode=mode)
     return {"row_logits": zr, "col_logits": zc, **sel, "schedule": sched, "y": y}

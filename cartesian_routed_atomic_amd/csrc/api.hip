@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -141,6 +141,12 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, const int32_t* exper
                                           out->task_gate, out->task_index, ws, stream));
 }
 
+int omni_atomic_forward_mode(omni_dtype dt, int L, int d, int N, int K, int B) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
+  if (!schedule_args_ok(L, K, N, B) || d < 1) return 0;
+  return omni::auto_exec_mode(dt == OMNI_BF16, L, d, K);
+}
+
 size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B) {
   (void)dt; (void)d; (void)N; (void)B;
   if (L <= 0 || K < 1 || !fits_i32(static_cast<long long>(L) * K)) return 0;
@@ -149,9 +155,12 @@ size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, 
 
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B, const void* x,
                                 const void* w, const void* v, const omni_schedule* sched,
-                                float* y, int accumulate, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+                                float* y, int accumulate, omni_exec_mode mode, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
+  if (mode != OMNI_EXEC_AUTO && mode != OMNI_EXEC_EXPERT_CENTRIC &&
+      mode != OMNI_EXEC_TOKEN_CENTRIC)
+    return OMNI_ERR_INVALID_ARG;
   if (!schedule_args_ok(L, K, N, B) || d < 1) return OMNI_ERR_INVALID_ARG;
   if (!w || !v || !sched) return OMNI_ERR_INVALID_ARG;
   const long long M = static_cast<long long>(L) * K;
@@ -160,13 +169,17 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                 !sched->task_index))
     return OMNI_ERR_INVALID_ARG;
   if (d < 64 || d > 4096 || (d & (d - 1)) != 0) return OMNI_ERR_UNSUPPORTED;
+  const int bf16 = dt == OMNI_BF16;
+  const int form = mode == OMNI_EXEC_AUTO ? omni::auto_exec_mode(bf16, L, d, K) : mode;
+  if (form == OMNI_EXEC_TOKEN_CENTRIC && !omni::token_centric_supported(bf16, d))
+    return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(v)) return OMNI_ERR_INVALID_ARG;
   if (L > 0 && !aligned16(y)) return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;
   if (L == 0) return OMNI_OK;
   const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
-  return hip_status(omni::launch_atomic_forward(dt == OMNI_BF16, L, d, N, K, x, w, v,
+  return hip_status(omni::launch_atomic_forward(bf16, form, L, d, N, K, x, w, v,
                                                 sched->task_token, sched->task_expert,
                                                 sched->task_gate, sched->task_index, y,
                                                 accumulate != 0, ws, stream));

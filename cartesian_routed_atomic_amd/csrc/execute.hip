@@ -1,25 +1,37 @@
-// Expert-centric execution of the schedule.  Pages: gist.science explainer
-// §2.1 (atomic expert E_i(x) = sigma(x . w_in) w_out; all experts live in the
-// global matrices W, V in R^{N x d}) and interactive explainer
-// "Expert-Centric Scheduling" (each group's parameters are loaded once and
-// reused for every token assigned to the group; parameter traffic
-// 2d * |E_active| instead of 2d * L * K).
+// Execution of the routed layer.  Pages: gist.science explainer §2.1 (atomic
+// expert E_i(x) = sigma(x . w_in) w_out; all experts live in the global
+// matrices W, V in R^{N x d}; per token the selected rows are assembled into
+// one block) and interactive explainer "Expert-Centric Scheduling" (each
+// group's parameters are loaded once and reused for every token assigned to
+// the group; parameter traffic 2d * |E_active| instead of 2d * L * K).
 //
-// Two kernels, no atomics:
-//   phase 1 (expert-centric, in the schedule's (group, token) order): per
-//     task h = x_t . W[e], coef = g * silu(h), written at the task's flat id
+// Expert-centric form, two kernels, no atomics:
+//   phase 1 (in the schedule's (group, token) order): per task
+//     h = x_t . W[e], coef = g * silu(h), written at the task's flat id
 //     m = t*K + k together with e.  Each wave walks a contiguous run of the
 //     sorted tasks with three tasks' rows in flight; x_t is fetched once per
 //     (group, token) run.  Workgroups are laid out XCD by XCD over the task
-//     list, so a group's tasks run on one XCD and an expert used by several
-//     tokens of the group is re-read from that XCD's L2, not from HBM.  The
-//     bf16 dot product runs on v_dot2_f32_bf16 (two products per instruction,
-//     float32 accumulation).
+//     list, so the W rows of a group are read by one XCD, and the tasks of a
+//     group visit the tokens in increasing order, so at any moment the waves
+//     of the chip read x rows from a narrow token window that stays in L2.
+//     The bf16 dot product runs on v_dot2_f32_bf16 (two products per
+//     instruction, float32 accumulation).
 //   phase 2 (token-centric gather): y_t = sum_k coef[t,k] * V[e_tk], one wave
 //     (or a few, splitting d) per token, y written once with plain stores.
 // Scattering the V contributions in expert-centric order instead needs a
-// float32 atomic add into y per (group, token) run, which measured about
-// twice as slow on MI355X as reading the few repeated V rows again.
+// float32 atomic add into y per task, which measured about twice as slow on
+// MI355X as reading the repeated V rows again.
+//
+// Token-centric form (the Dynamic Expert Assembly view of §2.1), one kernel:
+//   one wave per token holds x_t in registers, streams the token's K W rows
+//   (pass A: h_k, coef_k) and then its K V rows (pass B: y_t += coef_k V[e]).
+//   It reads every W and V row once per task, like phase 1 + phase 2 above,
+//   but x once per token and no coefficient round trip.  When the tasks reuse
+//   experts little (uniform routing over N = 2^20 experts: 1.28 tasks per
+//   active expert) both forms are bound by the DRAM rate for random 4 KiB
+//   rows, and this one does less other work; with few tokens it cannot fill
+//   the chip.  Both forms sum y in the same order with the same fragment
+//   layout, so they give bit-identical y.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -168,13 +180,40 @@ __global__ __launch_bounds__(256) void coef_kernel(
   }
 }
 
+// Store (or add) a lane's accumulators to its columns of a y row, in the
+// RowFrag element layout, with 16-byte stores where the layout allows.
+template <typename T, int EPL>
+__device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __restrict__ yrow,
+                                          int accumulate) {
+  constexpr int VEC = RowFrag<T, EPL>::VEC, NCH = RowFrag<T, EPL>::NCH;
+  const int l = lane();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    float* p = yrow + c * 64 * VEC + l * VEC;
+    if constexpr (VEC >= 4) {
+#pragma unroll
+      for (int j = 0; j < VEC; j += 4) {
+        float4 v = make_float4(acc[c * VEC + j], acc[c * VEC + j + 1], acc[c * VEC + j + 2],
+                               acc[c * VEC + j + 3]);
+        if (accumulate) {
+          const float4 o = *reinterpret_cast<const float4*>(p + j);
+          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        }
+        *reinterpret_cast<float4*>(p + j) = v;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) p[q] = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
+    }
+  }
+}
+
 // Phase 2.  Wave g serves token g / split, columns [s * 64 * EPL, +64 * EPL).
 template <typename T, int EPL>
 __global__ __launch_bounds__(256) void gather_kernel(
     const T* __restrict__ V, const float* __restrict__ coef, const int32_t* __restrict__ eflat,
     int L, int K, int d, int N, int split, float* __restrict__ y, int accumulate) {
   using Frag = RowFrag<T, EPL>;
-  constexpr int VEC = Frag::VEC, NCH = Frag::NCH;
   const long long g = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int l = lane();
   if (g >= static_cast<long long>(L) * split) return;
@@ -207,26 +246,93 @@ __global__ __launch_bounds__(256) void gather_kernel(
       }
     }
   }
-  float* yt = y + static_cast<size_t>(t) * d + col0;
+  store_row<T, EPL>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
+}
+
+// A task of a token's list: expert id and gate, at flat position t*K + k.
+struct TokTask {
+  int32_t e;
+  float g;
+};
+
+// Inverse of the schedule's task permutation: the (e, g) list of every token
+// in top-K order.  Ids outside their range (only from a corrupted schedule)
+// are mapped to expert 0 so every later access stays in bounds.
+__global__ __launch_bounds__(256) void unpermute_kernel(const int32_t* __restrict__ texp,
+                                                        const float* __restrict__ tgate,
+                                                        const int32_t* __restrict__ tidx, int M,
+                                                        int N, TokTask* __restrict__ lists) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  const int i = tidx[m];
+  if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) return;
+  const int e = texp[m];
+  lists[i] = TokTask{static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0, tgate[m]};
+}
+
+constexpr int kTokRing = 6;  // row slots per wave in the token-centric kernel: five in flight
+
+template <typename T, int EPL>
+__global__ __launch_bounds__(256, 3) void token_kernel(
+    const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ V,
+    const TokTask* __restrict__ lists, int L, int K, int d, int N, float* __restrict__ y,
+    int accumulate) {
+  using Frag = RowFrag<T, EPL>;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = lane();
+  if (t >= L) return;
+  Frag xf;
+  xf.load(x + static_cast<size_t>(t) * d, l);
+  float acc[EPL];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    float* p = yt + c * 64 * VEC + l * VEC;
+  for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
+  Frag f[kTokRing];  // one ring for both passes keeps the register count down
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int n = min(64, K - k0);
+    int my_e = 0;
+    float my_g = 0.f;
+    if (l < n) {
+      const TokTask tk = lists[static_cast<size_t>(t) * K + k0 + l];
+      my_e = static_cast<unsigned>(tk.e) < static_cast<unsigned>(N) ? tk.e : 0;
+      my_g = tk.g;
+    }
+    // pass A: h_k = x_t . W[e_k], kTokRing - 1 rows in flight; h_k ends in lane k
+    float my_h = 0.f;
 #pragma unroll
-    for (int j = 0; j < VEC; j += (VEC >= 4 ? 4 : VEC)) {
-      if constexpr (VEC >= 4) {
-        float4 v = make_float4(acc[c * VEC + j], acc[c * VEC + j + 1], acc[c * VEC + j + 2],
-                               acc[c * VEC + j + 3]);
-        if (accumulate) {
-          const float4 o = *reinterpret_cast<const float4*>(p + j);
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-        }
-        *reinterpret_cast<float4*>(p + j) = v;
-      } else {
+    for (int s = 0; s < kTokRing - 1; ++s)
+      if (s < n) f[s].load(W + static_cast<size_t>(rdlane(my_e, s)) * d, l);
+    for (int i = 0; i < n; i += kTokRing) {
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) p[q] = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
+      for (int s = 0; s < kTokRing; ++s) {
+        const int ii = i + s;
+        if (ii >= n) break;
+        if (ii + kTokRing - 1 < n)
+          f[(s + kTokRing - 1) % kTokRing].load(
+              W + static_cast<size_t>(rdlane(my_e, ii + kTokRing - 1)) * d, l);
+        const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
+        if (l == ii) my_h = h;
+      }
+    }
+    const float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
+    // pass B: y_t += coef_k * V[e_k]
+#pragma unroll
+    for (int s = 0; s < kTokRing - 1; ++s)
+      if (s < n) f[s].load(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
+    for (int i = 0; i < n; i += kTokRing) {
+#pragma unroll
+      for (int s = 0; s < kTokRing; ++s) {
+        const int ii = i + s;
+        if (ii >= n) break;
+        if (ii + kTokRing - 1 < n)
+          f[(s + kTokRing - 1) % kTokRing].load(
+              V + static_cast<size_t>(rdlane(my_e, ii + kTokRing - 1)) * d, l);
+        const float c = rdlane(my_c, ii);
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
       }
     }
   }
+  store_row<T, EPL>(acc, y + static_cast<size_t>(t) * d, accumulate);
 }
 
 static inline int clampi(long long v, int lo, int hi) {
@@ -294,7 +400,44 @@ size_t atomic_forward_ws_bytes(int L, int K) {
   return 2 * ((m + 255) & ~static_cast<size_t>(255));
 }
 
-hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int K, const void* x,
+template <typename T>
+static bool dispatch_token(const T* x, const T* w, const T* v, const int32_t* te,
+                           const float* tg, const int32_t* ti, int M, int d, int L, int K, int N,
+                           TokTask* lists, float* y, int accumulate, hipStream_t s) {
+  unpermute_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(te, tg, ti, M, N,
+                                                                          lists);
+  const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
+  // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
+  switch (d) {
+#define OMNI_TOK(D_, EPL_) case D_: token_kernel<T, EPL_><<<nblk, 256, 0, s>>>(x, w, v, lists, L, K, d, N, y, accumulate); break;
+    OMNI_TOK(64, 1) OMNI_TOK(128, 2) OMNI_TOK(256, 4) OMNI_TOK(512, 8) OMNI_TOK(1024, 16)
+#undef OMNI_TOK
+    case 2048:
+      if constexpr (sizeof(T) == 2) {
+        token_kernel<T, 32><<<nblk, 256, 0, s>>>(x, w, v, lists, L, K, d, N, y, accumulate);
+        break;
+      }
+      return false;
+    default: return false;
+  }
+  return true;
+}
+
+bool token_centric_supported(int bf16, int d) {
+  const long long row_bytes = static_cast<long long>(d) * (bf16 ? 2 : 4);
+  return row_bytes <= 4096 && d >= 64 && (d & (d - 1)) == 0;
+}
+
+int auto_exec_mode(int bf16, int L, int d, int K) {
+  (void)K;
+  // One wave per token keeps 3072 waves resident (3 per SIMD); it beat the
+  // two-kernel form from L = 8192 tokens of d = 2048 up (2.7 resident rounds),
+  // and lost at L = 4096, d = 1024 and at L = 256.
+  if (L >= 8192 && d >= 1024 && token_centric_supported(bf16, d)) return 2;
+  return 1;
+}
+
+hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,
                                  const void* w, const void* v, const int32_t* task_token,
                                  const int32_t* task_expert, const float* task_gate,
                                  const int32_t* task_index, float* y, bool accumulate, void* ws,
@@ -309,18 +452,33 @@ hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int K, const voi
     }
     return hipGetLastError();
   }
-  float* coef = static_cast<float*>(ws);
-  int32_t* eflat = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + atomic_forward_ws_bytes(L, K) / 2);
+  const int acc = accumulate ? 1 : 0;
   bool ok;
-  if (bf16)
-    ok = dispatch_exec<uint16_t>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
-                                 static_cast<const uint16_t*>(v), task_token, task_expert,
-                                 task_gate, task_index, M, d, L, K, N, coef, eflat, y,
-                                 accumulate ? 1 : 0, s);
-  else
-    ok = dispatch_exec<float>(static_cast<const float*>(x), static_cast<const float*>(w),
-                              static_cast<const float*>(v), task_token, task_expert, task_gate,
-                              task_index, M, d, L, K, N, coef, eflat, y, accumulate ? 1 : 0, s);
+  if (mode == 2) {
+    TokTask* lists = static_cast<TokTask*>(ws);
+    if (bf16)
+      ok = dispatch_token<uint16_t>(static_cast<const uint16_t*>(x),
+                                    static_cast<const uint16_t*>(w),
+                                    static_cast<const uint16_t*>(v), task_expert, task_gate,
+                                    task_index, M, d, L, K, N, lists, y, acc, s);
+    else
+      ok = dispatch_token<float>(static_cast<const float*>(x), static_cast<const float*>(w),
+                                 static_cast<const float*>(v), task_expert, task_gate,
+                                 task_index, M, d, L, K, N, lists, y, acc, s);
+  } else {
+    float* coef = static_cast<float*>(ws);
+    int32_t* eflat = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                atomic_forward_ws_bytes(L, K) / 2);
+    if (bf16)
+      ok = dispatch_exec<uint16_t>(static_cast<const uint16_t*>(x),
+                                   static_cast<const uint16_t*>(w),
+                                   static_cast<const uint16_t*>(v), task_token, task_expert,
+                                   task_gate, task_index, M, d, L, K, N, coef, eflat, y, acc, s);
+    else
+      ok = dispatch_exec<float>(static_cast<const float*>(x), static_cast<const float*>(w),
+                                static_cast<const float*>(v), task_token, task_expert, task_gate,
+                                task_index, M, d, L, K, N, coef, eflat, y, acc, s);
+  }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -36,7 +36,9 @@ hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx
 
 // execute.hip
 size_t atomic_forward_ws_bytes(int L, int K);
-hipError_t launch_atomic_forward(int bf16, int L, int d, int N, int K, const void* x,
+bool token_centric_supported(int bf16, int d);
+int auto_exec_mode(int bf16, int L, int d, int K);  // 1 expert-centric, 2 token-centric
+hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,
                                  const void* w, const void* v, const int32_t* task_token,
                                  const int32_t* task_expert, const float* task_gate,
                                  const int32_t* task_index, float* y, bool accumulate, void* ws,

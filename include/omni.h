@@ -17,8 +17,9 @@
  *                           (token, expert, gate) tasks, group the unique
  *                           active experts B at a time, order the tasks by
  *                           (group, token);
- *   4. omni_atomic_forward  expert-centric execution of the schedule:
- *                           y_t = sum_k g_tk * silu(x_t . W[e_tk]) * V[e_tk].
+ *   4. omni_atomic_forward  execution of the schedule:
+ *                           y_t = sum_k g_tk * silu(x_t . W[e_tk]) * V[e_tk],
+ *                           expert-centric or token-centric (same result).
  *
  * Conventions shared by every call
  *   - All pointers except the `omni_schedule` descriptor itself are DEVICE
@@ -60,7 +61,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 2 */
+int omni_abi_version(void);  /* 3 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -179,16 +180,27 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B,
  * omni_atomic_forward — execution of a schedule.
  * Pages: gist.science explainer §2.1 (atomic expert E_i(x) = sigma(x w_in^T)
  * w_out; all N experts live in two global matrices W, V in R^{N x d}; per
- * token the selected rows are assembled into one block) and interactive
- * explainer "Expert-Centric Scheduling" (each group's parameters are loaded
- * once and reused for all tokens assigned to it; traffic 2d*|E_active|
- * instead of 2d*L*K).  sigma = SiLU.
+ * token the selected rows are assembled into one block: Dynamic Expert
+ * Assembly) and interactive explainer "Expert-Centric Scheduling" (each
+ * group's parameters are loaded once and reused for all tokens assigned to
+ * it; traffic 2d*|E_active| instead of 2d*L*K).  sigma = SiLU.
  *
  *   y[t, :] = sum over scheduled tasks (t, e, g): g * silu(x[t,:] . W[e,:]) * V[e,:]
  *
- * Two kernels: the first walks the tasks in the schedule's (group, token)
- * order and computes c = g * silu(x_t . W[e]) per task; the second gathers
- * y_t = sum_k c_tk V[e_tk] per token, so y is written once, without atomics.
+ * Two execution forms, selected by `mode`:
+ *   OMNI_EXEC_EXPERT_CENTRIC: two kernels; the first walks the tasks in the
+ *     schedule's (group, token) order and computes c = g * silu(x_t . W[e])
+ *     per task, the second gathers y_t = sum_k c_tk V[e_tk] per token, so y
+ *     is written once, without atomics.
+ *   OMNI_EXEC_TOKEN_CENTRIC: the schedule is inverted into per-token task
+ *     lists, then one wave per token assembles its experts: x_t stays in
+ *     registers, the token's W rows give the K coefficients, its V rows are
+ *     summed into y_t.  Needs d * element size <= 4096 bytes (else
+ *     UNSUPPORTED).
+ *   OMNI_EXEC_AUTO: the form omni_atomic_forward_mode() names for the shape
+ *     (the one that measured faster on MI355X).
+ * Both forms evaluate every coefficient and every y element with the same
+ * operations in the same order (k = 0..K-1), so they give bit-identical y.
  *
  * x [L, d], w [N, d], v [N, d] of dt; sched: a schedule produced by
  * omni_schedule_tasks for the same L, K, N, B, with task_index present;
@@ -196,15 +208,24 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B,
  * with the routed output; accumulate != 0: the routed output is added to y as
  * it stands (e.g. onto the output of a shared dense branch).
  * ws / ws_bytes: at least omni_atomic_forward_workspace(...) bytes, 256-byte
- * aligned (a coefficient and an expert id per task).  Requires
- * d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED); 16-byte aligned x,
- * w, v.  Deterministic: every y element is summed in a fixed order.
+ * aligned (8 bytes per task: a coefficient and an expert id, or the per-token
+ * lists).  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
+ * 16-byte aligned x, w, v.  Deterministic.
  */
+typedef enum omni_exec_mode {
+  OMNI_EXEC_AUTO = 0,
+  OMNI_EXEC_EXPERT_CENTRIC = 1,
+  OMNI_EXEC_TOKEN_CENTRIC = 2
+} omni_exec_mode;
+
+/* The form OMNI_EXEC_AUTO runs for this shape (1 or 2); 0 for invalid args. */
+int omni_atomic_forward_mode(omni_dtype dt, int L, int d, int N, int K, int B);
 size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B);
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B,
                                 const void* x, const void* w, const void* v,
                                 const omni_schedule* sched, float* y, int accumulate,
-                                void* ws, size_t ws_bytes, hipStream_t stream);
+                                omni_exec_mode mode, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

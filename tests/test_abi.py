@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 2
+    assert lib.omni_abi_version() == 3
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -120,18 +120,40 @@ def test_atomic_forward_argument_checks(lib):
     st = B.ScheduleStruct(*([1 << 20] * 7))
     f = lib.omni_atomic_forward
 
-    def call(dt=1, L=4, d=128, N=64, K=2, Bg=4, x=FAKE, w=FAKE, v=FAKE, y=FAKE, s=st):
+    def call(dt=1, L=4, d=128, N=64, K=2, Bg=4, x=FAKE, w=FAKE, v=FAKE, y=FAKE, s=st, mode=0):
         return f(dt, L, d, N, K, Bg, x, w, v, ctypes.byref(s) if s is not None else None,
-                 y, 0, None, 0, None)
+                 y, 0, mode, None, 0, None)
     assert call(dt=3) == B.OMNI_ERR_INVALID_ARG
     assert call(s=None) == B.OMNI_ERR_INVALID_ARG
     assert call(y=None) == B.OMNI_ERR_INVALID_ARG
     assert call(w=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(mode=3) == B.OMNI_ERR_INVALID_ARG
+    assert call(mode=-1) == B.OMNI_ERR_INVALID_ARG
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=8192) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=32) == B.OMNI_ERR_UNSUPPORTED
+    # token-centric rows must fit 4 KiB: bf16 up to d = 2048, float32 up to 1024
+    assert call(d=4096, mode=2) == B.OMNI_ERR_UNSUPPORTED
+    assert call(dt=0, d=2048, mode=2) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=2048, mode=2) == B.OMNI_ERR_WORKSPACE
+    assert call(dt=0, d=1024, mode=2) == B.OMNI_ERR_WORKSPACE
+    assert call(d=4096, mode=1) == B.OMNI_ERR_WORKSPACE
     assert call(L=0) == B.OMNI_OK
     assert call() == B.OMNI_ERR_WORKSPACE                  # L*K tasks need a workspace
     noidx = B.ScheduleStruct(*([1 << 20] * 6 + [0]))
     assert call(s=noidx) == B.OMNI_ERR_INVALID_ARG          # task_index is required
     assert lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256) >= 8 * 8192 * 64
+
+
+def test_atomic_forward_auto_mode(lib):
+    mode = lib.omni_atomic_forward_mode
+    # the measured crossover: token-centric from L = 8192 tokens of d >= 1024
+    assert mode(1, 8192, 2048, 1 << 20, 64, 256) == 2      # large
+    assert mode(1, 16384, 2048, 1 << 18, 64, 128) == 2     # mid
+    assert mode(1, 4096, 1024, 1 << 14, 32, 64) == 1       # small
+    assert mode(1, 256, 2048, 1 << 20, 64, 64) == 1        # decode
+    assert mode(0, 64, 128, 1024, 8, 16) == 1              # tiny float32
+    assert mode(1, 8192, 4096, 1 << 20, 64, 256) == 1      # row over 4 KiB
+    assert mode(0, 8192, 2048, 1 << 20, 64, 256) == 1      # float32 row over 4 KiB
+    assert mode(3, 8192, 2048, 1 << 20, 64, 256) == 0      # bad dtype
+    assert mode(1, 8192, 2048, 1 << 20, 0, 256) == 0       # bad K

@@ -126,6 +126,27 @@ def test_stage_parity(name):
     check_topk(out["row_logp"], out["col_logp"], out, wl.kprime, wl.K)
     check_schedule(out, out["schedule"], wl.N, wl.B)
     check_y(inp, out, out["y"], wl.dtype)
+    check_forms(wl, inp, out)
+
+
+def check_forms(wl, inp, out):
+    """Both execution forms, explicitly: each within tolerance of the oracle and
+    bit-identical to the other (same operations in the same order)."""
+    t = {k: dev(inp[k]) for k in ("x", "w", "v")}
+    ys = {}
+    for mode in ("expert", "token"):
+        if mode == "token" and wl.d * (2 if wl.dtype == "bf16" else 4) > 4096:
+            with pytest.raises(B.OmniError) as ei:
+                B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], mode=mode)
+            assert ei.value.code == B.OMNI_ERR_UNSUPPORTED
+            continue
+        y = torch.full((wl.L, wl.d), float("nan"), device="cuda")
+        B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], y=y, mode=mode)
+        torch.cuda.synchronize()
+        ys[mode] = host(y)
+    for y in ys.values():
+        np.testing.assert_array_equal(y.view(np.uint32), host(out["y"]).view(np.uint32))
+    log(f"  execution forms {sorted(ys)} bit-identical")
 
 
 def test_end_to_end_selection_agreement_is_reported():
@@ -229,27 +250,51 @@ def test_empty_batch():
     assert wl.L == 0
 
 
-def test_y_is_overwritten_not_accumulated():
+@pytest.mark.parametrize("mode", ["expert", "token"])
+def test_y_is_overwritten_not_accumulated(mode):
     wl = WORKLOADS["tiny"]
     inp = make_inputs(wl)
     t = {k: dev(v) for k, v in inp.items()}
     out = run_pipeline(wl, inp)
     y = torch.full_like(out["y"], 123.0)
-    B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], y=y)
+    B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], y=y, mode=mode)
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(y), host(out["y"]), rtol=1e-5, atol=1e-6)
 
 
-def test_accumulate_adds_onto_y():
+@pytest.mark.parametrize("mode", ["expert", "token"])
+def test_accumulate_adds_onto_y(mode):
     wl = WORKLOADS["tiny"]
     inp = make_inputs(wl)
     t = {k: dev(v) for k, v in inp.items()}
     out = run_pipeline(wl, inp)
     base = torch.linspace(-1, 1, out["y"].numel(), device="cuda").reshape(out["y"].shape)
     y = base.clone()
-    B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], y=y, accumulate=True)
+    B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], y=y, accumulate=True, mode=mode)
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(y), host(base) + host(out["y"]), rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("K", [65, 130])
+def test_executor_more_than_64_tasks_per_token(K):
+    """K above one wave's 64 lanes (the product top-K stops at 64, the schedule
+    and the executor do not): seeded (expert, gate) lists, both forms."""
+    L, d, N, Bg = 37, 256, 500, 16
+    rng = np.random.default_rng(K)
+    idx = np.stack([rng.choice(N, K, replace=False) for _ in range(L)]).astype(np.int32)
+    gate = rng.random((L, K)).astype(np.float32)
+    x = (rng.standard_normal((L, d)) / 4).astype(np.float32)
+    w = (rng.standard_normal((N, d)) / np.sqrt(d)).astype(np.float32)
+    v = (rng.standard_normal((N, d)) / np.sqrt(d)).astype(np.float32)
+    sched = B.schedule_tasks(dev(idx), dev(gate), N, Bg)
+    want = O.atomic_forward(x, w, v, idx, gate)
+    ys = []
+    for mode in ("expert", "token"):
+        y = B.atomic_forward(dev(x), dev(w), dev(v), sched, mode=mode)
+        torch.cuda.synchronize()
+        ys.append(host(y))
+        assert rel_err(ys[-1], want) <= TOL_Y["f32"]
+    np.testing.assert_array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
 
 
 @pytest.mark.parametrize("L,d,Nr,Nc", [(77, 40, 24, 40), (300, 200, 96, 33), (513, 2048, 300, 260)])

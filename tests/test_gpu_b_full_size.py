@@ -29,7 +29,14 @@ def test_full_size_parity(name):
     out = B.forward(t["x"], t["wr"], t["wc"], t["w"], t["v"], wl.kprime, wl.K, wl.B,
                     t["row_bias"], t["col_bias"])
     torch.cuda.synchronize()
-    del t
+    # the form auto did not pick, on the same schedule: must give the same bits
+    auto = B.atomic_forward_mode(t["x"].dtype, wl.L, wl.d, wl.N, wl.K, wl.B)
+    other = "expert" if auto == "token" else "token"
+    y2 = B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], mode=other)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int32), out["y"].view(torch.int32))
+    log(f"  y of the {auto}-centric (auto) and {other}-centric forms bit-identical")
+    del t, y2
     log(f"  gpu done {time.time() - t0:.1f}s")
     check_router(inp, out)
     rng = np.random.default_rng(0)
