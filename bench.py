@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 METRIC = "routed tokens/sec per atomic-expert layer at 1 GPU; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
-EXEC_SRC = os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", "execute.hip")
+EXEC_SRCS = [os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", f)
+             for f in ("execute.hip", "device.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
 EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
@@ -39,22 +40,25 @@ def say(msg):
 
 
 def exec_src_hash():
-    with open(EXEC_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Fingerprint of the executor's kernel sources (a counter record taken on
+    other sources no longer describes the kernel)."""
+    h = hashlib.sha256()
+    for p in EXEC_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """Counter-derived HBM bytes per executor launch, if taken on this kernel."""
+def measured_traffic(workload, form):
+    """Counter-derived HBM bytes per executor call, if taken on this kernel."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    txt = open(TRAFFIC_FILE).read()
-    m = re.search(r"traffic_record:\s*(\{.*\})", txt)
-    if not m:
-        return None
-    rec = json.loads(m.group(1))
-    if rec.get("workload") != workload or rec.get("execute_hip_sha256_16") != exec_src_hash():
-        return None
-    return rec.get("bytes_per_launch")
+    for m in re.finditer(r"traffic_record:\s*(\{.*\})", open(TRAFFIC_FILE).read()):
+        rec = json.loads(m.group(1))
+        if (rec.get("workload") == workload and rec.get("form") == form
+                and rec.get("executor_src_sha256_16") == exec_src_hash()):
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def cpu_baseline(inp, wl, target_s):
@@ -93,6 +97,9 @@ def main():
     ap.add_argument("--workload", default="large")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run three device-to-device copies of this many MiB (a "
+                         "kernel of known traffic, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -196,13 +203,23 @@ def main():
     M = L * K
     bytes_alg = 2 * wl.d * s * n_active + L * wl.d * s + 4 * L * wl.d + 12 * M
     achieved = bytes_alg / (exec_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, form)
     router_flop = 2.0 * L * wl.d * (wl.Nr + wl.Nc)
     router_tflops = router_flop / (stages["router"] * 1e-3) / 1e12
     say(f"[bench] stages ms {json.dumps({k: round(v4, 4) for k, v4 in stages.items()})}; "
         f"executor ({form}-centric) {exec_ms:.4f} ms, {achieved:.0f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of HBM); n_active={n_active} "
         f"n_groups={n_groups}; forms ms {forms_ms}")
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        say(f"[bench] copy probe: 3 copies of {args.copy_probe_mib} MiB")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -228,6 +245,7 @@ def main():
                    "zipf_s": wl.zipf_s},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_over_alg": None if traffic is None else traffic / bytes_alg,
                      "kernel": EXEC_KERNELS[form], "bytes_alg": bytes_alg,
                      "kernel_ms": exec_ms},
         "executor_form": form,
