@@ -6,7 +6,9 @@ A step is one pass of the whole path on one batch: router logits ->
 product top-K + gates -> expert-centric schedule -> execution of the schedule
 (in the form the library's auto mode picks for the shape; the other form is
 timed beside it), all four C-ABI calls enqueued back to back on one stream,
-inputs resident in HBM, every output buffer allocated before timing.
+inputs resident in HBM, every output buffer allocated before timing.  The
+same four calls captured once into a HIP graph are timed beside it
+(graph_ms_per_step; --no-graph skips that).
 
     python bench.py [--steps 50] [--warmup 5] [--workload large]
 
@@ -96,6 +98,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the HIP-graph replay of the step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run three device-to-device copies of this many MiB (a "
@@ -163,16 +167,29 @@ def main():
         stage_schedule()
         stage_execute()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t1
-    ms = 1e3 * elapsed / args.steps
-    say(f"[bench] {args.steps} steps in {elapsed:.3f}s: {ms:.3f} ms/step")
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t1) / args.steps
+
+    # the four calls launched one by one: the timed step
+    ms = timed(step)
+    say(f"[bench] {args.steps} steps, {ms:.3f} ms/step")
+    # the same four calls captured once into a HIP graph and replayed (the
+    # library allocates, frees and memsets nothing, so the step is capturable)
+    graph_ms = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph_ms = timed(graph.replay)
+        say(f"[bench] graph replay: {args.steps} replays, {graph_ms:.3f} ms/step")
 
     # per-stage times (HIP events on the stream the kernels run on)
     def ev_time(fn, reps=10):
@@ -235,6 +252,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "graph_ms_per_step": graph_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
