@@ -32,206 +32,203 @@ namespace omni {
 
 // ---------------------------------------------------------------- selection
 
-// Result of a value-key selection: the selected items are those with
-// key > T plus the first `eq_take` items with key == T in index order, or,
-// when eq_take < 0, every item with key >= T.
-struct Sel32 {
-  uint32_t T;
-  int eq_take;
+// Number of the wave's keys >= c (NI keys per lane; key 0 is an empty slot
+// and never counts, since every c used here is >= 1).  One compare and a
+// ballot per slot; the counts are summed in scalar registers.
+template <int NI>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&vk)[NI], uint32_t c) {
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) n += __popcll(__ballot(vk[j] >= c));
+  return n;
+}
+
+// State of an exact k-th-largest search over 32-bit keys: the answer is
+// built bit by bit from the most significant bit where the keys differ.
+// Invariant: n = #keys >= prefix >= k.  When n reaches k the k largest keys
+// are exactly those >= prefix and the search stops early; otherwise it ends
+// with prefix = the k-th largest key and n = #keys >= it (ties at it).
+struct KthSearch {
+  uint32_t prefix;
+  int n, bit;  // bit < 0: finished
 };
 
-// k largest of the wave's 32-bit keys (NI per lane; bit j of `valid` marks
-// slot j as an item).  Requires 1 <= k <= number of items.
-// hist: 256 words of LDS owned by this wave.
 template <int NI>
-__device__ __forceinline__ Sel32 wave_select32(const uint32_t (&vk)[NI], uint32_t valid, int k,
-                                               uint32_t* hist) {
-  const int l = lane();
-  uint32_t cand = valid;
-  uint32_t need = static_cast<uint32_t>(k);
-  for (int pass = 0; pass < 5; ++pass) {
-    uint32_t a = ~0u, o = 0u;
+__device__ __forceinline__ KthSearch kth_begin(const uint32_t (&vk)[NI], int k) {
+  uint32_t a = ~0u, o = 0u;
+  int items = 0;
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if ((cand >> j) & 1u) {
-        a &= vk[j];
-        o |= vk[j];
-      }
-    a = wave_and32(a);
-    o = wave_or32(o);
-    const uint32_t diff = a ^ o;
-    if (diff == 0) return Sel32{o, static_cast<int>(need)};  // equal keys left: ties
-    const int h = 31 - __clz(diff);
-    const int lo = h > 7 ? h - 7 : 0;
-    *reinterpret_cast<uint4*>(&hist[4 * l]) = make_uint4(0, 0, 0, 0);
-    wave_lds_fence();
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if ((cand >> j) & 1u) atomicAdd(&hist[(vk[j] >> lo) & 255u], 1u);
-    wave_lds_fence();
-    const uint4 c = *reinterpret_cast<const uint4*>(&hist[4 * l]);
-    const uint32_t s = c.x + c.y + c.z + c.w;
-    const uint32_t S = wave_suffix_sum(s);
-    const uint32_t above = S - s;
-    const uint64_t hm = __ballot(above < need && need <= S);
-    if (hm == 0) return Sel32{0u, -1};  // unreachable while k <= #items
-    const int hl = __ffsll(static_cast<unsigned long long>(hm)) - 1;
-    uint32_t dstar = 0, nneed = 0, bcnt = 0;
-    if (l == hl) {
-      uint32_t cum = above;
-      if (cum + c.w >= need) { dstar = 4 * l + 3; nneed = need - cum; bcnt = c.w; }
-      else if ((cum += c.w) + c.z >= need) { dstar = 4 * l + 2; nneed = need - cum; bcnt = c.z; }
-      else if ((cum += c.z) + c.y >= need) { dstar = 4 * l + 1; nneed = need - cum; bcnt = c.y; }
-      else { cum += c.y; dstar = 4 * l; nneed = need - cum; bcnt = c.x; }
-    }
-    dstar = __builtin_amdgcn_readlane(dstar, hl);
-    nneed = __builtin_amdgcn_readlane(nneed, hl);
-    bcnt = __builtin_amdgcn_readlane(bcnt, hl);
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if (((cand >> j) & 1u) && ((vk[j] >> lo) & 255u) != dstar) cand &= ~(1u << j);
-    need = nneed;
-    wave_lds_fence();
-    if (bcnt == need) {
-      const uint32_t hi_mask = (h >= 31) ? 0u : (~0u << (h + 1));
-      return Sel32{(a & hi_mask) | (dstar << lo), -1};
-    }
+  for (int j = 0; j < NI; ++j) {
+    a &= vk[j] ? vk[j] : ~0u;
+    o |= vk[j];
+    items += __popcll(__ballot(vk[j] != 0u));
   }
-  return Sel32{0u, -1};  // not reached
+  a = wave_and32(a);
+  o = wave_or32(o);
+  const uint32_t diff = a ^ o;
+  if (diff == 0u || items == k) return KthSearch{items == k ? a : o, items, -1};
+  const int h = 31 - __clz(diff);
+  const uint32_t low = (h == 31) ? ~0u : ((2u << h) - 1u);  // bits h..0
+  return KthSearch{a & ~low, items, h};
 }
 
-// Threshold T such that exactly k of this wave's 64-bit keys are >= T.
-// keys[j] is this lane's j-th key (0 = no item); keys are distinct.
 template <int NI>
-__device__ __forceinline__ uint64_t wave_select64(const uint64_t (&keys)[NI], int k,
-                                                  uint32_t* hist) {
-  const int l = lane();
-  uint32_t cand = 0;
-#pragma unroll
-  for (int j = 0; j < NI; ++j)
-    if (keys[j] != 0) cand |= (1u << j);
-  uint32_t need = static_cast<uint32_t>(k);
-  for (int pass = 0; pass < 9; ++pass) {
-    uint64_t a = ~0ull, o = 0;
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if ((cand >> j) & 1u) {
-        a &= keys[j];
-        o |= keys[j];
-      }
-    a = wave_and64(a);
-    o = wave_or64(o);
-    const uint64_t diff = a ^ o;
-    if (diff == 0) return o;  // one candidate left
-    const int h = 63 - __clzll(diff);
-    const int lo = h > 7 ? h - 7 : 0;
-    *reinterpret_cast<uint4*>(&hist[4 * l]) = make_uint4(0, 0, 0, 0);
-    wave_lds_fence();
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if ((cand >> j) & 1u) atomicAdd(&hist[(keys[j] >> lo) & 255], 1u);
-    wave_lds_fence();
-    const uint4 c = *reinterpret_cast<const uint4*>(&hist[4 * l]);
-    const uint32_t s = c.x + c.y + c.z + c.w;
-    const uint32_t S = wave_suffix_sum(s);
-    const uint32_t above = S - s;
-    const uint64_t hm = __ballot(above < need && need <= S);
-    if (hm == 0) return 0;  // unreachable while k <= #items
-    const int hl = __ffsll(static_cast<unsigned long long>(hm)) - 1;
-    uint32_t dstar = 0, nneed = 0, bcnt = 0;
-    if (l == hl) {
-      uint32_t cum = above;
-      if (cum + c.w >= need) { dstar = 4 * l + 3; nneed = need - cum; bcnt = c.w; }
-      else if ((cum += c.w) + c.z >= need) { dstar = 4 * l + 2; nneed = need - cum; bcnt = c.z; }
-      else if ((cum += c.z) + c.y >= need) { dstar = 4 * l + 1; nneed = need - cum; bcnt = c.y; }
-      else { cum += c.y; dstar = 4 * l; nneed = need - cum; bcnt = c.x; }
-    }
-    dstar = __builtin_amdgcn_readlane(dstar, hl);
-    nneed = __builtin_amdgcn_readlane(nneed, hl);
-    bcnt = __builtin_amdgcn_readlane(bcnt, hl);
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      if (((cand >> j) & 1u) && static_cast<uint32_t>((keys[j] >> lo) & 255) != dstar)
-        cand &= ~(1u << j);
-    need = nneed;
-    wave_lds_fence();
-    if (bcnt == need) {
-      const uint64_t hi_mask = (h >= 63) ? 0ull : (~0ull << (h + 1));
-      return (a & hi_mask) | (static_cast<uint64_t>(dstar) << lo);
-    }
+__device__ __forceinline__ void kth_step(KthSearch& s, const uint32_t (&vk)[NI], int k) {
+  if (s.bit < 0) return;
+  const uint32_t c = s.prefix | (1u << s.bit);
+  const int n = wave_count_ge<NI>(vk, c);
+  if (n >= k) {
+    s.prefix = c;
+    s.n = n;
   }
-  return 0;  // not reached for distinct keys
+  s.bit = (s.n == k) ? -1 : s.bit - 1;
 }
 
-// Descending bitonic sort of one 64-bit key per lane.
-__device__ __forceinline__ uint64_t bitonic_desc(uint64_t key) {
+// Sort the k (<= 64) distinct keys buf[0..k) descending; buf[k..64) must be
+// 0.  Each lane counts the keys above its own with broadcast LDS reads (no
+// cross-lane shuffles on the critical path), then stores its key at that
+// rank in `out`.  Returns rank r in lane r (0 past k).
+__device__ __forceinline__ uint64_t rank_sort64(const uint64_t* buf, uint64_t* out, int k) {
   const int l = lane();
+  const uint64_t mine = buf[l];
+  int rank = 0;
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t o = __shfl_xor(key, stride);
-      const bool take_max = ((l & stride) == 0) == ((l & size) == 0);
-      key = take_max ? (key > o ? key : o) : (key < o ? key : o);
-    }
+  for (int i = 0; i < 64; i += 2) {
+    const ulonglong2 p = *reinterpret_cast<const ulonglong2*>(&buf[i]);
+    rank += (p.x > mine) + (p.y > mine);
   }
-  return key;
+  if (l < k) out[rank] = mine;
+  wave_lds_fence();
+  const uint64_t r = (l < k) ? out[l] : 0ull;
+  wave_lds_fence();
+  return r;
 }
 
-// Compacts the selected axis items into buf as (value key << 32 | ~index)
-// and returns them sorted, rank r in lane r (0 past k).  Item (j, lane) has
-// index j * 64 + lane, so slot order is index order.
+// The k largest axis items (value key desc, index asc) into buf as
+// (key << 32 | ~index), buf zero-padded to 64.  Slot j of lane l is index
+// j * 64 + l, so slot order is index order and ties at the threshold are
+// taken in index order.
 template <int NI>
-__device__ __forceinline__ uint64_t axis_collect_sorted(const uint32_t (&vk)[NI], uint32_t valid,
-                                                        Sel32 sel, int k, uint64_t* buf) {
+__device__ __forceinline__ void axis_collect(const uint32_t (&vk)[NI], const KthSearch& s, int k,
+                                             uint64_t* buf) {
   const int l = lane();
+  buf[l] = 0ull;
+  wave_lds_fence();
+  const bool all_ge = s.n == k;  // no partial ties: take every key >= prefix
   int base = 0;
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const bool in = ((valid >> j) & 1u) && (sel.eq_take < 0 ? vk[j] >= sel.T : vk[j] > sel.T);
+    const bool in = vk[j] != 0u && (all_ge ? vk[j] >= s.prefix : vk[j] > s.prefix);
     const uint64_t m = __ballot(in);
-    const int slot = base + mbcnt(m);
-    if (in && slot < 64)
-      buf[slot] = (static_cast<uint64_t>(vk[j]) << 32) | static_cast<uint32_t>(~(j * 64 + l));
+    if (in) buf[base + mbcnt(m)] = (static_cast<uint64_t>(vk[j]) << 32) |
+                                   static_cast<uint32_t>(~(j * 64 + l));
     base += __popcll(m);
   }
-  int rest = sel.eq_take;
+  if (!all_ge) {
+    int rest = k - base;
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const bool eq = rest > 0 && ((valid >> j) & 1u) && vk[j] == sel.T;
-    const uint64_t m = __ballot(eq);
-    const int r = mbcnt(m);
-    const int slot = base + r;
-    if (eq && r < rest && slot < 64)
-      buf[slot] = (static_cast<uint64_t>(vk[j]) << 32) | static_cast<uint32_t>(~(j * 64 + l));
-    const int taken = min(__popcll(m), max(rest, 0));
-    base += taken;
-    rest -= taken;
+    for (int j = 0; j < NI; ++j) {
+      const bool eq = rest > 0 && vk[j] == s.prefix;
+      const uint64_t m = __ballot(eq);
+      const int r = mbcnt(m);
+      if (eq && r < rest)
+        buf[base + r] = (static_cast<uint64_t>(vk[j]) << 32) |
+                        static_cast<uint32_t>(~(j * 64 + l));
+      const int taken = min(__popcll(m), max(rest, 0));
+      base += taken;
+      rest -= taken;
+    }
   }
   wave_lds_fence();
-  uint64_t key = (l < k) ? buf[l] : 0ull;
-  wave_lds_fence();
-  return bitonic_desc(key);
 }
 
-// The k keys >= T in descending order: lane r holds rank r (0 past k).
+// The k largest of a wave's 64-bit keys held in two 32-bit words per slot
+// (hi = value key, lo = ~index; 0/0 = empty; keys distinct), as a predicate
+// per slot: first the k-th largest value word, then, if several slots tie at
+// it, the split among the tied slots by their lo words.
+struct Top64 {
+  uint32_t T, T2;  // take hi > T, or hi == T && lo >= T2 (T2 = 0 takes every hi == T)
+};
+
 template <int NI>
-__device__ __forceinline__ uint64_t wave_collect_sorted(const uint64_t (&keys)[NI], uint64_t T,
-                                                        int k, uint64_t* buf) {
+__device__ __forceinline__ Top64 top64_finish(const uint32_t (&hi)[NI], const uint32_t (&lo)[NI],
+                                              int k, const KthSearch& q) {
+  if (q.n == k) return Top64{q.prefix, 0u};  // every key with hi >= prefix
+  uint32_t tk[NI];
+  int n_gt = 0;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    tk[j] = (hi[j] == q.prefix) ? lo[j] : 0u;
+    n_gt += __popcll(__ballot(hi[j] > q.prefix));
+  }
+  KthSearch qt = kth_begin<NI>(tk, k - n_gt);
+  while (qt.bit >= 0) kth_step<NI>(qt, tk, k - n_gt);
+  return Top64{q.prefix, qt.prefix};
+}
+
+template <int NI>
+__device__ __forceinline__ bool top64_take(const Top64& s, uint32_t hi, uint32_t lo) {
+  return hi != 0u && (hi > s.T || (hi == s.T && lo >= s.T2));
+}
+
+// Write the taken keys to buf[0..k) (slot order), buf zero-padded to 64.
+template <int NI>
+__device__ __forceinline__ void top64_collect(const uint32_t (&hi)[NI], const uint32_t (&lo)[NI],
+                                              const Top64& s, uint64_t* buf) {
   const int l = lane();
+  buf[l] = 0ull;
+  wave_lds_fence();
   int base = 0;
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const bool p = keys[j] >= T && keys[j] != 0;
-    const uint64_t m = __ballot(p);
-    const int slot = base + mbcnt(m);
-    if (p && slot < 64) buf[slot] = keys[j];
+    const bool in = top64_take<NI>(s, hi[j], lo[j]);
+    const uint64_t m = __ballot(in);
+    if (in) buf[base + mbcnt(m)] = (static_cast<uint64_t>(hi[j]) << 32) | lo[j];
     base += __popcll(m);
   }
   wave_lds_fence();
-  uint64_t key = (l < k) ? buf[l] : 0ull;
+}
+
+// Items of one axis with value key >= v, compacted in index order into
+// cand[0..128) as (key << 32 | ~index), zero-padded; returns them two per
+// lane (cand[l], cand[64 + l]).  Requires at most 128 such items.
+template <int NI>
+__device__ __forceinline__ void axis_compact(const uint32_t (&vk)[NI], uint32_t v, uint64_t* cand,
+                                             uint32_t (&hi)[2], uint32_t (&lo)[2]) {
+  const int l = lane();
+  cand[l] = 0ull;
+  cand[64 + l] = 0ull;
   wave_lds_fence();
-  return bitonic_desc(key);
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const bool in = vk[j] >= v && vk[j] != 0u;
+    const uint64_t m = __ballot(in);
+    if (in) cand[base + mbcnt(m)] = (static_cast<uint64_t>(vk[j]) << 32) |
+                                    static_cast<uint32_t>(~(j * 64 + l));
+    base += __popcll(m);
+  }
+  wave_lds_fence();
+  const uint64_t a = cand[l], b = cand[64 + l];
+  hi[0] = static_cast<uint32_t>(a >> 32);
+  lo[0] = static_cast<uint32_t>(a);
+  hi[1] = static_cast<uint32_t>(b >> 32);
+  lo[1] = static_cast<uint32_t>(b);
+  wave_lds_fence();
+}
+
+// Per-lane two largest keys (0 = empty).
+template <int NI>
+__device__ __forceinline__ void lane_top2(const uint32_t (&vk)[NI], uint32_t (&t)[2]) {
+  uint32_t t1 = 0u, t2 = 0u;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const uint32_t v = vk[j];
+    t2 = v > t1 ? t1 : (v > t2 ? v : t2);
+    t1 = v > t1 ? v : t1;
+  }
+  t[0] = t1;
+  t[1] = t2;
 }
 
 __device__ __forceinline__ void write_outputs(uint64_t best, int t, int K,
@@ -252,26 +249,10 @@ __device__ __forceinline__ void write_outputs(uint64_t best, int t, int K,
   }
 }
 
-// ln sum exp over one row held NI per lane (invalid slots excluded), as
-// m + ln sum exp(z - m) with m the row maximum.
-template <int NI>
-__device__ __forceinline__ float row_lse(const float (&z)[NI], uint32_t valid) {
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NI; ++j)
-    if ((valid >> j) & 1u) m = fmaxf(m, z[j]);
-  m = wave_max(m);
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < NI; ++j)
-    if ((valid >> j) & 1u) s += expf(z[j] - m);
-  s = wave_sum(s);
-  return m + logf(s);
-}
-
 struct TopkLds {
-  uint32_t hist[256];
-  uint64_t buf[64];
+  uint64_t cand[2][128]; // per axis: the items that pass the pre-filter
+  uint64_t buf[2][64];   // per axis: selected items, then the merge's K cells
+  uint64_t srt[2][64];   // rank-sorted copies
   float av[64];
   float bv[64];
   uint32_t R[64];
@@ -298,42 +279,94 @@ __global__ __launch_bounds__(256) void product_topk_kernel(
   if (t >= L) return;  // the whole wave leaves together
   TopkLds& S = smem[w];
 
-  // ---- per axis: log-softmax, then the k' best lines in rank order
-#pragma unroll 1
-  for (int axis = 0; axis < 2; ++axis) {
-    const int n = axis ? Nc : Nr;
-    const float* src = axis ? Zc + static_cast<size_t>(t) * Nc : Zr + static_cast<size_t>(t) * Nr;
-    float* dst = axis ? col_logp : row_logp;
-    float z[NI];
-    uint32_t valid = 0;
+  // ---- both logit rows, then both log-softmax normalisers
+  const float* zr_row = Zr + static_cast<size_t>(t) * Nr;
+  const float* zc_row = Zc + static_cast<size_t>(t) * Nc;
+  float zr[NI], zc[NI];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int i = j * 64 + l;
-      z[j] = 0.f;
-      if (i < n) {
-        z[j] = src[i];
-        valid |= 1u << j;
-      }
-    }
-    const float lse = row_lse<NI>(z, valid);
-    uint32_t vk[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const float a = z[j] - lse;
-      vk[j] = fkey(a);
-      if (dst && ((valid >> j) & 1u)) dst[static_cast<size_t>(t) * n + j * 64 + l] = a;
-    }
-    if (l == 0) lse_out[2 * static_cast<size_t>(t) + axis] = lse;
-    const Sel32 sel = wave_select32<NI>(vk, valid, kp, S.hist);
-    const uint64_t kk = axis_collect_sorted<NI>(vk, valid, sel, kp, S.buf);
-    int32_t* out = axis ? col_sel : row_sel;
-    if (l < kp) {
-      (axis ? S.bv : S.av)[l] = sel_val(kk);
-      (axis ? S.C : S.R)[l] = sel_idx(kk);
-      out[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(kk));
-    }
+  for (int j = 0; j < NI; ++j) {
+    const int i = j * 64 + l;
+    zr[j] = (i < Nr) ? zr_row[i] : -INFINITY;
+    zc[j] = (i < Nc) ? zc_row[i] : -INFINITY;
   }
-  wave_lds_fence();
+  float mr = -INFINITY, mc = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    mr = fmaxf(mr, zr[j]);
+    mc = fmaxf(mc, zc[j]);
+  }
+  mr = wave_max(mr);
+  mc = wave_max(mc);
+  float sr = 0.f, sc = 0.f;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    if (j * 64 + l < Nr) sr += __expf(zr[j] - mr);
+    if (j * 64 + l < Nc) sc += __expf(zc[j] - mc);
+  }
+  sr = wave_sum(sr);
+  sc = wave_sum(sc);
+  const float lse_r = mr + __logf(sr), lse_c = mc + __logf(sc);
+  if (l == 0) {
+    lse_out[2 * static_cast<size_t>(t)] = lse_r;
+    lse_out[2 * static_cast<size_t>(t) + 1] = lse_c;
+  }
+  // value keys of a = z - lse (0 = no item); optional log-probability rows
+  uint32_t kr[NI], kc[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = j * 64 + l;
+    const float ar = zr[j] - lse_r, ac = zc[j] - lse_c;
+    kr[j] = (i < Nr) ? fkey(ar) : 0u;
+    kc[j] = (i < Nc) ? fkey(ac) : 0u;
+    if (row_logp && i < Nr) row_logp[static_cast<size_t>(t) * Nr + i] = ar;
+    if (col_logp && i < Nc) col_logp[static_cast<size_t>(t) * Nc + i] = ac;
+  }
+
+  // ---- the k' best rows and columns.  Pre-filter: v = the k'-th largest of
+  // the per-lane top-2 keys is a lower bound of the k'-th largest key (k' keys
+  // are >= v), and for Gaussian-like rows only ~70 keys reach it.  Those are
+  // compacted two per lane and searched exactly; more than 128 falls back to
+  // the search over all slots.  Both axes advance together.
+  uint32_t tr[2], tc[2];
+  lane_top2<NI>(kr, tr);
+  lane_top2<NI>(kc, tc);
+  KthSearch fr = kth_begin<2>(tr, kp), fc = kth_begin<2>(tc, kp);
+  while (fr.bit >= 0 || fc.bit >= 0) {
+    kth_step<2>(fr, tr, kp);
+    kth_step<2>(fc, tc, kp);
+  }
+  const bool cr = wave_count_ge<NI>(kr, fr.prefix) <= 128;
+  const bool cc = wave_count_ge<NI>(kc, fc.prefix) <= 128;
+  if (cr && cc) {
+    uint32_t hr[2], lr[2], hc[2], lc[2];
+    axis_compact<NI>(kr, fr.prefix, S.cand[0], hr, lr);
+    axis_compact<NI>(kc, fc.prefix, S.cand[1], hc, lc);
+    KthSearch qr = kth_begin<2>(hr, kp), qc = kth_begin<2>(hc, kp);
+    while (qr.bit >= 0 || qc.bit >= 0) {
+      kth_step<2>(qr, hr, kp);
+      kth_step<2>(qc, hc, kp);
+    }
+    top64_collect<2>(hr, lr, top64_finish<2>(hr, lr, kp, qr), S.buf[0]);
+    top64_collect<2>(hc, lc, top64_finish<2>(hc, lc, kp, qc), S.buf[1]);
+  } else {  // rare: search all slots
+    KthSearch qr = kth_begin<NI>(kr, kp), qc = kth_begin<NI>(kc, kp);
+    while (qr.bit >= 0 || qc.bit >= 0) {
+      kth_step<NI>(qr, kr, kp);
+      kth_step<NI>(qc, kc, kp);
+    }
+    axis_collect<NI>(kr, qr, kp, S.buf[0]);
+    axis_collect<NI>(kc, qc, kp, S.buf[1]);
+  }
+  const uint64_t rk = rank_sort64(S.buf[0], S.srt[0], kp);
+  const uint64_t ck = rank_sort64(S.buf[1], S.srt[1], kp);
+  if (l < kp) {
+    S.av[l] = sel_val(rk);
+    S.R[l] = sel_idx(rk);
+    S.bv[l] = sel_val(ck);
+    S.C[l] = sel_idx(ck);
+    row_sel[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(rk));
+    col_sel[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(ck));
+  }
 
   // ---- staircase P: row r contributes columns c < len_r = min(k', K / (r + 1))
   const int len = (l < kp) ? min(kp, K / (l + 1)) : 0;
@@ -342,11 +375,12 @@ __global__ __launch_bounds__(256) void product_topk_kernel(
   if (l == 0) S.poff[0] = 0;
   const int P = __builtin_amdgcn_readlane(inc, 63);
   wave_lds_fence();
-  uint64_t pk[kStairItems];
+  uint32_t phi[kStairItems], plo[kStairItems];  // cell key = value key << 32 | ~expert
 #pragma unroll
   for (int j = 0; j < kStairItems; ++j) {
     const int p = l + 64 * j;
-    pk[j] = 0ull;
+    phi[j] = 0u;
+    plo[j] = 0u;
     if (p < P) {
       int lo = 0, hi = kp;  // largest r with poff[r] <= p
       while (hi - lo > 1) {
@@ -354,12 +388,17 @@ __global__ __launch_bounds__(256) void product_topk_kernel(
         if (S.poff[mid] <= p) lo = mid; else hi = mid;
       }
       const int r = lo, c = p - S.poff[r];
-      const float sv = S.av[r] + S.bv[c];
-      pk[j] = sel_key(sv, S.R[r] * static_cast<uint32_t>(Nc) + S.C[c]);
+      phi[j] = fkey(S.av[r] + S.bv[c]);
+      plo[j] = ~(S.R[r] * static_cast<uint32_t>(Nc) + S.C[c]);
     }
   }
-  const uint64_t Tp = wave_select64<kStairItems>(pk, K, S.hist);
-  const uint64_t best = wave_collect_sorted<kStairItems>(pk, Tp, K, S.buf);
+  // K best cells by (value desc, expert asc): value threshold first; cells
+  // tied at it are split by a second search on ~expert among them.
+  KthSearch qm = kth_begin<kStairItems>(phi, K);
+  while (qm.bit >= 0) kth_step<kStairItems>(qm, phi, K);
+  uint64_t* mb = S.buf[0];
+  top64_collect<kStairItems>(phi, plo, top64_finish<kStairItems>(phi, plo, K, qm), mb);
+  const uint64_t best = rank_sort64(mb, S.srt[0], K);
   const uint32_t tau = static_cast<uint32_t>(__shfl(best, K - 1) >> 32);
 
   // ---- a cell past the staircase can only tie at tau; check each row's first
