@@ -128,13 +128,17 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
 // from global memory into a 4-stage LDS ring with global_load_lds_dwordx4
 // (three K steps in flight, no register staging).  An LDS row holds 32 bf16
 // (64 B = four 16-B chunks); chunk c of row r is stored at position
-// c ^ ((r >> 2) & 3), so the 16 rows a fragment read touches fall on
-// distinct banks.
+// c ^ ((r >> 1) & 3).  A 16-byte-per-lane LDS read is served eight lanes at a
+// time from one 128-byte bank window; the eight rows such a group of a
+// fragment read touches (r .. r+7, same chunk) then land on eight distinct
+// 16-byte bank groups (measured on gfx950: the (r >> 2) swizzle costs four
+// conflict cycles per read, this one none).
 constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4;
 constexpr int GSTAGE_BYTES = (GBM + GBN) * GBK * 2;  // 32 KiB
 
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+  return row * 64 + (swz_chunk(row, chunk) << 4);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
@@ -142,6 +146,67 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// vmcnt <= N and every LDS access of this wave complete (lgkmcnt = 0)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Issue the direct global->LDS loads of K step kt into its ring stage: each
+// wave fills 2 KiB of A and 2 KiB of B with two 1-KiB instructions each.
+__device__ __forceinline__ void gemm_issue(uint8_t* smem, const uint16_t* const (&asrc)[2],
+                                           const uint16_t* const (&bsrc)[2], int wv, int kt) {
+  uint8_t* st = smem + (kt % GSTAGES) * GSTAGE_BYTES;
+  const int k0 = kt * GBK;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wv * 2 + u) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + GBM * 64 + (wv * 2 + u) * 1024, 16, 0, 0);
+  }
+}
+
+// Read one stage's MFMA fragments: 8 A tiles (16 rows each) and 4 B tiles.
+__device__ __forceinline__ void gemm_read_frags(const uint8_t* smem, int kt, int wm, int wn,
+                                                int fr, int fc, bf16x8 (&af)[8],
+                                                bf16x8 (&bfr)[4]) {
+  const uint8_t* st = smem + (kt % GSTAGES) * GSTAGE_BYTES;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    af[i] = *reinterpret_cast<const bf16x8*>(st + swz(wm * 128 + i * 16 + fr, fc));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bfr[j] = *reinterpret_cast<const bf16x8*>(st + GBM * 64 + swz(wn * 64 + j * 16 + fr, fc));
+}
+
+// One pipeline iteration (see the kernel): stage kt's fragments are in
+// (ca, cb); stage kt+1's go to (na, nb).
+__device__ __forceinline__ void gemm_step(uint8_t* smem, const uint16_t* const (&asrc)[2],
+                                          const uint16_t* const (&bsrc)[2], int wv, int wm,
+                                          int wn, int fr, int fc, int kt, int nk,
+                                          const bf16x8 (&ca)[8], const bf16x8 (&cb)[4],
+                                          bf16x8 (&na)[8], bf16x8 (&nb)[4],
+                                          f32x4 (&acc)[8][4]) {
+  if (kt + 1 < nk) {
+    // stages issued so far: 0 .. min(kt + 3, nk - 1); those after kt + 1 may stay in flight
+    // (and this wave's reads of stage kt's fragments complete, so the slot
+    // can be refilled once every wave has passed the barrier)
+    const int after = min(kt + 3, nk - 1) - (kt + 1);
+    if (after >= 2) wait_vmcnt_lds<8>();
+    else if (after == 1) wait_vmcnt_lds<4>();
+    else wait_vmcnt_lds<0>();
+    // a bare barrier: a fenced one would also wait for the stages in flight
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (kt + GSTAGES < nk) gemm_issue(smem, asrc, bsrc, wv, kt + GSTAGES);
+    gemm_read_frags(smem, kt + 1, wm, wn, fr, fc, na, nb);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
 }
 
 __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
@@ -161,31 +226,21 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
 
   // Direct loads: each wave fills 2 KiB of A (32 rows) and 2 KiB of B per
   // stage with two 1-KiB instructions each; lane i of an instruction lands
-  // on row r = base + i / 4, stored chunk i % 4, so it fetches logical chunk
-  // (i % 4) ^ ((r >> 2) & 3).  Rows past the end re-read a valid row (their
-  // results are never stored).
+  // on row r = base + i / 4, stored chunk i % 4, so it fetches the logical
+  // chunk that swz_chunk maps there (the map is its own inverse).  Rows past
+  // the end re-read a valid row (their results are never stored).
   const uint16_t* asrc[2];
   const uint16_t* bsrc[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int r = (wv * 2 + u) * 16 + (l >> 2);
-    const int c = (l & 3) ^ ((r >> 2) & 3);
+    const int c = swz_chunk(r, l & 3);
     const int t = min(m0 + r, L - 1);
     asrc[u] = x + static_cast<size_t>(t) * d + c * 8;
     const int n = min(n0 + r, NT - 1);
     bsrc[u] = (n < Nr ? wr + static_cast<size_t>(n) * d : wc + static_cast<size_t>(n - Nr) * d) +
               c * 8;
   }
-  auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % GSTAGES) * GSTAGE_BYTES;
-    const int k0 = kt * GBK;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wv * 2 + u) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + GBM * 64 + (wv * 2 + u) * 1024, 16, 0,
-                                       0);
-    }
-  };
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -196,33 +251,27 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
   const int wm = wv >> 2, wn = wv & 3;  // 2 x 4 waves
   const int fr = l & 15, fc = l >> 4;
   const int nk = d / GBK;
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = nk - 1 - kt;  // stages issued after this one (at most 2)
-    if (ahead >= 2) wait_vmcnt<8>();
-    else if (ahead == 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-    // Every wave's loads for stage kt have landed (the wait above) and every
-    // wave is done reading stage kt-1, whose slot the next issue reuses.  A
-    // bare barrier: a fenced one would also wait for the stages still in
-    // flight.
-    __builtin_amdgcn_s_barrier();
-    if (kt + 3 < nk) issue(kt + 3);
-    const uint8_t* st = smem + (kt % GSTAGES) * GSTAGE_BYTES;
-    bf16x8 af[8], bfr[4];
+  // Software pipeline.  Iteration kt: wait until stage kt+1 has landed,
+  // barrier, refill the slot of stage kt (its fragments are already in
+  // registers) with stage kt+4, read stage kt+1's fragments into the other
+  // register set, then run stage kt's MFMAs while those reads are in flight.
+  // Three stages of global loads stay in flight behind the one being read.
+  bf16x8 af[2][8], bfr[2][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(st + swz(wm * 128 + i * 16 + fr, fc));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(st + GBM * 64 + swz(wn * 64 + j * 16 + fr, fc));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  for (int u = 0; u < GSTAGES; ++u)
+    if (u < nk) gemm_issue(smem, asrc, bsrc, wv, u);
+  if (nk > 3) wait_vmcnt<12>();
+  else if (nk == 3) wait_vmcnt<8>();
+  else if (nk == 2) wait_vmcnt<4>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  gemm_read_frags(smem, 0, wm, wn, fr, fc, af[0], bfr[0]);
+  for (int kt = 0; kt < nk; kt += 2) {
+    gemm_step(smem, asrc, bsrc, wv, wm, wn, fr, fc, kt, nk, af[0], bfr[0], af[1], bfr[1], acc);
+    if (kt + 1 < nk)
+      gemm_step(smem, asrc, bsrc, wv, wm, wn, fr, fc, kt + 1, nk, af[1], bfr[1], af[0], bfr[0],
+                acc);
   }
 
   // Accumulator lane layout (16x16 output tile): column = lane % 16,
