@@ -112,6 +112,9 @@ CASES = {
                    zipf_s=1.1, index=205),
     "d64": custom(L=50, d=64, Nr=8, Nc=8, kprime=4, K=4, B=3, dtype="bf16", index=206),
     "d4096": custom(L=40, d=4096, Nr=32, Nc=32, kprime=8, K=8, B=16, dtype="bf16", index=207),
+    # the largest grid line count per axis (2048: 32 slots per lane in the top-K)
+    "grid2048x64": custom(L=100, d=128, Nr=2048, Nc=64, kprime=64, K=64, B=100, dtype="bf16",
+                          index=209),
 }
 
 
@@ -177,7 +180,8 @@ FAULTED_ONCE = ("faulted the GPU (memory aperture violation) in its first run, i
     (40, 24, 8, 8, 0.5),
     pytest.param(64, 64, 16, 12, 0.25, marks=pytest.mark.skip(reason=FAULTED_ONCE)),
     (128, 96, 64, 64, 1.0), (33, 65, 5, 25, 0.5), (1024, 1024, 64, 64, 0.125),
-    (64, 64, 16, 12, 0.5), (100, 80, 32, 20, 0.25)])
+    (64, 64, 16, 12, 0.5), (100, 80, 32, 20, 0.25),
+    (2048, 64, 64, 64, 0.125), (1500, 2048, 48, 30, 0.25)])  # 32 slots per lane
 def test_topk_with_ties_is_bit_exact(Nr, Nc, kp, K, step):
     # Quantised inputs produce many equal values, so ties decide the order and
     # the merge's exact fallback (a tie at the staircase threshold) runs.
