@@ -18,14 +18,15 @@ LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
     "omni_abi_version", "omni_status_string", "omni_router_logits",
     "omni_product_topk_workspace", "omni_product_topk", "omni_schedule_max_groups",
     "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_mode",
-    "omni_atomic_forward_workspace", "omni_atomic_forward",
+    "omni_atomic_forward_workspace", "omni_atomic_forward", "omni_routed_backward_workspace",
+    "omni_routed_backward",
 )
 
 
@@ -57,6 +58,8 @@ _SIGS = {
     "omni_atomic_forward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "omni_atomic_forward": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
                                  ctypes.POINTER(ScheduleStruct), _vp, _i, _i, _vp, _sz, _vp]),
+    "omni_routed_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "omni_routed_backward": (_i, [_i, _i, _i, _i, _i, _i] + [_vp] * 19 + [_sz, _vp]),
 }
 
 _lib = None
@@ -286,3 +289,53 @@ def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, str
     sched = schedule_tasks(sel["expert_idx"], sel["gate"], N, B, stream=stream)
     y = atomic_forward(x, w, v, sched, stream=stream, mode=mode)
     return {"row_logits": zr, "col_logits": zc, **sel, "schedule": sched, "y": y}
+
+
+def routed_backward(x, wr_t, wc_t, w, v, expert_idx, gate, dy, out=None, workspace=None,
+                    stream=None):
+    """omni_routed_backward: gradients of the routed layer for upstream dy [L, d] float32.
+
+    Returns dict dx [L, d], dwr [Nr, d], dwc [Nc, d], drb [Nr], dcb [Nc],
+    counts [2], active [min(N, L*K)], dw, dv [min(N, L*K), d] (row r is the
+    gradient of expert active[r], r < counts[0]), dgate [L, K]; all float32
+    except counts / active (int32)."""
+    L, d = x.shape
+    Nr, Nc = wr_t.shape[0], wc_t.shape[0]
+    N = Nr * Nc
+    K = expert_idx.shape[1]
+    _req(x, "x")
+    for name, t in (("wr_t", wr_t), ("wc_t", wc_t)):
+        _req(t, name, x.dtype)
+    _req(w, "w", x.dtype, (N, d))
+    _req(v, "v", x.dtype, (N, d))
+    _req(expert_idx, "expert_idx", torch.int32, (L, K))
+    _req(gate, "gate", torch.float32, (L, K))
+    _req(dy, "dy", torch.float32, (L, d))
+    dev = x.device
+    o = dict(out or {})
+    na = max(1, min(N, L * K))
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+        _req(t, name, dtype, shape)
+        return t
+    r = {"dx": get("dx", (L, d), torch.float32), "dwr": get("dwr", (Nr, d), torch.float32),
+         "dwc": get("dwc", (Nc, d), torch.float32), "drb": get("drb", (Nr,), torch.float32),
+         "dcb": get("dcb", (Nc,), torch.float32), "counts": get("counts", (2,), torch.int32),
+         "active": get("active", (na,), torch.int32),
+         "dw": get("dw", (na, d), torch.float32), "dv": get("dv", (na, d), torch.float32),
+         "dgate": get("dgate", (L, K), torch.float32)}
+    code = _dtype_code(x)
+    nws = lib().omni_routed_backward_workspace(code, L, d, Nr, Nc, K)
+    ws = workspace
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    _check("omni_routed_backward", lib().omni_routed_backward(
+        code, L, d, Nr, Nc, K, _ptr(x), _ptr(wr_t), _ptr(wc_t), _ptr(w), _ptr(v),
+        _ptr(expert_idx), _ptr(gate), _ptr(dy), _ptr(r["dx"]), _ptr(r["dwr"]), _ptr(r["dwc"]),
+        _ptr(r["drb"]), _ptr(r["dcb"]), _ptr(r["counts"]), _ptr(r["active"]), _ptr(r["dw"]),
+        _ptr(r["dv"]), _ptr(r["dgate"]), _ptr(ws), nws, _stream(stream)))
+    r["workspace"] = ws
+    return r

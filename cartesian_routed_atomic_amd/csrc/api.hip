@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -183,6 +183,40 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                                                 sched->task_token, sched->task_expert,
                                                 sched->task_gate, sched->task_index, y,
                                                 accumulate != 0, ws, stream));
+}
+
+size_t omni_routed_backward_workspace(omni_dtype dt, int L, int d, int Nr, int Nc, int K) {
+  (void)dt;
+  if (L < 0 || d < 1 || Nr < 1 || Nc < 1 || K < 1 || K > 64) return 0;
+  if (!fits_i32(static_cast<long long>(Nr) * Nc) || !fits_i32(static_cast<long long>(L) * K))
+    return 0;
+  return omni::routed_backward_ws_bytes(L, d, Nr, Nc, K);
+}
+
+omni_status omni_routed_backward(omni_dtype dt, int L, int d, int Nr, int Nc, int K,
+                                 const void* x, const void* wr_t, const void* wc_t,
+                                 const void* w, const void* v, const int32_t* expert_idx,
+                                 const float* gate, const float* dy, float* dx, float* dwr_t,
+                                 float* dwc_t, float* drow_bias, float* dcol_bias,
+                                 int32_t* counts, int32_t* active, float* dw, float* dv,
+                                 float* dgate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
+  if (L < 0 || d < 1 || Nr < 1 || Nc < 1 || K < 1) return OMNI_ERR_INVALID_ARG;
+  if (!fits_i32(static_cast<long long>(Nr) * Nc) || !fits_i32(static_cast<long long>(L) * K) ||
+      !fits_i32(static_cast<long long>(L) * d))
+    return OMNI_ERR_INVALID_ARG;
+  if (!wr_t || !wc_t || !w || !v || !dwr_t || !dwc_t || !counts || !active || !dw || !dv)
+    return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && (!x || !expert_idx || !gate || !dy || !dx)) return OMNI_ERR_INVALID_ARG;
+  if (!omni::routed_backward_supported(dt == OMNI_BF16, d, K)) return OMNI_ERR_UNSUPPORTED;
+  const void* rows[] = {x, wr_t, wc_t, w, v, dy, dx, dwr_t, dwc_t, dw, dv};
+  for (const void* p : rows)
+    if (p && !aligned16(p)) return OMNI_ERR_INVALID_ARG;
+  const size_t need = omni_routed_backward_workspace(dt, L, d, Nr, Nc, K);
+  if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
+  return hip_status(omni::launch_routed_backward(
+      dt == OMNI_BF16, L, d, Nr, Nc, K, x, wr_t, wc_t, w, v, expert_idx, gate, dy, dx, dwr_t,
+      dwc_t, drow_bias, dcol_bias, counts, active, dw, dv, dgate, ws, stream));
 }
 
 }  // extern "C"

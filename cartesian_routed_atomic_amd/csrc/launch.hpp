@@ -44,4 +44,14 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
                                  const int32_t* task_index, float* y, bool accumulate, void* ws,
                                  hipStream_t s);
 
+// backward.hip
+size_t routed_backward_ws_bytes(int L, int d, int Nr, int Nc, int K);
+bool routed_backward_supported(int bf16, int d, int K);
+hipError_t launch_routed_backward(int bf16, int L, int d, int Nr, int Nc, int K, const void* x,
+                                  const void* wr, const void* wc, const void* w, const void* v,
+                                  const int32_t* expert_idx, const float* gate, const float* dy,
+                                  float* dx, float* dwr, float* dwc, float* drb, float* dcb,
+                                  int32_t* counts, int32_t* active, float* dw, float* dv,
+                                  float* dgate, void* ws, hipStream_t s);
+
 }  // namespace omni

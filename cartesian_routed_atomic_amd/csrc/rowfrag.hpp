@@ -1,0 +1,110 @@
+// Row fragments shared by the executor and its backward: how one wave holds
+// a d-long row of W, V or x (bf16 bits or float32) spread over its 64 lanes,
+// the per-lane partial dot product, and the store of a float32 result row.
+#pragma once
+#include "device.hpp"
+
+namespace omni {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A row fragment of one lane: EPL elements held raw (as loaded) so a load
+// can stay in flight until the first use; element q = c * VEC + j maps to
+// row[c * 64 * VEC + lane * VEC + j].
+template <typename T, int EPL> struct RowFrag;
+
+template <int EPL> struct RowFrag<uint16_t, EPL> {  // bfloat16 bits
+  static constexpr int VEC = EPL < 8 ? EPL : 8;
+  static constexpr int NCH = EPL / VEC;
+  static constexpr int NW = (EPL + 1) / 2;
+  uint32_t w[NW];
+  __device__ __forceinline__ void load(const uint16_t* row, int l) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint16_t* p = row + c * 64 * VEC + l * VEC;
+      if constexpr (VEC == 8) *reinterpret_cast<uint4*>(&w[c * 4]) = *reinterpret_cast<const uint4*>(p);
+      else if constexpr (VEC == 4) *reinterpret_cast<uint2*>(&w[c * 2]) = *reinterpret_cast<const uint2*>(p);
+      else if constexpr (VEC == 2) w[c] = *reinterpret_cast<const uint32_t*>(p);
+      else w[0] = static_cast<uint32_t>(*p);
+    }
+  }
+  __device__ __forceinline__ float get(int q) const {
+    if constexpr (VEC == 1) return bf_lo(w[0]);
+    else return (q & 1) ? bf_hi(w[q >> 1]) : bf_lo(w[q >> 1]);
+  }
+};
+
+template <int EPL> struct RowFrag<float, EPL> {
+  static constexpr int VEC = EPL < 4 ? EPL : 4;
+  static constexpr int NCH = EPL / VEC;
+  float f[EPL];
+  __device__ __forceinline__ void load(const float* row, int l) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const float* p = row + c * 64 * VEC + l * VEC;
+      if constexpr (VEC == 4) *reinterpret_cast<float4*>(&f[c * 4]) = *reinterpret_cast<const float4*>(p);
+      else if constexpr (VEC == 2) *reinterpret_cast<float2*>(&f[c * 2]) = *reinterpret_cast<const float2*>(p);
+      else f[0] = *p;
+    }
+  }
+  __device__ __forceinline__ float get(int q) const { return f[q]; }
+};
+
+// Partial dot product of this lane's fragment elements.
+template <int EPL>
+__device__ __forceinline__ float frag_dot(const RowFrag<uint16_t, EPL>& a,
+                                          const RowFrag<uint16_t, EPL>& b) {
+  float p = 0.f;
+  if constexpr (EPL == 1) {
+    p = a.get(0) * b.get(0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RowFrag<uint16_t, EPL>::NW; ++i)
+      p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w[i]),
+                                          __builtin_bit_cast(bf16x2, b.w[i]), p, false);
+  }
+  return p;
+}
+template <int EPL>
+__device__ __forceinline__ float frag_dot(const RowFrag<float, EPL>& a,
+                                          const RowFrag<float, EPL>& b) {
+  float p = 0.f;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) p = fmaf(a.f[q], b.f[q], p);
+  return p;
+}
+
+__device__ __forceinline__ int rdlane(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+__device__ __forceinline__ float rdlane(float v, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
+}
+
+// Store (or add) a lane's accumulators to its columns of a y row, in the
+// RowFrag element layout, with 16-byte stores where the layout allows.
+template <typename T, int EPL>
+__device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __restrict__ yrow,
+                                          int accumulate) {
+  constexpr int VEC = RowFrag<T, EPL>::VEC, NCH = RowFrag<T, EPL>::NCH;
+  const int l = lane();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    float* p = yrow + c * 64 * VEC + l * VEC;
+    if constexpr (VEC >= 4) {
+#pragma unroll
+      for (int j = 0; j < VEC; j += 4) {
+        float4 v = make_float4(acc[c * VEC + j], acc[c * VEC + j + 1], acc[c * VEC + j + 2],
+                               acc[c * VEC + j + 3]);
+        if (accumulate) {
+          const float4 o = *reinterpret_cast<const float4*>(p + j);
+          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        }
+        *reinterpret_cast<float4*>(p + j) = v;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) p[q] = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
+    }
+  }
+}
+
+}  // namespace omni

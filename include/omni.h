@@ -19,7 +19,8 @@
  *                           (group, token);
  *   4. omni_atomic_forward  execution of the schedule:
  *                           y_t = sum_k g_tk * silu(x_t . W[e_tk]) * V[e_tk],
- *                           expert-centric or token-centric (same result).
+ *                           expert-centric or token-centric (same result);
+ *   5. omni_routed_backward gradients of the whole routed layer.
  *
  * Conventions shared by every call
  *   - All pointers except the `omni_schedule` descriptor itself are DEVICE
@@ -61,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 3 */
+int omni_abi_version(void);  /* 4 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -226,6 +227,45 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                                 const omni_schedule* sched, float* y, int accumulate,
                                 omni_exec_mode mode, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * omni_routed_backward — gradients of the routed layer for a given upstream
+ * gradient dy = dL/dy.  The pages train models with this layer but print no
+ * backward pass; the gradients follow from the forward above by the chain rule
+ * (gist.science explainer §2.1-§2.2; interactive explainer "Cartesian Product
+ * Router", "Expert-Centric Scheduling").  The expert selection is piecewise
+ * constant and passes no gradient; sigma = SiLU, gate = softmax of the K
+ * selected scores, as in the forward.
+ *
+ *   per task (t, e = i * Nc + j, gate g): u = dy_t . V[e], h = x_t . W[e]
+ *     dV[e] += g silu(h) dy_t      dW[e] += g silu'(h) u x_t
+ *     dx_t  += g silu'(h) u W[e]   dgate = silu(h) u
+ *   dS_k = g_k (dgate_k - sum_j g_j dgate_j);  dz_r[t, i_k] += dS_k, dz_c[t, j_k] += dS_k
+ *   (the log-softmax backward adds nothing more because sum_k dS_k = 0)
+ *   dx += dz_r Wr + dz_c Wc;  dWr = dz_r^T x;  dWc = dz_c^T x;  d bias = column sums
+ *
+ * Inputs: x [L, d], wr_t [Nr, d], wc_t [Nc, d], w [N, d], v [N, d] of dt
+ * (N = Nr * Nc); expert_idx, gate [L, K]: the forward's omni_product_topk
+ * output; dy [L, d] float32.
+ * Outputs (float32, overwritten): dx [L, d]; dwr_t [Nr, d]; dwc_t [Nc, d];
+ * drow_bias [Nr], dcol_bias [Nc] (either may be null); counts[0] = number of
+ * active experts n (counts[1] = n as well); active [min(N, L*K)] ascending
+ * active expert ids; dw, dv [min(N, L*K), d]: row r is the gradient of
+ * W[active[r]] / V[active[r]] for r < n (rows from n on are left untouched);
+ * dgate [L, K] (may be null).
+ * ws / ws_bytes: at least omni_routed_backward_workspace(...) bytes, 256-byte
+ * aligned.  Requires K <= 64, d = 64 * 2^p with rows of at most 4 KiB
+ * (bf16 d <= 2048, float32 d <= 1024), else UNSUPPORTED; 16-byte aligned
+ * row arrays.  Deterministic: every sum runs in a fixed order.
+ */
+size_t omni_routed_backward_workspace(omni_dtype dt, int L, int d, int Nr, int Nc, int K);
+omni_status omni_routed_backward(omni_dtype dt, int L, int d, int Nr, int Nc, int K,
+                                 const void* x, const void* wr_t, const void* wc_t,
+                                 const void* w, const void* v, const int32_t* expert_idx,
+                                 const float* gate, const float* dy, float* dx, float* dwr_t,
+                                 float* dwc_t, float* drow_bias, float* dcol_bias,
+                                 int32_t* counts, int32_t* active, float* dw, float* dv,
+                                 float* dgate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 3
+    assert lib.omni_abi_version() == 4
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -157,3 +157,27 @@ def test_atomic_forward_auto_mode(lib):
     assert mode(0, 8192, 2048, 1 << 20, 64, 256) == 1      # float32 row over 4 KiB
     assert mode(3, 8192, 2048, 1 << 20, 64, 256) == 0      # bad dtype
     assert mode(1, 8192, 2048, 1 << 20, 0, 256) == 0       # bad K
+
+
+def test_routed_backward_argument_checks(lib):
+    f = lib.omni_routed_backward
+    nws = lib.omni_routed_backward_workspace(1, 4, 128, 8, 8, 4)
+    assert nws > 0
+    assert lib.omni_routed_backward_workspace(1, 4, 128, 8, 8, 65) == 0
+
+    def call(dt=1, L=4, d=128, Nr=8, Nc=8, K=4, x=FAKE, dy=FAKE, dw=FAKE, ws=FAKE, n=nws,
+             dwr=FAKE):
+        P = [x, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dy, FAKE, dwr, FAKE, None, None, FAKE,
+             FAKE, dw, FAKE, None]
+        return f(dt, L, d, Nr, Nc, K, *P, ws, n, None)
+    assert call(dt=2) == B.OMNI_ERR_INVALID_ARG
+    assert call(K=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(x=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(dw=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(dwr=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(K=65) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=4096) == B.OMNI_ERR_UNSUPPORTED           # bf16 rows over 4 KiB
+    assert call(dt=0, d=2048) == B.OMNI_ERR_UNSUPPORTED     # float32 rows over 4 KiB
+    assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
+    assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
