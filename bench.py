@@ -29,7 +29,7 @@ METRIC = "routed tokens/sec per atomic-expert layer at 1 GPU; % of HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 EXEC_SRCS = [os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", f)
-             for f in ("execute.hip", "device.hpp")]
+             for f in ("execute.hip", "rowfrag.hpp", "device.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
 EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing omni_routed_backward on the same batch")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the HIP-graph replay of the step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -238,6 +240,33 @@ def main():
         say(f"[bench] copy probe: 3 copies of {args.copy_probe_mib} MiB")
         del src, dst
 
+    bwd = None
+    if not args.no_backward and B.lib().omni_routed_backward_workspace(
+            1 if wl.dtype == "bf16" else 0, L, wl.d, wl.Nr, wl.Nc, K) > 0:
+        # one backward call of the routed layer for a seeded upstream gradient,
+        # on the selection of this batch; outputs and workspace allocated once
+        dy = torch.randn((L, wl.d), generator=torch.Generator(device=dev).manual_seed(7),
+                         device=dev, dtype=torch.float32)
+        gb = B.routed_backward(x, wr, wc, w, v, sel["expert_idx"], sel["gate"], dy)
+        bout = {k: t_ for k, t_ in gb.items() if k != "workspace"}
+        bws = gb["workspace"]
+        bwd_ms = ev_time(lambda: B.routed_backward(x, wr, wc, w, v, sel["expert_idx"],
+                                                   sel["gate"], dy, out=bout, workspace=bws),
+                         reps=5)
+        na = int(gb["counts"].cpu()[0])
+        NRC = wl.Nr + wl.Nc
+        # what the backward must move at least: each active expert's W and V
+        # rows once, x and dy once, dx, dW and dV (float32) once, the router
+        # rows once and their float32 gradients, the per-task lists
+        bwd_bytes = (2 * wl.d * s * na + L * wl.d * s + 4 * L * wl.d + 4 * L * wl.d
+                     + 8 * wl.d * na + NRC * wl.d * s + 4 * NRC * wl.d + 8 * M)
+        bwd = {"ms": bwd_ms, "bytes_alg": bwd_bytes,
+               "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+               "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "tokens_per_s": L / (bwd_ms * 1e-3), "n_active": na}
+        say(f"[bench] backward {bwd_ms:.3f} ms, {bwd['achieved']:.0f} GB/s "
+            f"({100 * bwd['frac']:.1f}% of HBM), {bwd['tokens_per_s']:.0f} tokens/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         say("[bench] timing the CPU oracle ...")
@@ -274,6 +303,7 @@ def main():
         "stages_ms": stages,
         "n_active": n_active,
         "expert_usage": n_active / wl.N,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -186,11 +186,11 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
 }
 
 size_t omni_routed_backward_workspace(omni_dtype dt, int L, int d, int Nr, int Nc, int K) {
-  (void)dt;
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
   if (L < 0 || d < 1 || Nr < 1 || Nc < 1 || K < 1 || K > 64) return 0;
   if (!fits_i32(static_cast<long long>(Nr) * Nc) || !fits_i32(static_cast<long long>(L) * K))
     return 0;
-  return omni::routed_backward_ws_bytes(L, d, Nr, Nc, K);
+  return omni::routed_backward_ws_bytes(dt == OMNI_BF16, L, d, Nr, Nc, K);
 }
 
 omni_status omni_routed_backward(omni_dtype dt, int L, int d, int Nr, int Nc, int K,

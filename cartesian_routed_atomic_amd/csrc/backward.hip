@@ -9,19 +9,19 @@
 //   dx_t += dz_r Wr + dz_c Wc,  dWr = dz_r^T x,  dWc = dz_c^T x, bias = column sums
 // The log-softmax backward dz = da - softmax(z) sum(da) reduces to dz = da
 // because sum_k dS_k = 0 exactly: the logit gradient is nonzero only on the
-// rows and columns of the selected experts, which is what makes the router
-// part a gather (dx) and a segmented reduction (dWr, dWc) instead of dense
-// GEMMs.
+// rows and columns of the selected experts.  Its part of dx is then a gather
+// of 2K router rows per token; dWr and dWc are one MFMA product
+// [dWr; dWc] = dz^T x over all tokens.
 //
 // Two kinds of kernels:
 //   bwd_token_kernel: one wave per token (x_t and dy_t in registers) walks the
 //     token's V rows (u_k), W rows (h_k -> dh_k, dg_k, c_k; dx += dh_k W[e])
-//     and router rows (dx += dS_k (Wr[i_k] + Wc[j_k])); writes dx_t and the
-//     per-task c, dh, dS, dg at the flat task id.
-//   seg_reduce_kernel + seg_fixup_kernel: out[row] = sum_task w_task src[token]
-//     over a task list sorted by output row (expert-major for dW and dV, by
-//     grid row / column for dWr and dWc).  The sorted lists are schedules with
-//     groups of one (B = 1) built by the forward's scheduling code.  Each wave
+//     and router rows (dx += dS_k (Wr[i_k] + Wc[j_k])); writes dx_t, the
+//     per-task c, dh, dS, dg at the flat task id, and the token's column of
+//     the transposed logit gradient dz^T.
+//   seg_reduce_kernel + seg_fixup_kernel: dV[row] = sum c dy[token] and
+//     dW[row] = sum dh x[token] over the expert-major task list, a schedule
+//     with groups of one (B = 1) built by the forward's scheduling code.  Each wave
 //     takes 64 consecutive tasks; rows whose tasks all lie in its chunk are
 //     written directly, rows that cross a chunk edge leave partial sums that a
 //     second kernel adds in chunk order, so every result is deterministic.
@@ -57,6 +57,7 @@ __device__ __forceinline__ void load_f32_as(const float* __restrict__ row, int l
 }
 
 constexpr int kBwdRing = 4;  // row slots per wave: three in flight
+constexpr int kSegEpl = 16;  // row elements per lane in the dV / dW reduction
 
 template <typename T, int EPL>
 __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
     const T* __restrict__ wr, const T* __restrict__ wc, const int32_t* __restrict__ expert_idx,
     const float* __restrict__ gate, const float* __restrict__ dy, int L, int K, int d, int N,
     int Nr, int Nc, float* __restrict__ dx, float* __restrict__ coef, float* __restrict__ dh_out,
-    float* __restrict__ ds_out, float* __restrict__ dgate) {
+    float* __restrict__ ds_out, float* __restrict__ dgate, float* __restrict__ dzt, int Lp) {
   using Frag = RowFrag<T, EPL>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
@@ -168,26 +169,96 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
     }
   }
   store_row<T, EPL>(acc, dx + static_cast<size_t>(t) * d, 0);
+  // this token's column of the transposed logit gradients: dz_r[t, i] is the
+  // sum of dS over the token's tasks in grid row i (summed in task order, and
+  // stored by the first such task), dz_c likewise at row Nr + j
+  float rsum = 0.f, csum = 0.f;
+  bool rfirst = true, cfirst = true;
+  for (int j = 0; j < K; ++j) {
+    const float dj = rdlane(my_ds, j);
+    if (rdlane(my_ri, j) == my_ri) {
+      rsum += dj;
+      rfirst = rfirst && j >= l;
+    }
+    if (rdlane(my_ci, j) == my_ci) {
+      csum += dj;
+      cfirst = cfirst && j >= l;
+    }
+  }
   if (l < K) {
     coef[tb + l] = my_c;
     dh_out[tb + l] = my_dh;
     ds_out[tb + l] = my_ds;
     if (dgate) dgate[tb + l] = my_dg;
+    if (rfirst) dzt[static_cast<size_t>(my_ri) * Lp + t] = rsum;
+    if (cfirst) dzt[static_cast<size_t>(Nr + my_ci) * Lp + t] = csum;
   }
-  (void)Nr;
 }
 
-// Row id of each expert / grid row / grid column: e / Nc and e mod Nc.
-__global__ __launch_bounds__(256) void split_ids_kernel(const int32_t* __restrict__ expert_idx,
-                                                        int M, int N, int Nc,
-                                                        int32_t* __restrict__ ri,
-                                                        int32_t* __restrict__ ci) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= M) return;
-  int e = expert_idx[m];
-  e = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
-  ri[m] = e / Nc;
-  ci[m] = e - (e / Nc) * Nc;
+// Row sums of the transposed logit gradients (the bias gradients) and their
+// bf16 copy for the GEMM.  One wave per row (Lp a multiple of 64), four float4
+// loads in flight per lane, lane partials added in a fixed order.
+__device__ __forceinline__ uint32_t bf16_rne2(float lo, float hi) {
+  // round to nearest even (finite values), two per word
+  const uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  return ((a + 0x7fffu + ((a >> 16) & 1u)) >> 16) |
+         ((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);
+}
+
+__global__ __launch_bounds__(256) void dz_rows_kernel(const float* __restrict__ dzt, int rows,
+                                                      int Lp, int Nr, uint16_t* __restrict__ dzt16,
+                                                      float* __restrict__ drb,
+                                                      float* __restrict__ dcb) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = lane();
+  if (r >= rows) return;
+  const float4* src = reinterpret_cast<const float4*>(dzt + static_cast<size_t>(r) * Lp);
+  uint2* dst = dzt16 ? reinterpret_cast<uint2*>(dzt16 + static_cast<size_t>(r) * Lp) : nullptr;
+  const int n4 = Lp >> 2;
+  float sum = 0.f;
+  for (int b = 0; b < n4; b += 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = b + u * 64 + l;
+      v[u] = i < n4 ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = b + u * 64 + l;
+      sum += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+      if (dst && i < n4) dst[i] = make_uint2(bf16_rne2(v[u].x, v[u].y), bf16_rne2(v[u].z, v[u].w));
+    }
+  }
+  sum = wave_sum(sum);
+  if (l == 0) {
+    if (r < Nr) {
+      if (drb) drb[r] = sum;
+    } else if (dcb) {
+      dcb[r - Nr] = sum;
+    }
+  }
+}
+
+// out[c][t] = in[t][c] for t < L, 0 for L <= t < Lp (in [L, d], out [d, Lp]),
+// through a 64 x 64 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict__ in, int L, int d,
+                                                            int Lp, T* __restrict__ out) {
+  __shared__ T tile[64][65];
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 64; i += 4) {
+    const int t = t0 + ty + i, c = c0 + tx;
+    tile[ty + i][tx] = (t < L && c < d) ? in[static_cast<size_t>(t) * d + c] : T(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 64; i += 4) {
+    const int c = c0 + ty + i, t = t0 + tx;
+    if (c < d && t < Lp) out[static_cast<size_t>(c) * Lp + t] = tile[tx][ty + i];
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_f32x4_kernel(float4* __restrict__ p, size_t n4) {
@@ -214,77 +285,92 @@ __device__ __forceinline__ int out_row_of(const int32_t* __restrict__ te,
   return static_cast<unsigned>(r) < static_cast<unsigned>(n_rows) ? r : 0;
 }
 
-// Wave w: sorted tasks [64 w, 64 w + 64).  out[row] = sum w_m src[token];
-// osum[row] = sum w_m (if osum).  Partials of rows crossing a chunk edge go
-// to part[(2 w + slot) * d]: slot 0 if the row began before the chunk, else
-// slot 1 (the row begins here and continues).
-template <typename S, int EPL>
+// Wave w of column block y: sorted tasks [64 w, 64 w + 64) and columns
+// [64 EPL y, 64 EPL (y + 1)).  dV[row] = sum_m c_m dy[token_m] and
+// dW[row] = sum_m dh_m x[token_m] over the tasks m of the row's expert, both
+// from one walk of the task list.  Partials of rows crossing a chunk edge go
+// to part[((2 w + slot) * 2 + o) * d] (o = 0 for dV, 1 for dW): slot 0 if the
+// row began before the chunk, else slot 1 (the row begins here and continues).
+template <typename T, int EPL>
 __global__ __launch_bounds__(256) void seg_reduce_kernel(
     const int32_t* __restrict__ task_token, const int32_t* __restrict__ task_expert,
     const int32_t* __restrict__ task_index, const int32_t* __restrict__ rank,
-    const float* __restrict__ wflat, const S* __restrict__ src, int M, int d, int L,
-    int n_ids, int n_rows, float* __restrict__ out, float* __restrict__ osum, float* __restrict__ part,
-    float* __restrict__ psum) {
+    const float* __restrict__ coef, const float* __restrict__ dh, const float* __restrict__ dy,
+    const T* __restrict__ x, int M, int d, int L, int n_ids, int n_rows, float* __restrict__ dv,
+    float* __restrict__ dw, float* __restrict__ part) {
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
   const int p0 = wv * 64;
   if (p0 >= M) return;
+  const int col0 = blockIdx.y * 64 * EPL;
   const int n = min(64, M - p0);
   int my_t = 0, my_r = 0;
-  float my_w = 0.f;
+  float my_c = 0.f, my_h = 0.f;
   if (l < n) {
     const int p = p0 + l;
     const int t = task_token[p];
     my_t = static_cast<unsigned>(t) < static_cast<unsigned>(L) ? t : 0;
     my_r = out_row_of(task_expert, rank, p, n_ids, n_rows);
     const int m = task_index[p];
-    my_w = static_cast<unsigned>(m) < static_cast<unsigned>(M) ? wflat[m] : 0.f;
+    const bool ok = static_cast<unsigned>(m) < static_cast<unsigned>(M);
+    my_c = ok ? coef[m] : 0.f;
+    my_h = ok ? dh[m] : 0.f;
   }
   // does the first row begin before this chunk / the last row continue after it?
   const bool head = p0 > 0 && out_row_of(task_expert, rank, p0 - 1, n_ids, n_rows) == rdlane(my_r, 0);
   const bool tail = p0 + n < M && out_row_of(task_expert, rank, p0 + n, n_ids, n_rows) == rdlane(my_r, n - 1);
   constexpr int R = kBwdRing;
-  using SF = RowFrag<S, EPL>;
-  SF f[R];
-  float acc[EPL];
+  RowFrag<float, EPL> fy[R];
+  RowFrag<T, EPL> fx[R];
+  const float* dyc = dy + col0;
+  const T* xc = x + col0;
+  float av[EPL], aw[EPL];
 #pragma unroll
-  for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
-  float wsum = 0.f;
+  for (int q = 0; q < EPL; ++q) av[q] = aw[q] = 0.f;
   int seg_start = 0;
 #pragma unroll
-  for (int s = 0; s < R - 1; ++s)
-    if (s < n) f[s].load(src + static_cast<size_t>(rdlane(my_t, s)) * d, l);
+  for (int s = 0; s < R - 1; ++s) {
+    if (s < n) {
+      const size_t o = static_cast<size_t>(rdlane(my_t, s)) * d;
+      fy[s].load(dyc + o, l);
+      fx[s].load(xc + o, l);
+    }
+  }
   for (int i = 0; i < n; i += R) {
 #pragma unroll
     for (int s = 0; s < R; ++s) {
       const int k = i + s;
       if (k >= n) break;
-      if (k + R - 1 < n)
-        f[(s + R - 1) % R].load(src + static_cast<size_t>(rdlane(my_t, k + R - 1)) * d, l);
-      const float wk = rdlane(my_w, k);
+      if (k + R - 1 < n) {
+        const size_t o = static_cast<size_t>(rdlane(my_t, k + R - 1)) * d;
+        fy[(s + R - 1) % R].load(dyc + o, l);
+        fx[(s + R - 1) % R].load(xc + o, l);
+      }
+      const float ck = rdlane(my_c, k), hk = rdlane(my_h, k);
 #pragma unroll
-      for (int q = 0; q < EPL; ++q) acc[q] = fmaf(wk, f[s].get(q), acc[q]);
-      wsum += wk;
+      for (int q = 0; q < EPL; ++q) {
+        av[q] = fmaf(ck, fy[s].get(q), av[q]);
+        aw[q] = fmaf(hk, fx[s].get(q), aw[q]);
+      }
       const int row = rdlane(my_r, k);
       const bool last_of_row = k == n - 1 || rdlane(my_r, k + 1) != row;
       if (last_of_row) {
         const bool began_before = seg_start == 0 && head;
         const bool goes_on = k == n - 1 && tail;
-        float* dst;
-        float* dsum;
+        float* dst_v;
+        float* dst_w;
         if (!began_before && !goes_on) {
-          dst = out + static_cast<size_t>(row) * d;
-          dsum = osum ? osum + row : nullptr;
+          dst_v = dv + static_cast<size_t>(row) * d + col0;
+          dst_w = dw + static_cast<size_t>(row) * d + col0;
         } else {
           const int slot = began_before ? 0 : 1;
-          dst = part + static_cast<size_t>(2 * wv + slot) * d;
-          dsum = psum + 2 * wv + slot;
+          dst_v = part + static_cast<size_t>((2 * wv + slot) * 2) * d + col0;
+          dst_w = dst_v + d;
         }
-        store_row<S, EPL>(acc, dst, 0);
-        if (l == 0 && dsum) *dsum = wsum;
+        store_row<float, EPL>(av, dst_v, 0);
+        store_row<T, EPL>(aw, dst_w, 0);
 #pragma unroll
-        for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
-        wsum = 0.f;
+        for (int q = 0; q < EPL; ++q) av[q] = aw[q] = 0.f;
         seg_start = k + 1;
       }
     }
@@ -292,14 +378,13 @@ __global__ __launch_bounds__(256) void seg_reduce_kernel(
 }
 
 // Rows that cross chunk edges: the wave of the chunk where such a row begins
-// (its slot-1 partial) adds the slot-0 partials of the following chunks, in
-// order, for as long as the row continues.  S fixes the element layout of the
-// partial rows (that of the reduction that wrote them).
-template <typename S, int EPL>
+// (its slot-1 partials) adds the slot-0 partials of the following chunks, in
+// order, for as long as the row continues.
+template <typename T, int EPL>
 __global__ __launch_bounds__(256) void seg_fixup_kernel(
     const int32_t* __restrict__ task_expert, const int32_t* __restrict__ rank, int M, int d,
-    int n_ids, int n_rows, float* __restrict__ out, float* __restrict__ osum,
-    const float* __restrict__ part, const float* __restrict__ psum) {
+    int n_ids, int n_rows, float* __restrict__ dv, float* __restrict__ dw,
+    const float* __restrict__ part) {
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
   const int p0 = wv * 64;
@@ -313,20 +398,24 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(
   if (out_row_of(task_expert, rank, p0, n_ids, n_rows) == row && p0 > 0 &&
       out_row_of(task_expert, rank, p0 - 1, n_ids, n_rows) == row)
     return;
-  float acc[EPL];
-  float tot[EPL];
-  load_f32_as<S, EPL>(part + static_cast<size_t>(2 * wv + 1) * d, l, tot);
-  float ws = psum[2 * wv + 1];
+  const int col0 = blockIdx.y * 64 * EPL;
+  float tv[EPL], tw[EPL], a[EPL];
+  const float* own = part + static_cast<size_t>((2 * wv + 1) * 2) * d + col0;
+  load_f32_as<float, EPL>(own, l, tv);
+  load_f32_as<T, EPL>(own + d, l, tw);
   for (int c = wv + 1;; ++c) {
-    load_f32_as<S, EPL>(part + static_cast<size_t>(2 * c) * d, l, acc);
+    const float* pc = part + static_cast<size_t>(2 * c * 2) * d + col0;
+    load_f32_as<float, EPL>(pc, l, a);
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) tot[q] += acc[q];
-    ws += psum[2 * c];
+    for (int q = 0; q < EPL; ++q) tv[q] += a[q];
+    load_f32_as<T, EPL>(pc + d, l, a);
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) tw[q] += a[q];
     const int ce = min((c + 1) * 64, M);
     if (ce >= M || out_row_of(task_expert, rank, ce, n_ids, n_rows) != row) break;
   }
-  store_row<S, EPL>(tot, out + static_cast<size_t>(row) * d, 0);
-  if (l == 0 && osum) osum[row] = ws;
+  store_row<float, EPL>(tv, dv + static_cast<size_t>(row) * d + col0, 0);
+  store_row<T, EPL>(tw, dw + static_cast<size_t>(row) * d + col0, 0);
 }
 
 // ------------------------------------------------------------ host side
@@ -358,104 +447,98 @@ static SchedBufs sched_bufs(size_t& o, int L, int K, int N) {
 
 namespace {
 struct BwdLayout {
-  size_t bytes, coef, dh, ds, ri, ci, part, psum;
-  SchedBufs es, rs, cs;  // experts (the caller's counts / active), grid rows, grid columns
+  size_t bytes, coef, dh, ds, part, dzt, dzt16, xt, cgrad;
+  int Lp;        // tokens padded to a multiple of 64 (the GEMM's inner dimension)
+  SchedBufs es;  // experts, groups of one (the caller's counts / active)
 };
 }  // namespace
 
-static BwdLayout bwd_layout(int L, int d, int Nr, int Nc, int K) {
+static BwdLayout bwd_layout(int L, int d, int Nr, int Nc, int K, int bf16) {
   BwdLayout w{};
   const size_t M = static_cast<size_t>(L) * K;
   const size_t m1 = M > 0 ? M : 1;
+  const size_t es = bf16 ? 2 : 4;
+  w.Lp = ((L > 0 ? L : 1) + 63) / 64 * 64;
+  const size_t nrc = static_cast<size_t>(Nr) + Nc;
   size_t o = 0;
-  w.coef = o; o = a256(o + m1 * 4);
-  w.dh = o;   o = a256(o + m1 * 4);
-  w.ds = o;   o = a256(o + m1 * 4);
-  w.ri = o;   o = a256(o + m1 * 4);
-  w.ci = o;   o = a256(o + m1 * 4);
+  w.coef = o;  o = a256(o + m1 * 4);
+  w.dh = o;    o = a256(o + m1 * 4);
+  w.ds = o;    o = a256(o + m1 * 4);
   const size_t chunks = (m1 + 63) / 64;
-  w.part = o; o = a256(o + chunks * 2 * static_cast<size_t>(d) * 4);
-  w.psum = o; o = a256(o + chunks * 2 * 4);
+  w.part = o;  o = a256(o + chunks * 4 * static_cast<size_t>(d) * 4);
+  w.dzt = o;   o = a256(o + nrc * w.Lp * 4);
+  w.dzt16 = o; o = a256(o + (bf16 ? nrc * w.Lp * 2 : 0));
+  w.xt = o;    o = a256(o + static_cast<size_t>(d) * w.Lp * es);
+  w.cgrad = o; o = a256(o + nrc * static_cast<size_t>(d) * 4);
   const long long N = static_cast<long long>(Nr) * Nc;
   w.es = sched_bufs(o, L, K, static_cast<int>(N));
-  w.rs = sched_bufs(o, L, K, Nr);
-  w.cs = sched_bufs(o, L, K, Nc);
   w.bytes = o;
   return w;
 }
 
-size_t routed_backward_ws_bytes(int L, int d, int Nr, int Nc, int K) {
-  return bwd_layout(L, d, Nr, Nc, K).bytes;
+size_t routed_backward_ws_bytes(int bf16, int L, int d, int Nr, int Nc, int K) {
+  return bwd_layout(L, d, Nr, Nc, K, bf16).bytes;
 }
 
 template <typename T, int EPL>
 static hipError_t launch_bwd_t(const T* x, const T* wr, const T* wc, const T* w, const T* v,
-                         const int32_t* expert_idx, const float* gate, const float* dy,
-                         float* dx, float* dwr, float* dwc, float* drb, float* dcb,
-                         int32_t* counts, int32_t* active, float* dw, float* dv, float* dgate,
-                         int L, int d, int Nr, int Nc, int K, char* ws, const BwdLayout& lay,
-                         hipStream_t s) {
+                               const int32_t* expert_idx, const float* gate, const float* dy,
+                               float* dx, float* dwr, float* dwc, float* drb, float* dcb,
+                               int32_t* counts, int32_t* active, float* dw, float* dv,
+                               float* dgate, int L, int d, int Nr, int Nc, int K, char* ws,
+                               const BwdLayout& lay, hipStream_t s) {
+  constexpr int bf16 = sizeof(T) == 2;
   const int N = Nr * Nc;
   const int M = L * K;
+  const int NRC = Nr + Nc, Lp = lay.Lp;
   float* coef = reinterpret_cast<float*>(ws + lay.coef);
   float* dh = reinterpret_cast<float*>(ws + lay.dh);
   float* ds = reinterpret_cast<float*>(ws + lay.ds);
-  int32_t* ri = reinterpret_cast<int32_t*>(ws + lay.ri);
-  int32_t* ci = reinterpret_cast<int32_t*>(ws + lay.ci);
   float* part = reinterpret_cast<float*>(ws + lay.part);
-  float* psum = reinterpret_cast<float*>(ws + lay.psum);
-  // dense router gradients: rows no task touches stay zero
-  const size_t nr4 = static_cast<size_t>(Nr) * d / 4, nc4 = static_cast<size_t>(Nc) * d / 4;
-  zero_f32x4_kernel<<<static_cast<unsigned>((nr4 + 255) / 256), 256, 0, s>>>(
-      reinterpret_cast<float4*>(dwr), nr4);
-  zero_f32x4_kernel<<<static_cast<unsigned>((nc4 + 255) / 256), 256, 0, s>>>(
-      reinterpret_cast<float4*>(dwc), nc4);
-  if (drb) zero_f32_kernel1<<<(Nr + 255) / 256, 256, 0, s>>>(drb, Nr);
-  if (dcb) zero_f32_kernel1<<<(Nc + 255) / 256, 256, 0, s>>>(dcb, Nc);
+  float* dzt = reinterpret_cast<float*>(ws + lay.dzt);
+  uint16_t* dzt16 = bf16 ? reinterpret_cast<uint16_t*>(ws + lay.dzt16) : nullptr;
+  T* xt = reinterpret_cast<T*>(ws + lay.xt);
+  float* cgrad = reinterpret_cast<float*>(ws + lay.cgrad);
+  // transposed logit gradients start at zero (a token writes only its rows)
+  const size_t nz4 = static_cast<size_t>(NRC) * Lp / 4;
+  zero_f32x4_kernel<<<static_cast<unsigned>((nz4 + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<float4*>(dzt), nz4);
   if (L > 0)
     bwd_token_kernel<T, EPL><<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(
-        x, w, v, wr, wc, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate);
-  if (M > 0)
-    split_ids_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(expert_idx, M, N, Nc,
-                                                                           ri, ci);
+        x, w, v, wr, wc, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate, dzt,
+        Lp);
+  // router weights: [dWr; dWc] = dz^T x, one MFMA product over the padded tokens
+  dz_rows_kernel<<<static_cast<unsigned>((NRC + 3) / 4), 256, 0, s>>>(dzt, NRC, Lp, Nr, dzt16,
+                                                                     drb, dcb);
+  transpose_pad_kernel<T><<<dim3(static_cast<unsigned>(Lp / 64),
+                                 static_cast<unsigned>((d + 63) / 64)), 256, 0, s>>>(x, L, d, Lp,
+                                                                                      xt);
+  hipError_t e = launch_gemm_nt(bf16, bf16 ? static_cast<const void*>(dzt16)
+                                           : static_cast<const void*>(dzt),
+                                xt, cgrad, NRC, d, Lp, s);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(dwr, cgrad, static_cast<size_t>(Nr) * d * 4, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(dwc, cgrad + static_cast<size_t>(Nr) * d, static_cast<size_t>(Nc) * d * 4,
+                     hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  // expert weights: dV[i] = sum c dy_t, dW[i] = sum dh x_t over the tasks of
+  // active expert i, from the expert-major task list
   auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  // expert-major, grid-row-major and grid-column-major task lists
-  hipError_t e = launch_schedule(L, K, N, 1, expert_idx, gate, counts, active, I(lay.es.off),
-                                 I(lay.es.tok), I(lay.es.exp), F(lay.es.gat), I(lay.es.idx),
-                                 ws + lay.es.ws, s);
-  if (e != hipSuccess) return e;
-  e = launch_schedule(L, K, Nr, 1, ri, gate, I(lay.rs.cnt), I(lay.rs.act), I(lay.rs.off),
-                      I(lay.rs.tok), I(lay.rs.exp), F(lay.rs.gat), I(lay.rs.idx), ws + lay.rs.ws, s);
-  if (e != hipSuccess) return e;
-  e = launch_schedule(L, K, Nc, 1, ci, gate, I(lay.cs.cnt), I(lay.cs.act), I(lay.cs.off),
-                      I(lay.cs.tok), I(lay.cs.exp), F(lay.cs.gat), I(lay.cs.idx), ws + lay.cs.ws, s);
+  e = launch_schedule(L, K, N, 1, expert_idx, gate, counts, active, I(lay.es.off), I(lay.es.tok),
+                      I(lay.es.exp), F(lay.es.gat), I(lay.es.idx), ws + lay.es.ws, s);
   if (e != hipSuccess) return e;
   if (M == 0) return hipGetLastError();
-  const unsigned nblk = static_cast<unsigned>((M + 255) / 256);  // 4 chunks of 64 per block
+  // columns in blocks of 64 * RE: more, smaller waves than one per whole row
+  constexpr int RE = EPL < kSegEpl ? EPL : kSegEpl;
+  const dim3 grid(static_cast<unsigned>((M + 255) / 256), EPL / RE);  // 4 chunks of 64 per block
   const int32_t* rank = I(lay.es.ws + lay.es.lay.rank);
   const int n_exp = lay.es.lay.max_groups;
-  // dV[i] = sum c dy_t, dW[i] = sum dh x_t over the tasks of active expert i
-  seg_reduce_kernel<float, EPL><<<nblk, 256, 0, s>>>(I(lay.es.tok), I(lay.es.exp), I(lay.es.idx),
-                                                     rank, coef, dy, M, d, L, N, n_exp, dv,
-                                                     nullptr, part, psum);
-  seg_fixup_kernel<float, EPL><<<nblk, 256, 0, s>>>(I(lay.es.exp), rank, M, d, N, n_exp, dv, nullptr,
-                                                    part, psum);
-  seg_reduce_kernel<T, EPL><<<nblk, 256, 0, s>>>(I(lay.es.tok), I(lay.es.exp), I(lay.es.idx), rank,
-                                                 dh, x, M, d, L, N, n_exp, dw, nullptr, part, psum);
-  seg_fixup_kernel<T, EPL><<<nblk, 256, 0, s>>>(I(lay.es.exp), rank, M, d, N, n_exp, dw, nullptr,
-                                                part, psum);
-  // dWr[i] = sum dS x_t over the tasks whose expert lies in grid row i; columns alike
-  seg_reduce_kernel<T, EPL><<<nblk, 256, 0, s>>>(I(lay.rs.tok), I(lay.rs.exp), I(lay.rs.idx),
-                                                 nullptr, ds, x, M, d, L, Nr, Nr, dwr, drb, part,
-                                                 psum);
-  seg_fixup_kernel<T, EPL><<<nblk, 256, 0, s>>>(I(lay.rs.exp), nullptr, M, d, Nr, Nr, dwr, drb, part,
-                                                psum);
-  seg_reduce_kernel<T, EPL><<<nblk, 256, 0, s>>>(I(lay.cs.tok), I(lay.cs.exp), I(lay.cs.idx),
-                                                 nullptr, ds, x, M, d, L, Nc, Nc, dwc, dcb, part,
-                                                 psum);
-  seg_fixup_kernel<T, EPL><<<nblk, 256, 0, s>>>(I(lay.cs.exp), nullptr, M, d, Nc, Nc, dwc, dcb, part,
-                                                psum);
+  seg_reduce_kernel<T, RE><<<grid, 256, 0, s>>>(I(lay.es.tok), I(lay.es.exp), I(lay.es.idx), rank,
+                                                coef, dh, dy, x, M, d, L, N, n_exp, dv, dw, part);
+  seg_fixup_kernel<T, RE><<<grid, 256, 0, s>>>(I(lay.es.exp), rank, M, d, N, n_exp, dv, dw, part);
+  (void)ds;
   return hipGetLastError();
 }
 
@@ -470,7 +553,7 @@ hipError_t launch_routed_backward(int bf16, int L, int d, int Nr, int Nc, int K,
                                   float* dx, float* dwr, float* dwc, float* drb, float* dcb,
                                   int32_t* counts, int32_t* active, float* dw, float* dv,
                                   float* dgate, void* ws, hipStream_t s) {
-  const BwdLayout lay = bwd_layout(L, d, Nr, Nc, K);
+  const BwdLayout lay = bwd_layout(L, d, Nr, Nc, K, bf16);
   char* base = static_cast<char*>(ws);
 #define OMNI_BWD(T_, D_, EPL_)                                                                  \
   case D_:                                                                                     \

@@ -14,6 +14,8 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
 hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
                              const float* rb, const float* cb, float* zr, float* zc,
                              int L, int d, int Nr, int Nc, hipStream_t s);
+hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
+                          hipStream_t s);
 
 // topk.hip
 hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, int Nc, int kp,
@@ -45,7 +47,7 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
                                  hipStream_t s);
 
 // backward.hip
-size_t routed_backward_ws_bytes(int L, int d, int Nr, int Nc, int K);
+size_t routed_backward_ws_bytes(int bf16, int L, int d, int Nr, int Nc, int K);
 bool routed_backward_supported(int bf16, int d, int K);
 hipError_t launch_routed_backward(int bf16, int L, int d, int Nr, int Nc, int K, const void* x,
                                   const void* wr, const void* wc, const void* w, const void* v,

@@ -347,4 +347,24 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc, c
   return hipGetLastError();
 }
 
+// C[m][n] = sum_k A[m][k] B[n][k] (A [M, K], B [N, K], C [M, N] float32, all
+// row-major): the 128 x 128 MFMA kernel (bf16, K a multiple of 8) or the
+// float32 kernel, used as plain products by the backward pass.
+hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
+                          hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (bf16) {
+    const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
+    router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(
+        static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+        static_cast<const uint16_t*>(b), nullptr, nullptr, c, c, M, K, N, 0, n_mt, n_nt);
+  } else {
+    const size_t n = static_cast<size_t>(M) * N;
+    router_gemm_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+        static_cast<const float*>(a), static_cast<const float*>(b), static_cast<const float*>(b),
+        nullptr, nullptr, c, c, M, K, N, 0);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace omni
