@@ -9,16 +9,16 @@
 //   dx_t += dz_r Wr + dz_c Wc,  dWr = dz_r^T x,  dWc = dz_c^T x, bias = column sums
 // The log-softmax backward dz = da - softmax(z) sum(da) reduces to dz = da
 // because sum_k dS_k = 0 exactly: the logit gradient is nonzero only on the
-// rows and columns of the selected experts.  Its part of dx is then a gather
-// of 2K router rows per token; dWr and dWc are one MFMA product
-// [dWr; dWc] = dz^T x over all tokens.
+// rows and columns of the selected experts.  Both router products are dense
+// MFMA GEMMs over that mostly-zero dz: dx += dz [Wr; Wc] and
+// [dWr; dWc] = dz^T x (dense beats gathering 2K router rows per token: the
+// two tables together outgrow one XCD's L2).
 //
 // Two kinds of kernels:
 //   bwd_token_kernel: one wave per token (x_t and dy_t in registers) walks the
-//     token's V rows (u_k), W rows (h_k -> dh_k, dg_k, c_k; dx += dh_k W[e])
-//     and router rows (dx += dS_k (Wr[i_k] + Wc[j_k])); writes dx_t, the
-//     per-task c, dh, dS, dg at the flat task id, and the token's column of
-//     the transposed logit gradient dz^T.
+//     token's V rows (u_k) and W rows (h_k -> dh_k, dg_k, c_k; dx += dh_k W[e]);
+//     writes dx_t, the per-task c, dh, dS, dg at the flat task id, and the
+//     token's row of dz and column of dz^T.
 //   seg_reduce_kernel + seg_fixup_kernel: dV[row] = sum c dy[token] and
 //     dW[row] = sum dh x[token] over the expert-major task list, a schedule
 //     with groups of one (B = 1) built by the forward's scheduling code.  Each wave
@@ -56,16 +56,25 @@ __device__ __forceinline__ void load_f32_as(const float* __restrict__ row, int l
   }
 }
 
+// float32 -> element type: bf16 by round to nearest even (finite values)
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 constexpr int kBwdRing = 4;  // row slots per wave: three in flight
 constexpr int kSegEpl = 16;  // row elements per lane in the dV / dW reduction
 
 template <typename T, int EPL>
 __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ V,
-    const T* __restrict__ wr, const T* __restrict__ wc, const int32_t* __restrict__ expert_idx,
+    const int32_t* __restrict__ expert_idx,
     const float* __restrict__ gate, const float* __restrict__ dy, int L, int K, int d, int N,
     int Nr, int Nc, float* __restrict__ dx, float* __restrict__ coef, float* __restrict__ dh_out,
-    float* __restrict__ ds_out, float* __restrict__ dgate, float* __restrict__ dzt, int Lp) {
+    float* __restrict__ ds_out, float* __restrict__ dgate, float* __restrict__ dzt, int Lp,
+    T* __restrict__ dz, int ldz) {
   using Frag = RowFrag<T, EPL>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
@@ -140,38 +149,12 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
   const float gdg = wave_sum(l < K ? my_g * my_dg : 0.f);
   const float my_ds = my_g * (my_dg - gdg);
 
-  // pass 3: dx += dS_k (Wr[i_k] + Wc[j_k]); rows 2k (Wr) and 2k+1 (Wc)
-  const int n2 = 2 * K;
   const int my_ri = my_e / Nc, my_ci = my_e - (my_e / Nc) * Nc;
-#pragma unroll
-  for (int s = 0; s < kBwdRing - 1; ++s) {
-    if (s < n2) {
-      const int k = s >> 1;
-      f[s].load((s & 1) ? wc + static_cast<size_t>(rdlane(my_ci, k)) * d
-                        : wr + static_cast<size_t>(rdlane(my_ri, k)) * d, l);
-    }
-  }
-  for (int i = 0; i < n2; i += kBwdRing) {
-#pragma unroll
-    for (int s = 0; s < kBwdRing; ++s) {
-      const int q2 = i + s;
-      if (q2 >= n2) break;
-      const int qn = q2 + kBwdRing - 1;
-      if (qn < n2) {
-        const int k = qn >> 1;
-        f[(s + kBwdRing - 1) % kBwdRing].load(
-            (qn & 1) ? wc + static_cast<size_t>(rdlane(my_ci, k)) * d
-                     : wr + static_cast<size_t>(rdlane(my_ri, k)) * d, l);
-      }
-      const float ds = rdlane(my_ds, q2 >> 1);
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) acc[q] = fmaf(ds, f[s].get(q), acc[q]);
-    }
-  }
   store_row<T, EPL>(acc, dx + static_cast<size_t>(t) * d, 0);
-  // this token's column of the transposed logit gradients: dz_r[t, i] is the
-  // sum of dS over the token's tasks in grid row i (summed in task order, and
-  // stored by the first such task), dz_c likewise at row Nr + j
+  // the token's logit gradients: dz_r[t, i] is the sum of dS over the token's
+  // tasks in grid row i (summed in task order, stored by the first such task),
+  // dz_c likewise; written to row t of dz (grid rows, then grid columns, for
+  // the dx product) and to column t of dz^T (for the dWr, dWc product)
   float rsum = 0.f, csum = 0.f;
   bool rfirst = true, cfirst = true;
   for (int j = 0; j < K; ++j) {
@@ -190,8 +173,15 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
     dh_out[tb + l] = my_dh;
     ds_out[tb + l] = my_ds;
     if (dgate) dgate[tb + l] = my_dg;
-    if (rfirst) dzt[static_cast<size_t>(my_ri) * Lp + t] = rsum;
-    if (cfirst) dzt[static_cast<size_t>(Nr + my_ci) * Lp + t] = csum;
+    T* dzrow = dz + static_cast<size_t>(t) * ldz;
+    if (rfirst) {
+      dzt[static_cast<size_t>(my_ri) * Lp + t] = rsum;
+      dzrow[my_ri] = from_f32<T>(rsum);
+    }
+    if (cfirst) {
+      dzt[static_cast<size_t>(Nr + my_ci) * Lp + t] = csum;
+      dzrow[Nr + my_ci] = from_f32<T>(csum);
+    }
   }
 }
 
@@ -240,24 +230,32 @@ __global__ __launch_bounds__(256) void dz_rows_kernel(const float* __restrict__ 
   }
 }
 
-// out[c][t] = in[t][c] for t < L, 0 for L <= t < Lp (in [L, d], out [d, Lp]),
-// through a 64 x 64 LDS tile.
+// Transpose with zero padding of two stacked row blocks: the input rows are
+// in0 [R0, d] followed by in1 [R1, d]; out[c][r] = row r, column c for
+// r < R0 + R1 and 0 for R0 + R1 <= r < Lp (out [d, Lp]), through a 64 x 64
+// LDS tile.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict__ in, int L, int d,
-                                                            int Lp, T* __restrict__ out) {
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict__ in0, int R0,
+                                                            const T* __restrict__ in1, int R1,
+                                                            int d, int Lp, T* __restrict__ out) {
   __shared__ T tile[64][65];
   const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 64; i += 4) {
-    const int t = t0 + ty + i, c = c0 + tx;
-    tile[ty + i][tx] = (t < L && c < d) ? in[static_cast<size_t>(t) * d + c] : T(0);
+    const int r = t0 + ty + i, c = c0 + tx;
+    T v = T(0);
+    if (c < d) {
+      if (r < R0) v = in0[static_cast<size_t>(r) * d + c];
+      else if (r < R0 + R1) v = in1[static_cast<size_t>(r - R0) * d + c];
+    }
+    tile[ty + i][tx] = v;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 64; i += 4) {
-    const int c = c0 + ty + i, t = t0 + tx;
-    if (c < d && t < Lp) out[static_cast<size_t>(c) * Lp + t] = tile[tx][ty + i];
+    const int c = c0 + ty + i, r = t0 + tx;
+    if (c < d && r < Lp) out[static_cast<size_t>(c) * Lp + r] = tile[tx][ty + i];
   }
 }
 
@@ -447,8 +445,9 @@ static SchedBufs sched_bufs(size_t& o, int L, int K, int N) {
 
 namespace {
 struct BwdLayout {
-  size_t bytes, coef, dh, ds, part, dzt, dzt16, xt, cgrad;
-  int Lp;        // tokens padded to a multiple of 64 (the GEMM's inner dimension)
+  size_t bytes, coef, dh, ds, part, dzt, dzt16, xt, cgrad, dz, wrct;
+  int Lp;        // tokens padded to a multiple of 64 (inner dimension of the dWr, dWc product)
+  int Rp;        // grid rows + columns padded to a multiple of 64 (that of the dx product)
   SchedBufs es;  // experts, groups of one (the caller's counts / active)
 };
 }  // namespace
@@ -470,6 +469,9 @@ static BwdLayout bwd_layout(int L, int d, int Nr, int Nc, int K, int bf16) {
   w.dzt16 = o; o = a256(o + (bf16 ? nrc * w.Lp * 2 : 0));
   w.xt = o;    o = a256(o + static_cast<size_t>(d) * w.Lp * es);
   w.cgrad = o; o = a256(o + nrc * static_cast<size_t>(d) * 4);
+  w.Rp = static_cast<int>((nrc + 63) / 64 * 64);
+  w.dz = o;    o = a256(o + static_cast<size_t>(L > 0 ? L : 1) * w.Rp * es);
+  w.wrct = o;  o = a256(o + static_cast<size_t>(d) * w.Rp * es);
   const long long N = static_cast<long long>(Nr) * Nc;
   w.es = sched_bufs(o, L, K, static_cast<int>(N));
   w.bytes = o;
@@ -499,23 +501,36 @@ static hipError_t launch_bwd_t(const T* x, const T* wr, const T* wc, const T* w,
   uint16_t* dzt16 = bf16 ? reinterpret_cast<uint16_t*>(ws + lay.dzt16) : nullptr;
   T* xt = reinterpret_cast<T*>(ws + lay.xt);
   float* cgrad = reinterpret_cast<float*>(ws + lay.cgrad);
-  // transposed logit gradients start at zero (a token writes only its rows)
+  T* dz = reinterpret_cast<T*>(ws + lay.dz);
+  T* wrct = reinterpret_cast<T*>(ws + lay.wrct);
+  const int Rp = lay.Rp;
+  // logit gradients start at zero (a token writes only its own rows / columns)
   const size_t nz4 = static_cast<size_t>(NRC) * Lp / 4;
   zero_f32x4_kernel<<<static_cast<unsigned>((nz4 + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<float4*>(dzt), nz4);
+  const size_t nzb = static_cast<size_t>(L) * Rp * sizeof(T) / 16;
+  if (nzb > 0)
+    zero_f32x4_kernel<<<static_cast<unsigned>((nzb + 255) / 256), 256, 0, s>>>(
+        reinterpret_cast<float4*>(dz), nzb);
+  // [Wr; Wc]^T, zero-padded to Rp columns: the right operand of the dx product
+  transpose_pad_kernel<T><<<dim3(static_cast<unsigned>(Rp / 64),
+                                 static_cast<unsigned>((d + 63) / 64)), 256, 0, s>>>(
+      wr, Nr, wc, Nc, d, Rp, wrct);
   if (L > 0)
     bwd_token_kernel<T, EPL><<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(
-        x, w, v, wr, wc, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate, dzt,
-        Lp);
+        x, w, v, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate, dzt, Lp, dz,
+        Rp);
+  // router part of dx: dx += [dz_r dz_c] [Wr; Wc], one MFMA product
+  hipError_t e = launch_gemm_nt(bf16, dz, wrct, dx, L, d, Rp, 1, s);
+  if (e != hipSuccess) return e;
   // router weights: [dWr; dWc] = dz^T x, one MFMA product over the padded tokens
   dz_rows_kernel<<<static_cast<unsigned>((NRC + 3) / 4), 256, 0, s>>>(dzt, NRC, Lp, Nr, dzt16,
                                                                      drb, dcb);
   transpose_pad_kernel<T><<<dim3(static_cast<unsigned>(Lp / 64),
-                                 static_cast<unsigned>((d + 63) / 64)), 256, 0, s>>>(x, L, d, Lp,
-                                                                                      xt);
-  hipError_t e = launch_gemm_nt(bf16, bf16 ? static_cast<const void*>(dzt16)
-                                           : static_cast<const void*>(dzt),
-                                xt, cgrad, NRC, d, Lp, s);
+                                 static_cast<unsigned>((d + 63) / 64)), 256, 0, s>>>(
+      x, L, nullptr, 0, d, Lp, xt);
+  e = launch_gemm_nt(bf16, bf16 ? static_cast<const void*>(dzt16) : static_cast<const void*>(dzt),
+                     xt, cgrad, NRC, d, Lp, 0, s);
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(dwr, cgrad, static_cast<size_t>(Nr) * d * 4, hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return e;

@@ -14,8 +14,10 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
 hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
                              const float* rb, const float* cb, float* zr, float* zc,
                              int L, int d, int Nr, int Nc, hipStream_t s);
+// c[M, N] (+)= a[M, K] b[N, K]^T, row-major, fp32 accumulation; a, b bf16
+// bits (bf16 != 0, K a multiple of 8) or float32 (K a multiple of 4).
 hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
-                          hipStream_t s);
+                          int accumulate, hipStream_t s);
 
 // topk.hip
 hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, int Nc, int kp,

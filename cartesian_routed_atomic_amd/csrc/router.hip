@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wc, const float* __restrict__ rb,
     const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
-    int L, int d, int Nr, int Nc, int n_mt, int n_nt) {
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[RBM * RLD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[RBN * RLD];
 
@@ -108,15 +108,24 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     if (n >= NT) continue;
     const bool is_row = n < Nr;
     const float bias = is_row ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f);
+    float* col = is_row ? zr + n : zc + (n - Nr);
+    const size_t ld = is_row ? Nr : Nc;
+    // accumulate: read this column's old values first, all loads in flight
+    float old[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + q;
+        old[i][q] = (acc_out && t < L) ? col[static_cast<size_t>(t) * ld] : 0.f;
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + q;
         if (t >= L) continue;
-        const float val = acc[i][j][q] + bias;
-        if (is_row) zr[static_cast<size_t>(t) * Nr + n] = val;
-        else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = val;
+        col[static_cast<size_t>(t) * ld] = acc[i][j][q] + bias + old[i][q];
       }
     }
   }
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wc, const float* __restrict__ rb,
     const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
-    int L, int d, int Nr, int Nc, int n_mt, int n_nt) {
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[GSTAGES * GSTAGE_BYTES];
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int nblk = n_mt * n_nt;
@@ -282,15 +291,24 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
     if (n >= NT) continue;
     const bool is_row = n < Nr;
     const float bias = is_row ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f);
+    float* col = is_row ? zr + n : zc + (n - Nr);
+    const size_t ld = is_row ? Nr : Nc;
+    // accumulate: read this column's old values first, all loads in flight
+    float old[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
+        old[i][q] = (acc_out && t < L) ? col[static_cast<size_t>(t) * ld] : 0.f;
+      }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
         if (t >= L) continue;
-        const float val = acc[i][j][q] + bias;
-        if (is_row) zr[static_cast<size_t>(t) * Nr + n] = val;
-        else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = val;
+        col[static_cast<size_t>(t) * ld] = acc[i][j][q] + bias + old[i][q];
       }
     }
   }
@@ -301,7 +319,7 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
 __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ wc,
     const float* __restrict__ rb, const float* __restrict__ cb, float* __restrict__ zr,
-    float* __restrict__ zc, int L, int d, int Nr, int Nc) {
+    float* __restrict__ zc, int L, int d, int Nr, int Nc, int acc_out) {
   const int NT = Nr + Nc;
   const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (id >= static_cast<size_t>(L) * NT) return;
@@ -317,8 +335,9 @@ __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
     s = fmaf(a.z, b.z, s);
     s = fmaf(a.w, b.w, s);
   }
-  if (n < Nr) zr[static_cast<size_t>(t) * Nr + n] = s + (rb ? rb[n] : 0.f);
-  else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = s + (cb ? cb[n - Nr] : 0.f);
+  float* out = n < Nr ? zr + static_cast<size_t>(t) * Nr + n
+                      : zc + static_cast<size_t>(t) * Nc + (n - Nr);
+  *out = s + (n < Nr ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f)) + (acc_out ? *out : 0.f);
 }
 
 hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
@@ -328,12 +347,12 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
   if (d % GBK == 0) {
     const int n_mt = (L + GBM - 1) / GBM, n_nt = (Nr + Nc + GBN - 1) / GBN;
     router_gemm_bf16_big_kernel<<<n_mt * n_nt, 512, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr,
-                                                            Nc, n_mt, n_nt);
+                                                            Nc, n_mt, n_nt, 0);
     return hipGetLastError();
   }
   const int n_mt = (L + RBM - 1) / RBM, n_nt = (Nr + Nc + RBN - 1) / RBN;
   router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc,
-                                                      n_mt, n_nt);
+                                                      n_mt, n_nt, 0);
   return hipGetLastError();
 }
 
@@ -343,7 +362,7 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc, c
   if (L == 0) return hipSuccess;
   const size_t n = static_cast<size_t>(L) * (Nr + Nc);
   router_gemm_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-      x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc);
+      x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc, 0);
   return hipGetLastError();
 }
 
@@ -351,18 +370,26 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc, c
 // row-major): the 128 x 128 MFMA kernel (bf16, K a multiple of 8) or the
 // float32 kernel, used as plain products by the backward pass.
 hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
-                          hipStream_t s) {
+                          int accumulate, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (bf16) {
-    const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
-    router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(
-        static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
-        static_cast<const uint16_t*>(b), nullptr, nullptr, c, c, M, K, N, 0, n_mt, n_nt);
+    const uint16_t* pa = static_cast<const uint16_t*>(a);
+    const uint16_t* pb = static_cast<const uint16_t*>(b);
+    const int big_tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+    if (K % GBK == 0 && big_tiles >= 192) {  // the large tile only where it still fills the chip
+      router_gemm_bf16_big_kernel<<<big_tiles, 512, 0, s>>>(
+          pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, (M + GBM - 1) / GBM,
+          (N + GBN - 1) / GBN, accumulate);
+    } else {
+      const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
+      router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(pa, pb, pb, nullptr, nullptr, c, c, M,
+                                                          K, N, 0, n_mt, n_nt, accumulate);
+    }
   } else {
     const size_t n = static_cast<size_t>(M) * N;
     router_gemm_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(a), static_cast<const float*>(b), static_cast<const float*>(b),
-        nullptr, nullptr, c, c, M, K, N, 0);
+        nullptr, nullptr, c, c, M, K, N, 0, accumulate);
   }
   return hipGetLastError();
 }
