@@ -22,6 +22,10 @@ Recipe (the same for every workload):
     wc_t for grid columns.
   * the skewed workload adds a Zipf-shaped bias -s * ln(i + 1) (s = 1.1) to
     the logits of row i and, identically, of column i.
+  * the shared dense MLP branch (gate, up, down projections; tensor ids
+    Wg = 5, Wu = 6, Wd = 7) has hidden width d_ff = 256 * ceil(8 d / 768)
+    (two thirds of 4 d, rounded up to a multiple of 256) unless a workload
+    fixes it; Wg, Wu [d_ff, d] ~ N(0, 1/d), Wd [d, d_ff] ~ N(0, 1/d_ff).
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TENSOR_IDS = {"x": 0, "wr": 1, "wc": 2, "w": 3, "v": 4}
+TENSOR_IDS = {"x": 0, "wr": 1, "wc": 2, "w": 3, "v": 4, "wg": 5, "wu": 6, "wd": 7}
 
 # rows per generation chunk; fixed so the bits never depend on thread count
 _CHUNK_ELEMS = 1 << 22
@@ -51,7 +55,12 @@ class Workload:
     B: int              # active experts per group
     dtype: str          # "f32" or "bf16"
     zipf_s: float = 0.0  # 0 = no bias; else bias[i] = -zipf_s * ln(i + 1)
+    dff: int = 0         # shared-MLP hidden width; 0 = 256 * ceil(8 d / 768)
     note: str = field(default="", compare=False)
+
+    @property
+    def d_ff(self) -> int:
+        return self.dff if self.dff else 256 * -(-8 * self.d // 768)
 
     @property
     def N(self) -> int:
@@ -142,14 +151,17 @@ def zipf_bias(n: int, s: float) -> np.ndarray:
 def make_inputs(wl: Workload, parts=("x", "wr", "wc", "w", "v"), threads=None) -> dict:
     """Generate the named tensors of a workload on the host (numpy).
 
-    Returns a dict with any of x [L,d], wr [Nr,d], wc [Nc,d], w [N,d], v [N,d]
-    (float32 or uint16 bf16 bits), plus row_bias / col_bias (float32 or None).
+    Returns a dict with any of x [L,d], wr [Nr,d], wc [Nc,d], w [N,d], v [N,d],
+    wg [d_ff,d], wu [d_ff,d], wd [d,d_ff] (float32 or uint16 bf16 bits), plus
+    row_bias / col_bias (float32 or None).
     """
     c = wl.index
     sd = 1.0 / math.sqrt(wl.d)
     shapes = {"x": (wl.L, wl.d), "wr": (wl.Nr, wl.d), "wc": (wl.Nc, wl.d),
-              "w": (wl.N, wl.d), "v": (wl.N, wl.d)}
-    scales = {"x": 1.0, "wr": sd, "wc": sd, "w": sd, "v": sd}
+              "w": (wl.N, wl.d), "v": (wl.N, wl.d),
+              "wg": (wl.d_ff, wl.d), "wu": (wl.d_ff, wl.d), "wd": (wl.d, wl.d_ff)}
+    scales = {"x": 1.0, "wr": sd, "wc": sd, "w": sd, "v": sd, "wg": sd, "wu": sd,
+              "wd": 1.0 / math.sqrt(wl.d_ff)}
     out = {}
     for p in parts:
         out[p] = normal(shapes[p], 1000 * c + TENSOR_IDS[p], scales[p], wl.dtype, threads)
@@ -162,7 +174,8 @@ def make_inputs(wl: Workload, parts=("x", "wr", "wc", "w", "v"), threads=None) -
     return out
 
 
-def custom(L, d, Nr, Nc, kprime, K, B, dtype="f32", zipf_s=0.0, index=100, name="custom"):
+def custom(L, d, Nr, Nc, kprime, K, B, dtype="f32", zipf_s=0.0, index=100, name="custom",
+           dff=0):
     """A workload of arbitrary shape (tests use it for ragged and edge cases)."""
     return Workload(name, index, L=L, d=d, Nr=Nr, Nc=Nc, kprime=kprime, K=K, B=B,
-                    dtype=dtype, zipf_s=zipf_s)
+                    dtype=dtype, zipf_s=zipf_s, dff=dff)
