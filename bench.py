@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed tokens/sec per atomic-expert layer at 1 GPU; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+FP32_TFLOPS = 157.3            # MI355X float32 vector peak
 EXEC_SRCS = [os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", f)
              for f in ("execute.hip", "rowfrag.hpp", "device.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
@@ -100,6 +101,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing omni_routed_backward on the same batch")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip timing the whole layer (shared dense MLP + routed branch)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the HIP-graph replay of the step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -267,6 +270,43 @@ def main():
         say(f"[bench] backward {bwd_ms:.3f} ms, {bwd['achieved']:.0f} GB/s "
             f"({100 * bwd['frac']:.1f}% of HBM), {bwd['tokens_per_s']:.0f} tokens/s")
 
+    layer = None
+    if not args.no_layer:
+        # the whole OmniMoE layer: the shared dense MLP writes y, then the routed
+        # step runs with its executor adding onto y (one stream)
+        mlp = {k: to_dev(a_) for k, a_ in make_inputs(wl, parts=("wg", "wu", "wd")).items()
+               if k in ("wg", "wu", "wd")}
+        d_ff = wl.d_ff
+        mlp_ws = torch.empty(max(1, B.lib().omni_shared_mlp_workspace(
+            1 if wl.dtype == "bf16" else 0, L, d_ff)), dtype=torch.uint8, device=dev)
+        y_layer = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
+
+        def shared():
+            B.shared_mlp(x, mlp["wg"], mlp["wu"], mlp["wd"], y=y_layer, workspace=mlp_ws)
+
+        def layer_step():
+            shared()
+            stage_router()
+            stage_topk()
+            stage_schedule()
+            B.atomic_forward(x, w, v, sched, y=y_layer, accumulate=True, workspace=exec_ws)
+
+        shared()
+        layer_step()
+        mlp_ms = ev_time(shared)
+        layer_ms = ev_time(layer_step)
+        mlp_flop = 6.0 * L * wl.d * d_ff
+        mlp_tflops = mlp_flop / (mlp_ms * 1e-3) / 1e12
+        mlp_peak = MFMA_BF16_TFLOPS if wl.dtype == "bf16" else FP32_TFLOPS
+        layer = {"ms": layer_ms, "tokens_per_s": L / (layer_ms * 1e-3), "d_ff": d_ff,
+                 "shared_mlp_ms": mlp_ms,
+                 "shared_mlp_mfma": {"achieved": mlp_tflops, "peak": mlp_peak,
+                                     "unit": "TFLOP/s", "frac": mlp_tflops / mlp_peak},
+                 "routed_over_layer": ms / layer_ms}
+        say(f"[bench] layer (shared MLP d_ff={d_ff} + routed) {layer_ms:.3f} ms, "
+            f"{layer['tokens_per_s']:.0f} tokens/s; shared MLP {mlp_ms:.3f} ms = "
+            f"{mlp_tflops:.0f} TFLOP/s; routed-only step / layer = {ms / layer_ms:.3f}")
+
     cpu = None
     if not args.no_cpu_baseline:
         say("[bench] timing the CPU oracle ...")
@@ -304,6 +344,7 @@ def main():
         "n_active": n_active,
         "expert_usage": n_active / wl.N,
         "backward": bwd,
+        "layer": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -26,7 +26,7 @@ EXPORTS = (
     "omni_product_topk_workspace", "omni_product_topk", "omni_schedule_max_groups",
     "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_mode",
     "omni_atomic_forward_workspace", "omni_atomic_forward", "omni_routed_backward_workspace",
-    "omni_routed_backward",
+    "omni_routed_backward", "omni_shared_mlp_workspace", "omni_shared_mlp",
 )
 
 
@@ -60,6 +60,8 @@ _SIGS = {
                                  ctypes.POINTER(ScheduleStruct), _vp, _i, _i, _vp, _sz, _vp]),
     "omni_routed_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "omni_routed_backward": (_i, [_i, _i, _i, _i, _i, _i] + [_vp] * 19 + [_sz, _vp]),
+    "omni_shared_mlp_workspace": (_sz, [_i, _i, _i]),
+    "omni_shared_mlp": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -288,6 +290,44 @@ def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, str
     N = wr_t.shape[0] * wc_t.shape[0]
     sched = schedule_tasks(sel["expert_idx"], sel["gate"], N, B, stream=stream)
     y = atomic_forward(x, w, v, sched, stream=stream, mode=mode)
+    return {"row_logits": zr, "col_logits": zc, **sel, "schedule": sched, "y": y}
+
+
+def shared_mlp(x, w_gate, w_up, w_down, y=None, accumulate=False, workspace=None, stream=None):
+    """omni_shared_mlp: y [L, d] float32 = (or +=, if accumulate) the shared dense
+    MLP branch Wd (silu(Wg x) * (Wu x)); w_gate, w_up [d_ff, d], w_down [d, d_ff]."""
+    L, d = x.shape
+    d_ff = w_gate.shape[0]
+    _req(x, "x")
+    _req(w_gate, "w_gate", x.dtype, (d_ff, d))
+    _req(w_up, "w_up", x.dtype, (d_ff, d))
+    _req(w_down, "w_down", x.dtype, (d, d_ff))
+    if y is None:
+        y = torch.empty((L, d), dtype=torch.float32, device=x.device)
+    _req(y, "y", torch.float32, (L, d))
+    code = _dtype_code(x)
+    nws = lib().omni_shared_mlp_workspace(code, L, d_ff)
+    ws = workspace
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(max(1, nws), dtype=torch.uint8, device=x.device)
+    _check("omni_shared_mlp", lib().omni_shared_mlp(
+        code, L, d, d_ff, _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+        int(bool(accumulate)), _ptr(ws), nws, _stream(stream)))
+    return y
+
+
+def layer_forward(x, wr_t, wc_t, w, v, w_gate, w_up, w_down, kprime, K, B, row_bias=None,
+                  col_bias=None, stream=None, mode="auto"):
+    """The whole OmniMoE layer on one stream: the shared dense MLP writes y, then
+    the routed branch (router, product top-K, schedule) runs and its executor
+    adds the routed output onto y.  Returns every intermediate of the routed
+    branch and y."""
+    y = shared_mlp(x, w_gate, w_up, w_down, stream=stream)
+    zr, zc = router_logits(x, wr_t, wc_t, row_bias, col_bias, stream=stream)
+    sel = product_topk(zr, zc, kprime, K, stream=stream)
+    N = wr_t.shape[0] * wc_t.shape[0]
+    sched = schedule_tasks(sel["expert_idx"], sel["gate"], N, B, stream=stream)
+    atomic_forward(x, w, v, sched, y=y, accumulate=True, stream=stream, mode=mode)
     return {"row_logits": zr, "col_logits": zc, **sel, "schedule": sched, "y": y}
 
 

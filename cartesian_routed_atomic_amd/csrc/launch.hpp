@@ -18,6 +18,10 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
 // bits (bf16 != 0, K a multiple of 8) or float32 (K a multiple of 4).
 hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
                           int accumulate, hipStream_t s);
+// h[L, d_ff] = silu(x Wg^T) * (x Wu^T); x [L, d], wg / wu [d_ff, d]; h is bf16
+// bits (bf16 != 0, d a multiple of 8) or float32 (d a multiple of 4).
+hipError_t launch_swiglu_up(int bf16, const void* x, const void* wg, const void* wu, void* h,
+                            int L, int d, int d_ff, hipStream_t s);
 
 // topk.hip
 hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, int Nc, int kp,

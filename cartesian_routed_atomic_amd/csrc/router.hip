@@ -6,6 +6,10 @@
 // L x d x (Nr + Nc), so the bf16 path runs it on the gfx950 matrix cores
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  The per-axis log-softmax
 // is fused into the selection kernel, which reads each row once anyway.
+//
+// The same MFMA kernels serve the other dense products of the layer: the
+// backward's router products (launch_gemm_nt) and the shared dense MLP
+// (launch_swiglu_up with a fused SwiGLU epilogue, then launch_gemm_nt).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -19,11 +23,29 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // padded by 8 bf16 (16 bytes) to spread the 16-byte fragment reads over banks.
 constexpr int RBM = 128, RBN = 128, RBK = 64, RLD = RBK + 8;
 
+// Epilogues: grid-line logits (+ bias, or accumulated into the output), or
+// the SwiGLU hidden activation of the shared dense MLP.  In SwiGLU mode the
+// B operand is [Wg; Wu] seen through an interleave: logical columns come in
+// blocks of 16, even blocks are gate rows and odd blocks the up rows of the
+// same 16 hidden units, so one lane holds both halves of a hidden unit in
+// its tiles j and j + 1.
+constexpr int kEpiLogits = 0, kEpiSwiglu = 1;
+
+__device__ __forceinline__ int swiglu_hidden(int n) { return ((n >> 5) << 4) | (n & 15); }
+
+// silu(g) * u rounded to bf16 (nearest even; finite values)
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
+  const float v = g / (1.f + __expf(-g)) * u;
+  const uint32_t b = __float_as_uint(v);
+  return static_cast<uint16_t>((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+
+template <int EPI>
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wc, const float* __restrict__ rb,
     const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
-    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out) {
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out, uint16_t* __restrict__ hout) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[RBM * RLD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[RBN * RLD];
 
@@ -50,8 +72,13 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const int t = m0 + row;
     arow[i] = (t < L) ? x + static_cast<size_t>(t) * d : nullptr;
     const int n = n0 + row;
-    brow[i] = (n < Nr) ? wr + static_cast<size_t>(n) * d
-                       : ((n < NT) ? wc + static_cast<size_t>(n - Nr) * d : nullptr);
+    if constexpr (EPI == kEpiSwiglu) {
+      const int h = swiglu_hidden(n);
+      brow[i] = h < Nr ? ((n >> 4) & 1 ? wc : wr) + static_cast<size_t>(h) * d : nullptr;
+    } else {
+      brow[i] = (n < Nr) ? wr + static_cast<size_t>(n) * d
+                         : ((n < NT) ? wc + static_cast<size_t>(n - Nr) * d : nullptr);
+    }
   }
   uint4 ra[4], rbv[4];
   auto gload = [&](int k0) {
@@ -102,6 +129,25 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
 
   // Accumulator lane layout (16x16 output tile): column = lane % 16,
   // rows 4 * (lane / 16) + q, q = 0..3.
+  if constexpr (EPI == kEpiSwiglu) {
+    // tiles j = 0, 2 hold gate columns and j = 1, 3 the up columns of the
+    // same hidden units (the B rows were interleaved in blocks of 16)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int h = (n0 + wn * 64) / 2 + jp * 16 + fr;
+      if (h >= Nr) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + q;
+          if (t < L)
+            hout[static_cast<size_t>(t) * Nr + h] =
+                swiglu_bf16(acc[i][2 * jp][q], acc[i][2 * jp + 1][q]);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn * 64 + j * 16 + fr;
@@ -218,11 +264,12 @@ __device__ __forceinline__ void gemm_step(uint8_t* smem, const uint16_t* const (
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
 }
 
+template <int EPI>
 __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wc, const float* __restrict__ rb,
     const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
-    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out) {
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out, uint16_t* __restrict__ hout) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[GSTAGES * GSTAGE_BYTES];
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int nblk = n_mt * n_nt;
@@ -246,9 +293,15 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
     const int c = swz_chunk(r, l & 3);
     const int t = min(m0 + r, L - 1);
     asrc[u] = x + static_cast<size_t>(t) * d + c * 8;
-    const int n = min(n0 + r, NT - 1);
-    bsrc[u] = (n < Nr ? wr + static_cast<size_t>(n) * d : wc + static_cast<size_t>(n - Nr) * d) +
-              c * 8;
+    if constexpr (EPI == kEpiSwiglu) {
+      const int n = n0 + r;
+      const int h = min(swiglu_hidden(n), Nr - 1);
+      bsrc[u] = ((n >> 4) & 1 ? wc : wr) + static_cast<size_t>(h) * d + c * 8;
+    } else {
+      const int n = min(n0 + r, NT - 1);
+      bsrc[u] = (n < Nr ? wr + static_cast<size_t>(n) * d : wc + static_cast<size_t>(n - Nr) * d) +
+                c * 8;
+    }
   }
 
   f32x4 acc[8][4];
@@ -285,6 +338,25 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
 
   // Accumulator lane layout (16x16 output tile): column = lane % 16,
   // rows 4 * (lane / 16) + q, q = 0..3.
+  if constexpr (EPI == kEpiSwiglu) {
+    // tiles j = 0, 2 hold gate columns and j = 1, 3 the up columns of the
+    // same hidden units (the B rows were interleaved in blocks of 16)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int h = (n0 + wn * 64) / 2 + jp * 16 + fr;
+      if (h >= Nr) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
+          if (t < L)
+            hout[static_cast<size_t>(t) * Nr + h] =
+                swiglu_bf16(acc[i][2 * jp][q], acc[i][2 * jp + 1][q]);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn * 64 + j * 16 + fr;
@@ -346,13 +418,13 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
   if (L == 0) return hipSuccess;
   if (d % GBK == 0) {
     const int n_mt = (L + GBM - 1) / GBM, n_nt = (Nr + Nc + GBN - 1) / GBN;
-    router_gemm_bf16_big_kernel<<<n_mt * n_nt, 512, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr,
-                                                            Nc, n_mt, n_nt, 0);
+    router_gemm_bf16_big_kernel<kEpiLogits><<<n_mt * n_nt, 512, 0, s>>>(
+        x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr);
     return hipGetLastError();
   }
   const int n_mt = (L + RBM - 1) / RBM, n_nt = (Nr + Nc + RBN - 1) / RBN;
-  router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc,
-                                                      n_mt, n_nt, 0);
+  router_gemm_bf16_kernel<kEpiLogits><<<n_mt * n_nt, 256, 0, s>>>(
+      x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr);
   return hipGetLastError();
 }
 
@@ -377,19 +449,68 @@ hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int 
     const uint16_t* pb = static_cast<const uint16_t*>(b);
     const int big_tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
     if (K % GBK == 0 && big_tiles >= 192) {  // the large tile only where it still fills the chip
-      router_gemm_bf16_big_kernel<<<big_tiles, 512, 0, s>>>(
+      router_gemm_bf16_big_kernel<kEpiLogits><<<big_tiles, 512, 0, s>>>(
           pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, (M + GBM - 1) / GBM,
-          (N + GBN - 1) / GBN, accumulate);
+          (N + GBN - 1) / GBN, accumulate, nullptr);
     } else {
       const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
-      router_gemm_bf16_kernel<<<n_mt * n_nt, 256, 0, s>>>(pa, pb, pb, nullptr, nullptr, c, c, M,
-                                                          K, N, 0, n_mt, n_nt, accumulate);
+      router_gemm_bf16_kernel<kEpiLogits><<<n_mt * n_nt, 256, 0, s>>>(
+          pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, n_mt, n_nt, accumulate, nullptr);
     }
   } else {
     const size_t n = static_cast<size_t>(M) * N;
     router_gemm_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(a), static_cast<const float*>(b), static_cast<const float*>(b),
         nullptr, nullptr, c, c, M, K, N, 0, accumulate);
+  }
+  return hipGetLastError();
+}
+
+// Shared dense MLP, first product: h[t, j] = silu(x_t . Wg[j]) * (x_t . Wu[j]),
+// float32 path: one thread per (token, hidden unit), features in ascending
+// order, float4 loads.
+__global__ __launch_bounds__(256) void swiglu_f32_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ wg,
+                                                         const float* __restrict__ wu, int L,
+                                                         int d, int d_ff, float* __restrict__ h) {
+  const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= static_cast<size_t>(L) * d_ff) return;
+  const int t = static_cast<int>(id / d_ff), j = static_cast<int>(id - static_cast<size_t>(t) * d_ff);
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * d);
+  const float4* gr = reinterpret_cast<const float4*>(wg + static_cast<size_t>(j) * d);
+  const float4* ur = reinterpret_cast<const float4*>(wu + static_cast<size_t>(j) * d);
+  float g = 0.f, u = 0.f;
+  for (int c = 0; c < d / 4; ++c) {
+    const float4 a = xr[c], b = gr[c], e = ur[c];
+    g = fmaf(a.x, b.x, g); g = fmaf(a.y, b.y, g); g = fmaf(a.z, b.z, g); g = fmaf(a.w, b.w, g);
+    u = fmaf(a.x, e.x, u); u = fmaf(a.y, e.y, u); u = fmaf(a.z, e.z, u); u = fmaf(a.w, e.w, u);
+  }
+  h[id] = g / (1.f + __expf(-g)) * u;
+}
+
+hipError_t launch_swiglu_up(int bf16, const void* x, const void* wg, const void* wu, void* h,
+                            int L, int d, int d_ff, hipStream_t s) {
+  if (L == 0 || d_ff == 0) return hipSuccess;
+  if (bf16) {
+    const uint16_t* px = static_cast<const uint16_t*>(x);
+    const uint16_t* pg = static_cast<const uint16_t*>(wg);
+    const uint16_t* pu = static_cast<const uint16_t*>(wu);
+    uint16_t* ph = static_cast<uint16_t*>(h);
+    const int n_log = 2 * ((d_ff + 15) / 16 * 16);  // interleaved gate / up columns
+    const int big_mt = (L + GBM - 1) / GBM, big_nt = (n_log + GBN - 1) / GBN;
+    if (d % GBK == 0 && big_mt * big_nt >= 192) {
+      router_gemm_bf16_big_kernel<kEpiSwiglu><<<big_mt * big_nt, 512, 0, s>>>(
+          px, pg, pu, nullptr, nullptr, nullptr, nullptr, L, d, d_ff, 0, big_mt, big_nt, 0, ph);
+    } else {
+      const int n_mt = (L + RBM - 1) / RBM, n_nt = (n_log + RBN - 1) / RBN;
+      router_gemm_bf16_kernel<kEpiSwiglu><<<n_mt * n_nt, 256, 0, s>>>(
+          px, pg, pu, nullptr, nullptr, nullptr, nullptr, L, d, d_ff, 0, n_mt, n_nt, 0, ph);
+    }
+  } else {
+    const size_t n = static_cast<size_t>(L) * d_ff;
+    swiglu_f32_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+        static_cast<const float*>(x), static_cast<const float*>(wg), static_cast<const float*>(wu),
+        L, d, d_ff, static_cast<float*>(h));
   }
   return hipGetLastError();
 }

@@ -62,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 4 */
+int omni_abi_version(void);  /* 5 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -266,6 +266,33 @@ omni_status omni_routed_backward(omni_dtype dt, int L, int d, int Nr, int Nc, in
                                  float* dwc_t, float* drow_bias, float* dcol_bias,
                                  int32_t* counts, int32_t* active, float* dw, float* dv,
                                  float* dgate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * omni_shared_mlp — the shared dense MLP branch of the OmniMoE layer: the
+ * dense branch every token passes through, next to the routed atomic experts
+ * (gist.science explainer §2 and §2.1 "Shared Dense MLP"; interactive
+ * explainer "Atomic Expert").  The pages print no formula for it; this is the
+ * gated SwiGLU form (the activation the pages name):
+ *
+ *   y_t (+)= Wd (silu(Wg x_t) * (Wu x_t))
+ *
+ * x [L, d], w_gate [d_ff, d], w_up [d_ff, d] (row j: hidden unit j's input
+ * weights), w_down [d, d_ff] (row c: output feature c's weights), all of dt;
+ * y [L, d] float32.  accumulate = 0 overwrites y; accumulate != 0 adds the
+ * branch onto y as it stands, which is the layer's hybrid sum when y holds
+ * the routed output of omni_atomic_forward (or call omni_atomic_forward with
+ * its accumulate flag after this one).  The bf16 path runs both products on
+ * MFMA with fp32 accumulation and keeps the hidden activation in bf16; the
+ * float32 path computes it in float32.
+ * ws / ws_bytes: at least omni_shared_mlp_workspace(dt, L, d_ff) bytes,
+ * 256-byte aligned (the hidden activation, L * d_ff elements of dt).
+ * Requires d and d_ff multiples of 8 (bf16) or 4 (float32), else
+ * UNSUPPORTED; 16-byte aligned arrays.  Deterministic.
+ */
+size_t omni_shared_mlp_workspace(omni_dtype dt, int L, int d_ff);
+omni_status omni_shared_mlp(omni_dtype dt, int L, int d, int d_ff, const void* x,
+                            const void* w_gate, const void* w_up, const void* w_down, float* y,
+                            int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

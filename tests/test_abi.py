@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 4
+    assert lib.omni_abi_version() == 5
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -181,3 +181,30 @@ def test_routed_backward_argument_checks(lib):
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
+
+
+def test_shared_mlp_argument_checks(lib):
+    f = lib.omni_shared_mlp
+    nws = lib.omni_shared_mlp_workspace(1, 4, 256)
+    assert nws == 4 * 256 * 2
+    assert lib.omni_shared_mlp_workspace(0, 4, 256) == 4 * 256 * 4
+    assert lib.omni_shared_mlp_workspace(1, 4, 0) == 0
+    assert lib.omni_shared_mlp_workspace(2, 4, 256) == 0
+
+    def call(dt=1, L=4, d=128, d_ff=256, x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, y=FAKE, ws=FAKE,
+             n=nws):
+        return f(dt, L, d, d_ff, x, wg, wu, wd, y, 0, ws, n, None)
+    assert call(dt=2) == B.OMNI_ERR_INVALID_ARG
+    assert call(d=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(d_ff=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(L=-1) == B.OMNI_ERR_INVALID_ARG
+    assert call(x=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(wd=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(wu=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(d=132) == B.OMNI_ERR_UNSUPPORTED            # bf16 needs multiples of 8
+    assert call(d_ff=252) == B.OMNI_ERR_UNSUPPORTED
+    assert call(dt=0, d=130, n=4096) == B.OMNI_ERR_UNSUPPORTED  # float32: multiples of 4
+    assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
+    # an empty batch needs no x or y and enqueues nothing
+    assert call(L=0, x=None, y=None, n=lib.omni_shared_mlp_workspace(1, 0, 256)) == B.OMNI_OK
