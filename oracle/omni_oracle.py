@@ -194,12 +194,15 @@ def gates(score):
 # ---------------------------------------------------------------- O6 - O9
 
 
-def max_groups(N, L, K, B):
-    """Upper bound on the number of groups: ceil(min(N, L*K) / B)."""
+def max_groups(N, L, K, B, grouping="active"):
+    """Upper bound on the number of groups: ceil(min(N, L*K) / B) when the
+    active experts are cut B at a time; ceil(N / B) id windows otherwise."""
+    if grouping == "window":
+        return -(-N // B)
     return -(-min(N, L * K) // B)
 
 
-def build_schedule(expert_idx, gate, N, B):
+def build_schedule(expert_idx, gate, N, B, grouping="active"):
     """Expert-Centric Scheduling of the L*K routing decisions.
 
     [EXPL, Expert-Centric Scheduling] and [GS-NL §2.2]:
@@ -211,6 +214,10 @@ def build_schedule(expert_idx, gate, N, B):
          token's tasks inside one group keep their rank order k);
       4. each group's parameters are then loaded once and reused for all of
          its tokens (the executor's business; here only the CSR offsets).
+    grouping="window" is the fixed-window variant: group g holds the experts
+    with ids in [g B, (g + 1) B) ([GS-NL §2.2] groups tasks by contiguous
+    ranges of expert ids); every window is a group, empty or not, so
+    n_groups = ceil(N / B).
     Returns a dict of numpy arrays; group_offsets has max_groups + 1 entries
     and every entry past n_groups equals M.
     """
@@ -224,12 +231,16 @@ def build_schedule(expert_idx, gate, N, B):
 
     active = np.unique(task_expert)                     # sorted ascending
     n_active = int(active.size)
-    n_groups = -(-n_active // B)
-    rank = np.searchsorted(active, task_expert)         # position in active list
-    group = rank // B
+    if grouping == "window":
+        n_groups = -(-N // B)
+        group = task_expert // B                        # the id window
+    else:
+        n_groups = -(-n_active // B)
+        rank = np.searchsorted(active, task_expert)     # position in active list
+        group = rank // B
 
     order = np.lexsort((task_token, group))             # group, then token; stable
-    G = max_groups(N, L, K, B)
+    G = max_groups(N, L, K, B, grouping)
     sizes = np.bincount(group, minlength=G)[:G] if M else np.zeros(G, np.int64)
     offsets = np.zeros(G + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(sizes)

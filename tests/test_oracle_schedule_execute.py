@@ -79,6 +79,54 @@ def test_schedule_invariants(L, K, N, B, hot):
         assert act[min(len(act) - 1, (g + 1) * B - 1)] < act[(g + 1) * B]
 
 
+def test_window_grouping_golden_worked_examples():
+    g = load_golden("schedule_window_example.json")
+    for ex in g["examples"]:
+        idx = np.array(ex["expert_idx"])
+        gate = np.array(ex["gate"], np.float32)
+        s = O.build_schedule(idx, gate, ex["N"], ex["B"], grouping="window")
+        e = ex["expect"]
+        assert s["n_groups"] == e["n_groups"]
+        for key in ("group_offsets", "task_index", "task_token", "task_expert"):
+            assert list(s[key]) == e[key], (ex["note"], key)
+        np.testing.assert_array_equal(s["task_gate"], np.array(e["task_gate"], np.float32))
+        if "expect_active_grouping" in ex:
+            r = O.build_schedule(idx, gate, ex["N"], ex["B"])
+            assert r["n_groups"] == ex["expect_active_grouping"]["n_groups"]
+            assert list(r["task_index"]) == ex["expect_active_grouping"]["task_index"]
+
+
+@pytest.mark.parametrize("L,K,N,B,hot", [(37, 5, 200, 7, 0), (40, 4, 4096, 3, 30),
+                                         (50, 6, 64, 64, 0), (9, 3, 10, 1, 0),
+                                         (1, 1, 1, 1, 0), (12, 4, 100, 1000, 0)])
+def test_window_grouping_invariants(L, K, N, B, hot):
+    idx, gate = _random_routing(L, K, N, seed=3 * L + K + N + B, hot=hot)
+    s = O.build_schedule(idx, gate, N, B, grouping="window")
+    M = L * K
+    G = O.max_groups(N, L, K, B, "window")
+    assert s["n_groups"] == G == math.ceil(N / B)
+    offs = s["group_offsets"]
+    assert len(offs) == G + 1 and offs[0] == 0 and offs[-1] == M
+    assert sorted(s["task_index"]) == list(range(M))
+    for g in range(G):
+        lo, hi = offs[g], offs[g + 1]
+        ex = s["task_expert"][lo:hi]
+        assert ((ex >= g * B) & (ex < (g + 1) * B)).all()       # the id window
+        # every task of the window is in the group
+        assert hi - lo == int(((idx >= g * B) & (idx < (g + 1) * B)).sum())
+        assert (np.diff(s["task_token"][lo:hi]) >= 0).all()
+        ti, tok = s["task_index"][lo:hi], s["task_token"][lo:hi]
+        assert all(a_ < b_ for a_, b_, ta, tb in zip(ti[:-1], ti[1:], tok[:-1], tok[1:])
+                   if ta == tb)
+    # B = 1: windows are single experts, the same order as ranking the actives
+    if B == 1:
+        r = O.build_schedule(idx, gate, N, 1)
+        np.testing.assert_array_equal(s["task_index"], r["task_index"])
+    # one window holding every expert: flatten order unchanged
+    if B >= N:
+        np.testing.assert_array_equal(s["task_index"], np.arange(M))
+
+
 def test_expert_centric_equals_token_centric_and_counts_traffic():
     # The ablation table of the explainer: removing expert-centric scheduling
     # leaves model quality unchanged -> both orders compute the same y.
