@@ -18,7 +18,8 @@ LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
-ABI_VERSION = 5
+GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
+ABI_VERSION = 6
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -50,9 +51,9 @@ _SIGS = {
     "omni_product_topk_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "omni_product_topk": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _sz, _vp]),
-    "omni_schedule_max_groups": (_i, [_i, _i, _i, _i]),
-    "omni_schedule_workspace": (_sz, [_i, _i, _i, _i]),
-    "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),
+    "omni_schedule_max_groups": (_i, [_i, _i, _i, _i, _i]),
+    "omni_schedule_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),
                                  _vp, _sz, _vp]),
     "omni_atomic_forward_mode": (_i, [_i, _i, _i, _i, _i, _i]),
     "omni_atomic_forward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -188,6 +189,7 @@ class Schedule:
     K: int
     N: int
     B: int
+    grouping: str
     counts: torch.Tensor
     active: torch.Tensor
     group_offsets: torch.Tensor
@@ -203,17 +205,24 @@ class Schedule:
             self.task_gate, self.task_index)))
 
 
-def max_groups(L, K, N, B):
-    return lib().omni_schedule_max_groups(L, K, N, B)
+def _grouping(grouping):
+    if grouping not in GROUPINGS:
+        raise ValueError(f"grouping must be one of {sorted(GROUPINGS)}, got {grouping!r}")
+    return GROUPINGS[grouping]
 
 
-def alloc_schedule(L, K, N, B, device, with_index=True):
-    """Device buffers for a schedule of L*K tasks (and its workspace)."""
+def max_groups(L, K, N, B, grouping="active"):
+    return lib().omni_schedule_max_groups(L, K, N, B, _grouping(grouping))
+
+
+def alloc_schedule(L, K, N, B, device, with_index=True, grouping="active"):
+    """Device buffers for a schedule of L*K tasks (and its workspace).
+    grouping: "active" (B active experts per group) or "window" (id windows)."""
     M = L * K
-    G = max_groups(L, K, N, B)
-    nws = lib().omni_schedule_workspace(L, K, N, B)
+    G = max_groups(L, K, N, B, grouping)
+    nws = lib().omni_schedule_workspace(L, K, N, B, _grouping(grouping))
     i32 = dict(dtype=torch.int32, device=device)
-    return Schedule(L, K, N, B,
+    return Schedule(L, K, N, B, grouping,
                     counts=torch.zeros(2, **i32),
                     active=torch.empty(max(1, min(N, M)), **i32),
                     group_offsets=torch.empty(G + 1, **i32),
@@ -224,17 +233,19 @@ def alloc_schedule(L, K, N, B, device, with_index=True):
                     workspace=torch.empty(max(1, nws), dtype=torch.uint8, device=device))
 
 
-def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None):
+def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None, grouping="active"):
     """omni_schedule_tasks: returns a Schedule of device tensors."""
     L, K = expert_idx.shape
     _req(expert_idx, "expert_idx", torch.int32)
     _req(gate, "gate", torch.float32, (L, K))
     if sched is None:
-        sched = alloc_schedule(L, K, N, B, expert_idx.device)
+        sched = alloc_schedule(L, K, N, B, expert_idx.device, grouping=grouping)
+    elif sched.grouping != grouping:
+        raise ValueError(f"schedule buffers were sized for grouping {sched.grouping!r}")
     st = sched.struct()
     ws = sched.workspace
     _check("omni_schedule_tasks", lib().omni_schedule_tasks(
-        L, K, N, B, _ptr(expert_idx), _ptr(gate), ctypes.byref(st), _ptr(ws),
+        L, K, N, B, _grouping(grouping), _ptr(expert_idx), _ptr(gate), ctypes.byref(st), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(stream)))
     return sched
 

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -108,10 +108,14 @@ omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const fl
                                               csel, flags, lse, stream));
 }
 
-int omni_schedule_max_groups(int L, int K, int N, int B) {
-  if (L < 0 || K < 1 || N < 1 || B < 1) return 0;
+static bool grouping_ok(omni_grouping g) {
+  return g == OMNI_GROUP_ACTIVE || g == OMNI_GROUP_ID_WINDOW;
+}
+
+int omni_schedule_max_groups(int L, int K, int N, int B, omni_grouping grouping) {
+  if (L < 0 || K < 1 || N < 1 || B < 1 || !grouping_ok(grouping)) return 0;
   const long long M = static_cast<long long>(L) * K;
-  const long long mn = M < N ? M : N;
+  const long long mn = grouping == OMNI_GROUP_ID_WINDOW ? N : (M < N ? M : N);
   return static_cast<int>((mn + B - 1) / B);
 }
 
@@ -119,24 +123,26 @@ static bool schedule_args_ok(int L, int K, int N, int B) {
   return L >= 0 && K >= 1 && N >= 1 && B >= 1 && fits_i32(static_cast<long long>(L) * K);
 }
 
-size_t omni_schedule_workspace(int L, int K, int N, int B) {
-  if (!schedule_args_ok(L, K, N, B)) return 0;
-  return omni::schedule_ws_layout(L, K, N, B).bytes;
+size_t omni_schedule_workspace(int L, int K, int N, int B, omni_grouping grouping) {
+  if (!schedule_args_ok(L, K, N, B) || !grouping_ok(grouping)) return 0;
+  return omni::schedule_ws_layout(L, K, N, B, grouping == OMNI_GROUP_ID_WINDOW).bytes;
 }
 
-omni_status omni_schedule_tasks(int L, int K, int N, int B, const int32_t* expert_idx,
-                                const float* gate, const omni_schedule* out, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
-  if (!schedule_args_ok(L, K, N, B)) return OMNI_ERR_INVALID_ARG;
+omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping grouping,
+                                const int32_t* expert_idx, const float* gate,
+                                const omni_schedule* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!schedule_args_ok(L, K, N, B) || !grouping_ok(grouping)) return OMNI_ERR_INVALID_ARG;
   if (!out || !out->counts || !out->group_offsets) return OMNI_ERR_INVALID_ARG;
   const long long M = static_cast<long long>(L) * K;
   if (M > 0 && (!expert_idx || !gate || !out->active || !out->task_token || !out->task_expert ||
                 !out->task_gate))
     return OMNI_ERR_INVALID_ARG;
-  const size_t need = omni_schedule_workspace(L, K, N, B);
+  const size_t need = omni_schedule_workspace(L, K, N, B, grouping);
   if (M > 0 && (!ws || ws_bytes < need)) return OMNI_ERR_WORKSPACE;
   if (M > 0 && !aligned256(ws)) return OMNI_ERR_WORKSPACE;
-  return hip_status(omni::launch_schedule(L, K, N, B, expert_idx, gate, out->counts, out->active,
+  return hip_status(omni::launch_schedule(L, K, N, B, grouping == OMNI_GROUP_ID_WINDOW,
+                                          expert_idx, gate, out->counts, out->active,
                                           out->group_offsets, out->task_token, out->task_expert,
                                           out->task_gate, out->task_index, ws, stream));
 }

@@ -430,7 +430,7 @@ struct SchedBufs {  // a schedule with groups of one, in the backward workspace
 static SchedBufs sched_bufs(size_t& o, int L, int K, int N) {
   SchedBufs b{};
   const size_t M = static_cast<size_t>(L) * K;
-  b.lay = schedule_ws_layout(L, K, N, 1);
+  b.lay = schedule_ws_layout(L, K, N, 1, 0);
   const size_t g = static_cast<size_t>(b.lay.max_groups);
   b.cnt = o; o = a256(o + 2 * 4);
   b.act = o; o = a256(o + (g > 0 ? g : 1) * 4);
@@ -541,7 +541,7 @@ static hipError_t launch_bwd_t(const T* x, const T* wr, const T* wc, const T* w,
   // active expert i, from the expert-major task list
   auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  e = launch_schedule(L, K, N, 1, expert_idx, gate, counts, active, I(lay.es.off), I(lay.es.tok),
+  e = launch_schedule(L, K, N, 1, 0, expert_idx, gate, counts, active, I(lay.es.off), I(lay.es.tok),
                       I(lay.es.exp), F(lay.es.gat), I(lay.es.idx), ws + lay.es.ws, s);
   if (e != hipSuccess) return e;
   if (M == 0) return hipGetLastError();

@@ -36,8 +36,10 @@ struct ScheduleWs {
   size_t flags, tile_cnt, rank, key0, val0, key1, val1, hist, dtot;  // byte offsets
   int n_ftiles, n_ttiles, passes, max_groups;
 };
-ScheduleWs schedule_ws_layout(int L, int K, int N, int B);
-hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx,
+// window = 0: groups of B active experts in id order; window != 0: group g
+// is the id window [g B, (g + 1) B), every window a group.
+ScheduleWs schedule_ws_layout(int L, int K, int N, int B, int window);
+hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t* expert_idx,
                            const float* gate, int32_t* counts, int32_t* active,
                            int32_t* group_offsets, int32_t* task_token, int32_t* task_expert,
                            float* task_gate, int32_t* task_index, void* ws, hipStream_t s);

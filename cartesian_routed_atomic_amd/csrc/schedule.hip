@@ -11,7 +11,8 @@
 //   2. count flags per 4096-expert tile; each tile sums the counts of the
 //      tiles before it, scans its own flags and writes rank[e] (position
 //      among active experts) and the ascending active list;
-//   3. stable LSD radix sort of the tasks by group g = rank[e] / B, 8 bits
+//   3. stable LSD radix sort of the tasks by group g = rank[e] / B (or, in
+//      the fixed-window variant, g = e / B: the id window), 8 bits
 //      per pass.  Tasks enter in flatten order m = t*K + k, which is already
 //      token-major, so a stable sort by group alone yields (group, token)
 //      order with ties in flatten order.  Each pass: per-tile digit
@@ -30,12 +31,12 @@ constexpr int kSTile = 2048;  // tasks per sort tile (512 threads x 4)
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-ScheduleWs schedule_ws_layout(int L, int K, int N, int B) {
+ScheduleWs schedule_ws_layout(int L, int K, int N, int B, int window) {
   ScheduleWs w{};
   const long long M = static_cast<long long>(L) * K;
   w.n_ftiles = static_cast<int>((static_cast<long long>(N) + kTile - 1) / kTile);
   w.n_ttiles = static_cast<int>((M + kSTile - 1) / kSTile);
-  const long long mn = M < N ? M : N;
+  const long long mn = window ? N : (M < N ? M : N);  // every id window is a group
   w.max_groups = static_cast<int>((mn + B - 1) / B);
   int bits = 0;
   while (bits < 31 && (1ll << bits) < w.max_groups) ++bits;  // groups are < max_groups
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void tile_count_kernel(const uint8_t* __restri
 
 __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ flags, int N,
                                                    const int* __restrict__ tile_cnt, int n_tiles,
-                                                   int B, int* __restrict__ rank,
+                                                   int B, int window, int* __restrict__ rank,
                                                    int* __restrict__ active,
                                                    int* __restrict__ counts) {
   __shared__ int red[4];
@@ -135,16 +136,16 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ f
   }
   if (b == n_tiles - 1 && tid == 255) {
     counts[0] = run;
-    counts[1] = (run + B - 1) / B;
+    counts[1] = window ? static_cast<int>((static_cast<long long>(N) + B - 1) / B)
+                       : (run + B - 1) / B;
   }
-  (void)N;
 }
 
 // Per-tile digit histogram, digit-major: hist[d * n_tt + tile].  The first
 // pass computes the group key of each task (kout) on the way.
 __global__ __launch_bounds__(512) void radix_up_kernel(
     const int* __restrict__ kin, const int32_t* __restrict__ idx, const int* __restrict__ rank,
-    int* __restrict__ kout, int M, int N, int B, int pass, int n_tt,
+    int* __restrict__ kout, int M, int N, int B, int window, int pass, int n_tt,
     const int* __restrict__ counts, int* __restrict__ hist) {
   if (pass >= effective_passes(counts[1])) return;
   __shared__ uint32_t h[256];
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(512) void radix_up_kernel(
     int key;
     if (pass == 0) {
       const int e = idx[i];
-      key = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? rank[e] / B : 0;
+      key = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? (window ? e : rank[e]) / B : 0;
       kout[i] = key;
     } else {
       key = kin[i];
@@ -283,9 +284,10 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
   }
 }
 
-// CSR offsets: off[g] = first sorted position of group g (groups are never
-// empty); entries from n_groups to G hold M.  The sorted keys are those of
-// the last effective pass.
+// CSR offsets: off[g] = first sorted position of group g.  An empty group
+// (only id windows can be empty) gets the position of the next non-empty
+// one; entries past the last task's group, up to G, hold M.  The sorted keys
+// are those of the last effective pass.
 __global__ __launch_bounds__(256) void offsets_kernel(const int* __restrict__ skey_even,
                                                       const int* __restrict__ skey_odd, int M,
                                                       int G, const int* __restrict__ counts,
@@ -298,27 +300,35 @@ __global__ __launch_bounds__(256) void offsets_kernel(const int* __restrict__ sk
     const int gp = i ? min(skey[i - 1], G - 1) : -1;
     for (int j = gp + 1; j <= g; ++j) off[j] = i;
   }
-  if (i <= G && i >= counts[1]) off[i] = M;
+  if (i <= G && i > min(skey[M - 1], G - 1)) off[i] = M;
 }
 
-__global__ void empty_schedule_kernel(int* counts, int* off) {
-  counts[0] = 0;
-  counts[1] = 0;
-  off[0] = 0;
+// No tasks: no active expert; every group (only id windows exist without
+// tasks) is empty.
+__global__ __launch_bounds__(256) void empty_schedule_kernel(int* counts, int* off, int n_groups,
+                                                             int G) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) {
+    counts[0] = 0;
+    counts[1] = n_groups;
+  }
+  if (i <= G) off[i] = 0;
 }
 
 static inline unsigned blocks_for(long long n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }
 
-hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx,
+hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t* expert_idx,
                            const float* gate, int32_t* counts, int32_t* active,
                            int32_t* group_offsets, int32_t* task_token, int32_t* task_expert,
                            float* task_gate, int32_t* task_index, void* ws, hipStream_t s) {
   const int M = L * K;
-  const ScheduleWs lay = schedule_ws_layout(L, K, N, B);
+  const ScheduleWs lay = schedule_ws_layout(L, K, N, B, window);
   if (M == 0) {
-    empty_schedule_kernel<<<1, 1, 0, s>>>(counts, group_offsets);
+    const int ng = window ? lay.max_groups : 0;
+    empty_schedule_kernel<<<blocks_for(static_cast<long long>(lay.max_groups) + 1, 256), 256, 0,
+                            s>>>(counts, group_offsets, ng, lay.max_groups);
     return hipGetLastError();
   }
   char* base = static_cast<char*>(ws);
@@ -337,8 +347,8 @@ hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx
       reinterpret_cast<uint4*>(flags), n16);
   mark_kernel<<<blocks_for(M, 256), 256, 0, s>>>(expert_idx, M, N, flags);
   tile_count_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, tile_cnt);
-  rank_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, N, tile_cnt, lay.n_ftiles, B, rank, active,
-                                           counts);
+  rank_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, N, tile_cnt, lay.n_ftiles, B, window, rank,
+                                           active, counts);
   // pass p reads (key, val) from buffer p & 1 and writes buffer (p + 1) & 1;
   // pass 0 reads the group keys it computes itself (key0) and identity values
   int* kb[2] = {key0, key1};
@@ -346,8 +356,8 @@ hipError_t launch_schedule(int L, int K, int N, int B, const int32_t* expert_idx
   for (int p = 0; p < lay.passes; ++p) {
     int* kin = kb[p & 1];
     const int* vin = p == 0 ? nullptr : vb[p & 1];
-    radix_up_kernel<<<lay.n_ttiles, 512, 0, s>>>(kin, expert_idx, rank, key0, M, N, B, p,
-                                                 lay.n_ttiles, counts, hist);
+    radix_up_kernel<<<lay.n_ttiles, 512, 0, s>>>(kin, expert_idx, rank, key0, M, N, B, window,
+                                                 p, lay.n_ttiles, counts, hist);
     radix_rowscan_kernel<<<256, 64, 0, s>>>(hist, lay.n_ttiles, p, counts, dtot);
     radix_down_kernel<<<lay.n_ttiles, 512, 0, s>>>(
         kin, vin, M, p, lay.n_ttiles, hist, dtot, counts, kb[(p + 1) & 1], vb[(p + 1) & 1], K,

@@ -62,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 5 */
+int omni_abi_version(void);  /* 6 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -130,8 +130,27 @@ omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * How omni_schedule_tasks forms its groups.
+ *   OMNI_GROUP_ACTIVE     the unique active experts in id order, B per group
+ *                         (the last group may be short); n_groups =
+ *                         ceil(n_active / B).  Interactive explainer,
+ *                         "Expert-Centric Scheduling".
+ *   OMNI_GROUP_ID_WINDOW  fixed windows of the id space: group g holds the
+ *                         experts with ids in [g B, (g + 1) B), every window a
+ *                         group (empty ones too); n_groups = ceil(N / B).
+ *                         gist.science explainer §2.2 (tasks grouped by
+ *                         contiguous ranges of expert ids).
+ * Either way the tasks are ordered by (group, token), ties in flatten order.
+ */
+typedef enum omni_grouping {
+  OMNI_GROUP_ACTIVE = 0,
+  OMNI_GROUP_ID_WINDOW = 1
+} omni_grouping;
+
+/*
  * Schedule produced by omni_schedule_tasks (all members device pointers).
- * G = omni_schedule_max_groups(L, K, N, B) = ceil(min(N, L*K) / B).
+ * G = omni_schedule_max_groups(L, K, N, B, grouping): ceil(min(N, L*K) / B)
+ * for OMNI_GROUP_ACTIVE, ceil(N / B) for OMNI_GROUP_ID_WINDOW.
  *   counts        [2]      int32: n_active, n_groups.
  *   active        [min(N, L*K)] int32: the active expert ids ascending
  *                          (entries >= n_active unspecified).
@@ -152,8 +171,8 @@ typedef struct omni_schedule {
   int32_t* task_index;
 } omni_schedule;
 
-/* ceil(min(N, L*K) / B): the number of groups the schedule can hold. */
-int omni_schedule_max_groups(int L, int K, int N, int B);
+/* G above: the number of groups the schedule can hold (0 for invalid args). */
+int omni_schedule_max_groups(int L, int K, int N, int B, omni_grouping grouping);
 
 /*
  * omni_schedule_tasks — Expert-Centric Scheduling.
@@ -163,6 +182,9 @@ int omni_schedule_max_groups(int L, int K, int N, int B);
  * token id) and gist.science explainer §2.2 (task collection, grouping and
  * sorting, grouped execution).
  *
+ * grouping: OMNI_GROUP_ACTIVE (the pages' B active experts per group) or
+ * OMNI_GROUP_ID_WINDOW (fixed id windows), see omni_grouping; anything else
+ * is INVALID_ARG.
  * expert_idx [L, K] int32 in (each id in [0, N)); gate [L, K] float32 in.
  * out: host pointer to a descriptor whose members point to device buffers
  * of the sizes listed above.  ws / ws_bytes: workspace of at least
@@ -171,8 +193,8 @@ int omni_schedule_max_groups(int L, int K, int N, int B);
  * unspecified results (the ids are produced on the device and not checked).
  * Bit-exact: the result is a pure function of the inputs.
  */
-size_t omni_schedule_workspace(int L, int K, int N, int B);
-omni_status omni_schedule_tasks(int L, int K, int N, int B,
+size_t omni_schedule_workspace(int L, int K, int N, int B, omni_grouping grouping);
+omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping grouping,
                                 const int32_t* expert_idx, const float* gate,
                                 const omni_schedule* out,
                                 void* ws, size_t ws_bytes, hipStream_t stream);

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 5
+    assert lib.omni_abi_version() == 6
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -94,16 +94,24 @@ def test_product_topk_argument_checks(lib):
 
 def test_schedule_argument_checks(lib):
     L, K, N, Bg = 64, 8, 1024, 16
-    assert lib.omni_schedule_max_groups(L, K, N, Bg) == 32
-    assert lib.omni_schedule_max_groups(8192, 64, 1 << 20, 256) == 2048
-    assert lib.omni_schedule_max_groups(256, 64, 1 << 20, 64) == 256
-    nws = lib.omni_schedule_workspace(L, K, N, Bg)
+    assert lib.omni_schedule_max_groups(L, K, N, Bg, 0) == 32
+    assert lib.omni_schedule_max_groups(8192, 64, 1 << 20, 256, 0) == 2048
+    assert lib.omni_schedule_max_groups(256, 64, 1 << 20, 64, 0) == 256
+    # id windows: every window of the id space is a group
+    assert lib.omni_schedule_max_groups(L, K, N, Bg, 1) == 64
+    assert lib.omni_schedule_max_groups(256, 64, 1 << 20, 64, 1) == 16384
+    assert lib.omni_schedule_max_groups(L, K, N, Bg, 2) == 0
+    assert lib.omni_schedule_workspace(L, K, N, Bg, 2) == 0
+    nws = lib.omni_schedule_workspace(L, K, N, Bg, 0)
     assert nws > 0
     st = B.ScheduleStruct(*([1 << 20] * 7))
     f = lib.omni_schedule_tasks
 
-    def call(L=L, K=K, N=N, Bg=Bg, ws=FAKE, n=nws, s=st):
-        return f(L, K, N, Bg, FAKE, FAKE, ctypes.byref(s) if s is not None else None, ws, n, None)
+    def call(L=L, K=K, N=N, Bg=Bg, ws=FAKE, n=nws, s=st, grouping=0):
+        return f(L, K, N, Bg, grouping, FAKE, FAKE, ctypes.byref(s) if s is not None else None,
+                 ws, n, None)
+    assert call(grouping=2) == B.OMNI_ERR_INVALID_ARG
+    assert call(grouping=-1) == B.OMNI_ERR_INVALID_ARG
     assert call(K=0) == B.OMNI_ERR_INVALID_ARG
     assert call(Bg=0) == B.OMNI_ERR_INVALID_ARG
     assert call(N=0) == B.OMNI_ERR_INVALID_ARG

@@ -60,10 +60,10 @@ def check_topk(a, b, sel, kp, K, tokens=None):
     assert dg <= 2e-6
 
 
-def check_schedule(sel, sched, N, Bg):
+def check_schedule(sel, sched, N, Bg, grouping="active"):
     idx = host(sel["expert_idx"])
     gate = host(sel["gate"])
-    want = O.build_schedule(idx, gate, N, Bg)
+    want = O.build_schedule(idx, gate, N, Bg, grouping=grouping)
     counts = host(sched.counts)
     assert int(counts[0]) == want["n_active"] and int(counts[1]) == want["n_groups"]
     na = want["n_active"]
@@ -226,6 +226,52 @@ def test_schedule_direct_is_bit_exact(L, K, N, Bg, kind):
     sched = B.schedule_tasks(dev(idx), dev(gate), N, Bg)
     torch.cuda.synchronize()
     check_schedule({"expert_idx": dev(idx), "gate": dev(gate)}, sched, N, Bg)
+
+
+@pytest.mark.parametrize("L,K,N,Bg,kind", [(100, 8, 1000, 7, "uniform"),
+                                          (3000, 16, 50000, 64, "zipf"),
+                                          (37, 5, 1 << 20, 256, "uniform"),
+                                          (9, 3, 10, 1, "uniform"),
+                                          (70000, 3, 210000, 1, "uniform"),
+                                          (40, 4, 100, 1000, "uniform")])
+def test_window_schedule_is_bit_exact(L, K, N, Bg, kind):
+    # fixed id windows: every window a group, empty ones included (up to
+    # 210,000 groups: three radix passes), one window holding every expert
+    log(f"[schedule window] L={L} K={K} N={N} B={Bg} {kind}")
+    if kind == "zipf":
+        idx = _zipf_ids(L, K, N, 1.1, seed=L + 1)
+    else:
+        rng = np.random.default_rng(L + N + 1)
+        idx = np.stack([rng.choice(N, size=K, replace=False) for _ in range(L)]).astype(np.int32)
+    gate = np.random.default_rng(4).random((L, K)).astype(np.float32)
+    sched = B.schedule_tasks(dev(idx), dev(gate), N, Bg, grouping="window")
+    torch.cuda.synchronize()
+    check_schedule({"expert_idx": dev(idx), "gate": dev(gate)}, sched, N, Bg, grouping="window")
+
+
+def test_window_schedule_of_an_empty_batch():
+    idx = torch.empty((0, 4), dtype=torch.int32, device="cuda")
+    gate = torch.empty((0, 4), dtype=torch.float32, device="cuda")
+    sched = B.schedule_tasks(idx, gate, 100, 8, grouping="window")
+    torch.cuda.synchronize()
+    want = O.build_schedule(np.zeros((0, 4), np.int32), np.zeros((0, 4), np.float32), 100, 8,
+                            grouping="window")
+    assert host(sched.counts).tolist() == [0, want["n_groups"]] == [0, 13]
+    np.testing.assert_array_equal(host(sched.group_offsets), want["group_offsets"])
+
+
+@pytest.mark.parametrize("mode", ["expert", "token"])
+def test_window_schedule_gives_the_same_y(mode):
+    # the grouping changes the task order only: y is the same, bit for bit
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl)
+    t = {k: dev(v) for k, v in inp.items()}
+    out = run_pipeline(wl, inp)
+    sw = B.schedule_tasks(out["expert_idx"], out["gate"], wl.N, wl.B, grouping="window")
+    y_a = B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], mode=mode)
+    y_w = B.atomic_forward(t["x"], t["w"], t["v"], sw, mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(y_a.view(torch.int32), y_w.view(torch.int32))
 
 
 def test_schedule_is_deterministic_run_to_run():
