@@ -103,6 +103,8 @@ def main():
                     help="skip timing omni_routed_backward on the same batch")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip timing the whole layer (shared dense MLP + routed branch)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the variants (gated experts, id-window grouping)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the HIP-graph replay of the step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -307,6 +309,30 @@ def main():
             f"{layer['tokens_per_s']:.0f} tokens/s; shared MLP {mlp_ms:.3f} ms = "
             f"{mlp_tflops:.0f} TFLOP/s; routed-only step / layer = {ms / layer_ms:.3f}")
 
+    variants = None
+    if not args.no_variants:
+        variants = {}
+        # SwiGLU-gated experts: a third expert matrix U, read per task like W
+        u = to_dev(make_inputs(wl, parts=("u",))["u"])
+        try:
+            glu_ms = ev_time(lambda: B.atomic_forward_glu(x, w, u, v, sched, y=y,
+                                                          workspace=exec_ws), reps=10)
+            glu_bytes = 3 * wl.d * s * n_active + L * wl.d * s + 4 * L * wl.d + 12 * M
+            variants["glu_expert"] = {
+                "ms": glu_ms, "bytes_alg": glu_bytes,
+                "achieved": glu_bytes / (glu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": glu_bytes / (glu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        except B.OmniError as exc:
+            variants["glu_expert"] = {"unsupported": str(exc)}
+        del u
+        # the schedule with fixed id windows instead of B active experts per group
+        wsched = B.alloc_schedule(L, K, wl.N, wl.B, dev, grouping="window")
+        variants["window_schedule_ms"] = ev_time(
+            lambda: B.schedule_tasks(sel["expert_idx"], sel["gate"], wl.N, wl.B, sched=wsched,
+                                     grouping="window"))
+        variants["window_groups"] = int(wsched.counts.cpu()[1])
+        say(f"[bench] variants: {json.dumps(variants)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         say("[bench] timing the CPU oracle ...")
@@ -345,6 +371,7 @@ def main():
         "expert_usage": n_active / wl.N,
         "backward": bwd,
         "layer": layer,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

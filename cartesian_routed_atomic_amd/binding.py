@@ -19,7 +19,7 @@ OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ER
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -28,6 +28,7 @@ EXPORTS = (
     "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_mode",
     "omni_atomic_forward_workspace", "omni_atomic_forward", "omni_routed_backward_workspace",
     "omni_routed_backward", "omni_shared_mlp_workspace", "omni_shared_mlp",
+    "omni_atomic_forward_glu",
 )
 
 
@@ -62,6 +63,8 @@ _SIGS = {
     "omni_routed_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "omni_routed_backward": (_i, [_i, _i, _i, _i, _i, _i] + [_vp] * 19 + [_sz, _vp]),
     "omni_shared_mlp_workspace": (_sz, [_i, _i, _i]),
+    "omni_atomic_forward_glu": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                     ctypes.POINTER(ScheduleStruct), _vp, _i, _vp, _sz, _vp]),
     "omni_shared_mlp": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
 }
 
@@ -289,6 +292,32 @@ def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, str
     _check("omni_atomic_forward", lib().omni_atomic_forward(
         _dtype_code(x), L, d, N, sched.K, sched.B, _ptr(x), _ptr(w), _ptr(v),
         ctypes.byref(st), _ptr(y), int(bool(accumulate)), code, _ptr(ws),
+        nws if ws is not None else 0, _stream(stream)))
+    return y
+
+
+def atomic_forward_glu(x, w, u, v, sched, y=None, accumulate=False, workspace=None,
+                       stream=None):
+    """omni_atomic_forward_glu (SwiGLU-gated experts): returns y [L, d] float32,
+    y_t = sum_k g silu(x_t . W[e]) (x_t . U[e]) V[e] (y += that if accumulate)."""
+    L, d = x.shape
+    N = w.shape[0]
+    _req(x, "x")
+    for name, t in (("w", w), ("u", u), ("v", v)):
+        _req(t, name, x.dtype, (N, d))
+    if sched.task_index is None:
+        raise ValueError("the schedule must carry task_index")
+    if y is None:
+        y = torch.empty((L, d), dtype=torch.float32, device=x.device)
+    _req(y, "y", torch.float32, (L, d))
+    st = sched.struct()
+    nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B)
+    ws = workspace
+    if nws and (ws is None or ws.numel() < nws):
+        ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+    _check("omni_atomic_forward_glu", lib().omni_atomic_forward_glu(
+        _dtype_code(x), L, d, N, sched.K, sched.B, _ptr(x), _ptr(w), _ptr(u), _ptr(v),
+        ctypes.byref(st), _ptr(y), int(bool(accumulate)), _ptr(ws),
         nws if ws is not None else 0, _stream(stream)))
     return y
 

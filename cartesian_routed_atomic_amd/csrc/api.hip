@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -189,6 +189,32 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                                                 sched->task_token, sched->task_expert,
                                                 sched->task_gate, sched->task_index, y,
                                                 accumulate != 0, ws, stream));
+}
+
+omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, int B,
+                                    const void* x, const void* w, const void* u, const void* v,
+                                    const omni_schedule* sched, float* y, int accumulate,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
+  if (!schedule_args_ok(L, K, N, B) || d < 1) return OMNI_ERR_INVALID_ARG;
+  if (!w || !u || !v || !sched) return OMNI_ERR_INVALID_ARG;
+  const long long M = static_cast<long long>(L) * K;
+  if (L > 0 && (!x || !y)) return OMNI_ERR_INVALID_ARG;
+  if (M > 0 && (!sched->task_expert || !sched->task_gate || !sched->task_index))
+    return OMNI_ERR_INVALID_ARG;
+  const int bf16 = dt == OMNI_BF16;
+  if (!omni::token_centric_supported(bf16, d)) return OMNI_ERR_UNSUPPORTED;
+  if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(u) || !aligned16(v))
+    return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && !aligned16(y)) return OMNI_ERR_INVALID_ARG;
+  if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;
+  if (L == 0) return OMNI_OK;
+  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
+  return hip_status(omni::launch_atomic_forward_glu(bf16, L, d, N, K, x, w, u, v,
+                                                    sched->task_expert, sched->task_gate,
+                                                    sched->task_index, y, accumulate != 0, ws,
+                                                    stream));
 }
 
 size_t omni_routed_backward_workspace(omni_dtype dt, int L, int d, int Nr, int Nc, int K) {

@@ -172,11 +172,38 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const int32_t* __restric
 
 constexpr int kTokRing = 6;  // row slots per wave in the token-centric kernel: five in flight
 
+// h_k = x_t . M[e_k] for the n tasks of a chunk (expert e_k in lane k),
+// streamed through the row ring with kTokRing - 1 rows in flight; h_k ends
+// in lane k.
 template <typename T, int EPL>
+__device__ __forceinline__ float token_dots(const RowFrag<T, EPL>& xf, const T* __restrict__ M,
+                                            int my_e, int n, int d, int l,
+                                            RowFrag<T, EPL> (&f)[kTokRing]) {
+  float my_h = 0.f;
+#pragma unroll
+  for (int s = 0; s < kTokRing - 1; ++s)
+    if (s < n) f[s].load(M + static_cast<size_t>(rdlane(my_e, s)) * d, l);
+  for (int i = 0; i < n; i += kTokRing) {
+#pragma unroll
+    for (int s = 0; s < kTokRing; ++s) {
+      const int ii = i + s;
+      if (ii >= n) break;
+      if (ii + kTokRing - 1 < n)
+        f[(s + kTokRing - 1) % kTokRing].load(
+            M + static_cast<size_t>(rdlane(my_e, ii + kTokRing - 1)) * d, l);
+      const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
+      if (l == ii) my_h = h;
+    }
+  }
+  return my_h;
+}
+
+// GLU: the SwiGLU-gated variant, coefficient g silu(x . W[e]) (x . U[e]).
+template <typename T, int EPL, bool GLU>
 __global__ __launch_bounds__(256, 3) void token_kernel(
-    const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ V,
-    const TokTask* __restrict__ lists, int L, int K, int d, int N, float* __restrict__ y,
-    int accumulate) {
+    const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
+    const T* __restrict__ V, const TokTask* __restrict__ lists, int L, int K, int d, int N,
+    float* __restrict__ y, int accumulate) {
   using Frag = RowFrag<T, EPL>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
@@ -196,24 +223,11 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
       my_e = static_cast<unsigned>(tk.e) < static_cast<unsigned>(N) ? tk.e : 0;
       my_g = tk.g;
     }
-    // pass A: h_k = x_t . W[e_k], kTokRing - 1 rows in flight; h_k ends in lane k
-    float my_h = 0.f;
-#pragma unroll
-    for (int s = 0; s < kTokRing - 1; ++s)
-      if (s < n) f[s].load(W + static_cast<size_t>(rdlane(my_e, s)) * d, l);
-    for (int i = 0; i < n; i += kTokRing) {
-#pragma unroll
-      for (int s = 0; s < kTokRing; ++s) {
-        const int ii = i + s;
-        if (ii >= n) break;
-        if (ii + kTokRing - 1 < n)
-          f[(s + kTokRing - 1) % kTokRing].load(
-              W + static_cast<size_t>(rdlane(my_e, ii + kTokRing - 1)) * d, l);
-        const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
-        if (l == ii) my_h = h;
-      }
-    }
-    const float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
+    // pass A: h_k = x_t . W[e_k]; h_k ends in lane k
+    const float my_h = token_dots<T, EPL>(xf, W, my_e, n, d, l, f);
+    float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
+    // gated variant, pass A': the up factor x_t . U[e_k]
+    if constexpr (GLU) my_c *= token_dots<T, EPL>(xf, U, my_e, n, d, l, f);
     // pass B: y_t += coef_k * V[e_k]
 #pragma unroll
     for (int s = 0; s < kTokRing - 1; ++s)
@@ -300,8 +314,8 @@ size_t atomic_forward_ws_bytes(int L, int K) {
   return 2 * ((m + 255) & ~static_cast<size_t>(255));
 }
 
-template <typename T>
-static bool dispatch_token(const T* x, const T* w, const T* v, const int32_t* te,
+template <typename T, bool GLU>
+static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const int32_t* te,
                            const float* tg, const int32_t* ti, int M, int d, int L, int K, int N,
                            TokTask* lists, float* y, int accumulate, hipStream_t s) {
   unpermute_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(te, tg, ti, M, N,
@@ -309,12 +323,13 @@ static bool dispatch_token(const T* x, const T* w, const T* v, const int32_t* te
   const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
   // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
   switch (d) {
-#define OMNI_TOK(D_, EPL_) case D_: token_kernel<T, EPL_><<<nblk, 256, 0, s>>>(x, w, v, lists, L, K, d, N, y, accumulate); break;
+#define OMNI_TOK(D_, EPL_) case D_: token_kernel<T, EPL_, GLU><<<nblk, 256, 0, s>>>(x, w, u, v, lists, L, K, d, N, y, accumulate); break;
     OMNI_TOK(64, 1) OMNI_TOK(128, 2) OMNI_TOK(256, 4) OMNI_TOK(512, 8) OMNI_TOK(1024, 16)
 #undef OMNI_TOK
     case 2048:
       if constexpr (sizeof(T) == 2) {
-        token_kernel<T, 32><<<nblk, 256, 0, s>>>(x, w, v, lists, L, K, d, N, y, accumulate);
+        token_kernel<T, 32, GLU><<<nblk, 256, 0, s>>>(x, w, u, v, lists, L, K, d, N, y,
+                                                      accumulate);
         break;
       }
       return false;
@@ -357,14 +372,15 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
   if (mode == 2) {
     TokTask* lists = static_cast<TokTask*>(ws);
     if (bf16)
-      ok = dispatch_token<uint16_t>(static_cast<const uint16_t*>(x),
-                                    static_cast<const uint16_t*>(w),
-                                    static_cast<const uint16_t*>(v), task_expert, task_gate,
-                                    task_index, M, d, L, K, N, lists, y, acc, s);
+      ok = dispatch_token<uint16_t, false>(static_cast<const uint16_t*>(x),
+                                           static_cast<const uint16_t*>(w), nullptr,
+                                           static_cast<const uint16_t*>(v), task_expert,
+                                           task_gate, task_index, M, d, L, K, N, lists, y, acc, s);
     else
-      ok = dispatch_token<float>(static_cast<const float*>(x), static_cast<const float*>(w),
-                                 static_cast<const float*>(v), task_expert, task_gate,
-                                 task_index, M, d, L, K, N, lists, y, acc, s);
+      ok = dispatch_token<float, false>(static_cast<const float*>(x),
+                                        static_cast<const float*>(w), nullptr,
+                                        static_cast<const float*>(v), task_expert, task_gate,
+                                        task_index, M, d, L, K, N, lists, y, acc, s);
   } else {
     float* coef = static_cast<float*>(ws);
     int32_t* eflat = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
@@ -379,6 +395,40 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
                                 static_cast<const float*>(v), task_token, task_expert, task_gate,
                                 task_index, M, d, L, K, N, coef, eflat, y, acc, s);
   }
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// SwiGLU-gated variant: token-centric form only (the token's K tasks need
+// both of their input rows before the V pass).
+hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const void* x,
+                                     const void* w, const void* u, const void* v,
+                                     const int32_t* task_expert, const float* task_gate,
+                                     const int32_t* task_index, float* y, bool accumulate,
+                                     void* ws, hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  if (!token_centric_supported(bf16, d)) return hipErrorInvalidValue;
+  const int M = L * K;
+  if (M == 0) {
+    if (!accumulate) {
+      const size_t n4 = static_cast<size_t>(L) * d / 4;
+      zero_f32_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(
+          reinterpret_cast<float4*>(y), n4);
+    }
+    return hipGetLastError();
+  }
+  const int acc = accumulate ? 1 : 0;
+  TokTask* lists = static_cast<TokTask*>(ws);
+  const bool ok =
+      bf16 ? dispatch_token<uint16_t, true>(
+                 static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                 static_cast<const uint16_t*>(u), static_cast<const uint16_t*>(v), task_expert,
+                 task_gate, task_index, M, d, L, K, N, lists, y, acc, s)
+           : dispatch_token<float, true>(static_cast<const float*>(x),
+                                         static_cast<const float*>(w),
+                                         static_cast<const float*>(u),
+                                         static_cast<const float*>(v), task_expert, task_gate,
+                                         task_index, M, d, L, K, N, lists, y, acc, s);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -53,6 +53,12 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
                                  const int32_t* task_expert, const float* task_gate,
                                  const int32_t* task_index, float* y, bool accumulate, void* ws,
                                  hipStream_t s);
+// SwiGLU-gated variant (third matrix u), token-centric form only
+hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const void* x,
+                                     const void* w, const void* u, const void* v,
+                                     const int32_t* task_expert, const float* task_gate,
+                                     const int32_t* task_index, float* y, bool accumulate,
+                                     void* ws, hipStream_t s);
 
 // backward.hip
 size_t routed_backward_ws_bytes(int bf16, int L, int d, int Nr, int Nc, int K);

@@ -62,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 6 */
+int omni_abi_version(void);  /* 7 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -249,6 +249,24 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                                 const omni_schedule* sched, float* y, int accumulate,
                                 omni_exec_mode mode, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * omni_atomic_forward_glu — variant: SwiGLU-gated atomic experts.  The
+ * interactive explainer ("Atomic Expert") names SwiGLU as the expert's
+ * activation while the expert has a single input vector; this variant gives
+ * every expert a third vector, row e of u, and computes
+ *
+ *   y_t = sum_k g_tk * silu(x_t . W[e_tk]) * (x_t . U[e_tk]) * V[e_tk]
+ *
+ * (3d parameters per expert instead of 2d).  Arguments as omni_atomic_forward
+ * plus u [N, d] of dt; the workspace is omni_atomic_forward_workspace(...).
+ * Token-centric form only: requires d = 64 * 2^p with rows of at most 4 KiB
+ * (bf16 d <= 2048, float32 d <= 1024), else UNSUPPORTED.  Deterministic.
+ */
+omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, int B,
+                                    const void* x, const void* w, const void* u, const void* v,
+                                    const omni_schedule* sched, float* y, int accumulate,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * omni_routed_backward — gradients of the routed layer for a given upstream

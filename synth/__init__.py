@@ -26,6 +26,8 @@ Recipe (the same for every workload):
     Wg = 5, Wu = 6, Wd = 7) has hidden width d_ff = 256 * ceil(8 d / 768)
     (two thirds of 4 d, rounded up to a multiple of 256) unless a workload
     fixes it; Wg, Wu [d_ff, d] ~ N(0, 1/d), Wd [d, d_ff] ~ N(0, 1/d_ff).
+  * the gated-expert variant's third expert matrix U [N, d] (tensor id 8)
+    ~ N(0, 1/d) like W and V.
 """
 from __future__ import annotations
 
@@ -36,7 +38,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TENSOR_IDS = {"x": 0, "wr": 1, "wc": 2, "w": 3, "v": 4, "wg": 5, "wu": 6, "wd": 7}
+TENSOR_IDS = {"x": 0, "wr": 1, "wc": 2, "w": 3, "v": 4, "wg": 5, "wu": 6, "wd": 7, "u": 8}
 
 # rows per generation chunk; fixed so the bits never depend on thread count
 _CHUNK_ELEMS = 1 << 22
@@ -152,16 +154,17 @@ def make_inputs(wl: Workload, parts=("x", "wr", "wc", "w", "v"), threads=None) -
     """Generate the named tensors of a workload on the host (numpy).
 
     Returns a dict with any of x [L,d], wr [Nr,d], wc [Nc,d], w [N,d], v [N,d],
-    wg [d_ff,d], wu [d_ff,d], wd [d,d_ff] (float32 or uint16 bf16 bits), plus
+    wg [d_ff,d], wu [d_ff,d], wd [d,d_ff], u [N,d] (float32 or uint16 bf16 bits), plus
     row_bias / col_bias (float32 or None).
     """
     c = wl.index
     sd = 1.0 / math.sqrt(wl.d)
     shapes = {"x": (wl.L, wl.d), "wr": (wl.Nr, wl.d), "wc": (wl.Nc, wl.d),
               "w": (wl.N, wl.d), "v": (wl.N, wl.d),
-              "wg": (wl.d_ff, wl.d), "wu": (wl.d_ff, wl.d), "wd": (wl.d, wl.d_ff)}
+              "wg": (wl.d_ff, wl.d), "wu": (wl.d_ff, wl.d), "wd": (wl.d, wl.d_ff),
+              "u": (wl.N, wl.d)}
     scales = {"x": 1.0, "wr": sd, "wc": sd, "w": sd, "v": sd, "wg": sd, "wu": sd,
-              "wd": 1.0 / math.sqrt(wl.d_ff)}
+              "wd": 1.0 / math.sqrt(wl.d_ff), "u": sd}
     out = {}
     for p in parts:
         out[p] = normal(shapes[p], 1000 * c + TENSOR_IDS[p], scales[p], wl.dtype, threads)

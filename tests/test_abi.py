@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 6
+    assert lib.omni_abi_version() == 7
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -216,3 +216,23 @@ def test_shared_mlp_argument_checks(lib):
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
     # an empty batch needs no x or y and enqueues nothing
     assert call(L=0, x=None, y=None, n=lib.omni_shared_mlp_workspace(1, 0, 256)) == B.OMNI_OK
+
+
+def test_atomic_forward_glu_argument_checks(lib):
+    st = B.ScheduleStruct(*([1 << 20] * 7))
+    f = lib.omni_atomic_forward_glu
+    nws = lib.omni_atomic_forward_workspace(1, 4, 128, 64, 2, 4)
+
+    def call(dt=1, L=4, d=128, N=64, K=2, Bg=4, x=FAKE, u=FAKE, y=FAKE, s=st, ws=FAKE, n=nws):
+        return f(dt, L, d, N, K, Bg, x, FAKE, u, FAKE, ctypes.byref(s) if s is not None else None,
+                 y, 0, ws, n, None)
+    assert call(dt=2) == B.OMNI_ERR_INVALID_ARG
+    assert call(u=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(s=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(x=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(u=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=4096) == B.OMNI_ERR_UNSUPPORTED            # rows over 4 KiB
+    assert call(dt=0, d=2048) == B.OMNI_ERR_UNSUPPORTED
+    assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
+    assert call(L=0, x=None, y=None) == B.OMNI_OK
