@@ -331,6 +331,21 @@ def main():
             lambda: B.schedule_tasks(sel["expert_idx"], sel["gate"], wl.N, wl.B, sched=wsched,
                                      grouping="window"))
         variants["window_groups"] = int(wsched.counts.cpu()[1])
+        # the flat d x N router the Cartesian router replaces: logits for all N
+        # experts, exact top-K over N per token (the pages' "without the
+        # Cartesian router" ablation row)
+        from synth import normal
+        wf = to_dev(normal((wl.N, wl.d), 1000 * wl.index + 9, 1.0 / wl.d ** 0.5, wl.dtype))
+        fr = B.flat_router_topk(x, wf, K)
+        flat_ms = ev_time(lambda: B.flat_router_topk(x, wf, K, out=fr, workspace=fr["workspace"]),
+                          reps=2)
+        product_ms = stages["router"] + stages["topk"]
+        flat_flop = 2.0 * L * wl.d * wl.N
+        variants["flat_router"] = {
+            "ms": flat_ms, "product_router_ms": product_ms, "ratio": flat_ms / product_ms,
+            "gemm_tflops": flat_flop / (flat_ms * 1e-3) / 1e12,
+            "logits_bytes": 4 * L * wl.N}
+        del wf, fr
         say(f"[bench] variants: {json.dumps(variants)}")
 
     cpu = None

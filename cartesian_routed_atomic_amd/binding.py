@@ -19,7 +19,7 @@ OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ER
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -28,7 +28,7 @@ EXPORTS = (
     "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_mode",
     "omni_atomic_forward_workspace", "omni_atomic_forward", "omni_routed_backward_workspace",
     "omni_routed_backward", "omni_shared_mlp_workspace", "omni_shared_mlp",
-    "omni_atomic_forward_glu",
+    "omni_atomic_forward_glu", "omni_flat_router_workspace", "omni_flat_router_topk",
 )
 
 
@@ -63,6 +63,8 @@ _SIGS = {
     "omni_routed_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "omni_routed_backward": (_i, [_i, _i, _i, _i, _i, _i] + [_vp] * 19 + [_sz, _vp]),
     "omni_shared_mlp_workspace": (_sz, [_i, _i, _i]),
+    "omni_flat_router_workspace": (_sz, [_i, _i, _i]),
+    "omni_flat_router_topk": (_i, [_i, _i, _i, _i, _i] + [_vp] * 8 + [_sz, _vp]),
     "omni_atomic_forward_glu": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                      ctypes.POINTER(ScheduleStruct), _vp, _i, _vp, _sz, _vp]),
     "omni_shared_mlp": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -320,6 +322,37 @@ def atomic_forward_glu(x, w, u, v, sched, y=None, accumulate=False, workspace=No
         ctypes.byref(st), _ptr(y), int(bool(accumulate)), _ptr(ws),
         nws if ws is not None else 0, _stream(stream)))
     return y
+
+
+def flat_router_topk(x, wf, K, bias=None, want_logp=False, out=None, workspace=None,
+                     stream=None):
+    """omni_flat_router_topk (the d x N router baseline): returns dict expert_idx,
+    score, gate [L, K] and logp [L, N] (None unless want_logp), workspace."""
+    L, d = x.shape
+    N = wf.shape[0]
+    _req(x, "x")
+    _req(wf, "wf", x.dtype, (N, d))
+    if bias is not None:
+        _req(bias, "bias", torch.float32, (N,))
+    o = dict(out or {})
+    dev = x.device
+    r = {"expert_idx": o.get("expert_idx"), "score": o.get("score"), "gate": o.get("gate")}
+    for name, dt in (("expert_idx", torch.int32), ("score", torch.float32),
+                     ("gate", torch.float32)):
+        if r[name] is None:
+            r[name] = torch.empty((L, K), dtype=dt, device=dev)
+        _req(r[name], name, dt, (L, K))
+    r["logp"] = torch.empty((L, N), dtype=torch.float32, device=dev) if want_logp else None
+    code = _dtype_code(x)
+    nws = lib().omni_flat_router_workspace(code, L, N)
+    ws = workspace
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(max(1, nws), dtype=torch.uint8, device=dev)
+    _check("omni_flat_router_topk", lib().omni_flat_router_topk(
+        code, L, d, N, K, _ptr(x), _ptr(wf), _ptr(bias), _ptr(r["expert_idx"]),
+        _ptr(r["score"]), _ptr(r["gate"]), _ptr(r["logp"]), _ptr(ws), nws, _stream(stream)))
+    r["workspace"] = ws
+    return r
 
 
 def forward(x, wr_t, wc_t, w, v, kprime, K, B, row_bias=None, col_bias=None, stream=None,

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -215,6 +215,34 @@ omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, i
                                                     sched->task_expert, sched->task_gate,
                                                     sched->task_index, y, accumulate != 0, ws,
                                                     stream));
+}
+
+size_t omni_flat_router_workspace(omni_dtype dt, int L, int N) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
+  if (L < 0 || N < 1) return 0;
+  return omni::flat_router_ws_bytes(L, N);
+}
+
+omni_status omni_flat_router_topk(omni_dtype dt, int L, int d, int N, int K, const void* x,
+                                  const void* wf, const float* bias, int32_t* expert_idx,
+                                  float* score, float* gate, float* logp, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
+  if (L < 0 || d < 1 || N < 1 || K < 1 || K > N) return OMNI_ERR_INVALID_ARG;
+  if (!wf) return OMNI_ERR_INVALID_ARG;
+  if (L > 0 && (!x || !expert_idx || !score || !gate)) return OMNI_ERR_INVALID_ARG;
+  if (K > 64) return OMNI_ERR_UNSUPPORTED;
+  // the kernels index rows of wf and of the logits in 64 bits
+  if (!fits_i32(static_cast<long long>(L) * d) || !fits_i32(static_cast<long long>(L) * K))
+    return OMNI_ERR_UNSUPPORTED;
+  if (dt == OMNI_BF16 && d % 8 != 0) return OMNI_ERR_UNSUPPORTED;
+  if (dt == OMNI_F32 && d % 4 != 0) return OMNI_ERR_UNSUPPORTED;
+  if ((L > 0 && !aligned16(x)) || !aligned16(wf)) return OMNI_ERR_INVALID_ARG;
+  const size_t need = omni_flat_router_workspace(dt, L, N);
+  if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
+  if (L == 0) return OMNI_OK;
+  return hip_status(omni::launch_flat_router(dt == OMNI_BF16, L, d, N, K, x, wf, bias,
+                                             expert_idx, score, gate, logp, ws, stream));
 }
 
 size_t omni_routed_backward_workspace(omni_dtype dt, int L, int d, int Nr, int Nc, int K) {

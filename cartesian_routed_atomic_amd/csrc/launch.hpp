@@ -60,6 +60,12 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
                                      const int32_t* task_index, float* y, bool accumulate,
                                      void* ws, hipStream_t s);
 
+// flat_router.hip: the d x N router baseline
+size_t flat_router_ws_bytes(int L, int N);
+hipError_t launch_flat_router(int bf16, int L, int d, int N, int K, const void* x,
+                              const void* wf, const float* bias, int32_t* expert_idx,
+                              float* score, float* gate, float* logp, void* ws, hipStream_t s);
+
 // backward.hip
 size_t routed_backward_ws_bytes(int bf16, int L, int d, int Nr, int Nc, int K);
 bool routed_backward_supported(int bf16, int d, int K);

@@ -62,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 7 */
+int omni_abi_version(void);  /* 8 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -267,6 +267,29 @@ omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, i
                                     const void* x, const void* w, const void* u, const void* v,
                                     const omni_schedule* sched, float* y, int accumulate,
                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * omni_flat_router_topk — variant: the flat router the Cartesian Product
+ * Router replaces (gist.science explainer §2.2: a standard router scores all
+ * N experts with a d x N projection; interactive explainer, ablation table).
+ *
+ *   z = x Wf^T (+ bias);  log p = z - LSE(z) over all N experts;
+ *   top-K by (log p desc, e asc), values compared as float32 numbers;
+ *   gate = softmax over the K selected log p.
+ *
+ * x [L, d] of dt; wf [N, d] of dt (row e: expert e's router weights); bias
+ * [N] float32 or NULL.  Out: expert_idx [L, K] int32, score [L, K] float32
+ * (log p of the selected experts), gate [L, K] float32, in rank order;
+ * logp [L, N] float32 (NULL if not wanted).  ws / ws_bytes: at least
+ * omni_flat_router_workspace(dt, L, N) bytes (the L x N logits), 256-byte
+ * aligned.  Requires 1 <= K <= min(64, N); d a multiple of 8 (bf16) or 4
+ * (float32).  Bit-exact selection for given log p: ties go to the lower id.
+ */
+size_t omni_flat_router_workspace(omni_dtype dt, int L, int N);
+omni_status omni_flat_router_topk(omni_dtype dt, int L, int d, int N, int K, const void* x,
+                                  const void* wf, const float* bias, int32_t* expert_idx,
+                                  float* score, float* gate, float* logp, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /*
  * omni_routed_backward — gradients of the routed layer for a given upstream

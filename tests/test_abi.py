@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 7
+    assert lib.omni_abi_version() == 8
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -236,3 +236,23 @@ def test_atomic_forward_glu_argument_checks(lib):
     assert call(dt=0, d=2048) == B.OMNI_ERR_UNSUPPORTED
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(L=0, x=None, y=None) == B.OMNI_OK
+
+
+def test_flat_router_argument_checks(lib):
+    f = lib.omni_flat_router_topk
+    nws = lib.omni_flat_router_workspace(1, 4, 1000)
+    assert nws >= 4 * 1000 * 4 and nws % 256 == 0
+    assert lib.omni_flat_router_workspace(2, 4, 1000) == 0
+
+    def call(dt=1, L=4, d=128, N=1000, K=8, x=FAKE, wf=FAKE, idx=FAKE, ws=FAKE, n=nws):
+        return f(dt, L, d, N, K, x, wf, None, idx, FAKE, FAKE, None, ws, n, None)
+    assert call(dt=2) == B.OMNI_ERR_INVALID_ARG
+    assert call(K=0) == B.OMNI_ERR_INVALID_ARG
+    assert call(K=1001) == B.OMNI_ERR_INVALID_ARG             # K > N
+    assert call(wf=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(idx=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(wf=MIS) == B.OMNI_ERR_INVALID_ARG
+    assert call(K=65) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=132) == B.OMNI_ERR_UNSUPPORTED
+    assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
+    assert call(L=0, x=None, idx=None, n=lib.omni_flat_router_workspace(1, 0, 1000)) == B.OMNI_OK

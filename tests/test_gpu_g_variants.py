@@ -67,3 +67,55 @@ def test_glu_expert_is_deterministic_and_rejects_unsupported_rows():
                           torch.ones((2, 1), dtype=torch.float32, device="cuda"), 8, 1)
     with pytest.raises(B.OmniError):
         B.atomic_forward_glu(x4, w4, w4, w4, s4)
+
+
+# ------------------------------------------------------------ flat router
+
+from synth import normal  # noqa: E402
+
+FLAT_CASES = {
+    # name: (L, d, N, K, dtype, kind)
+    "tiny_f32": (64, 128, 1024, 8, "f32", "gauss"),
+    "ragged_bf16": (77, 264, 1920, 10, "bf16", "gauss"),
+    "dup_rows": (40, 256, 3000, 16, "bf16", "dup"),        # exact ties: ids e, e+1, e+2 equal
+    "all_equal": (8, 128, 5000, 64, "bf16", "zero"),       # more than 2048 tied: the fallback
+    "quantised_bias": (16, 128, 8192, 33, "f32", "qbias"),  # few distinct values: the fallback
+    "million": (32, 2048, 1 << 20, 64, "bf16", "gauss"),   # the large workload's N
+}
+
+
+def _flat_inputs(L, d, N, dtype, kind, seed):
+    x = normal((L, d), 1000 * seed, 1.0, dtype)
+    if kind == "zero" or kind == "qbias":
+        wf = np.zeros((N, d), np.uint16 if dtype == "bf16" else np.float32)
+    elif kind == "dup":
+        base = normal((N // 3 + 1, d), 1000 * seed + 1, 1 / np.sqrt(d), dtype)
+        wf = np.ascontiguousarray(np.repeat(base, 3, axis=0)[:N])
+    else:
+        wf = normal((N, d), 1000 * seed + 1, 1 / np.sqrt(d), dtype)
+    bias = None
+    if kind == "qbias":
+        bias = (np.round(np.random.default_rng(seed).standard_normal(N)) * 0.5).astype(np.float32)
+    return x, wf, bias
+
+
+@pytest.mark.parametrize("name", list(FLAT_CASES))
+def test_flat_router_parity(name):
+    L, d, N, K, dtype, kind = FLAT_CASES[name]
+    log(f"[flat router] {name}: L={L} d={d} N={N} K={K} {dtype} {kind}")
+    x, wf, bias = _flat_inputs(L, d, N, dtype, kind, seed=600 + len(name))
+    r = B.flat_router_topk(dev(x), dev(wf), K, bias=dev(bias), want_logp=True)
+    torch.cuda.synchronize()
+    logp = host(r["logp"])
+    # selection: bit-exact for the GPU's own log-probabilities
+    idx, score, gate = OV.flat_topk(logp, K)
+    np.testing.assert_array_equal(host(r["expert_idx"]), idx)
+    np.testing.assert_array_equal(host(r["score"]).view(np.uint32), score.view(np.uint32))
+    dg = float(np.abs(host(r["gate"]) - gate).max())
+    assert dg <= 2e-6, dg
+    # log-probabilities against the float64 oracle (a sample of tokens at large N)
+    toks = np.arange(L) if L * N <= 1 << 22 else np.arange(4)
+    want = OV.flat_router_logp(x[toks], wf, bias)
+    dl = float(np.abs(logp[toks] - want).max())
+    log(f"  selection bit-exact; gates max|d| {dg:.1e}; log p max|d| {dl:.1e}")
+    assert dl <= 2e-4
