@@ -156,8 +156,11 @@ def main():
     y = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
     form = B.atomic_forward_mode(x.dtype, L, wl.d, wl.N, K, wl.B)
 
+    router_ws = torch.empty(max(1, B.lib().omni_router_logits_workspace(
+        1 if wl.dtype == "bf16" else 0, L, wl.d, wl.Nr, wl.Nc)), dtype=torch.uint8, device=dev)
+
     def stage_router():
-        B.router_logits(x, wr, wc, rb, cb, row_logits=a, col_logits=b)
+        B.router_logits(x, wr, wc, rb, cb, row_logits=a, col_logits=b, workspace=router_ws)
 
     def stage_topk():
         B.product_topk(a, b, wl.kprime, K, want_sel=False, want_logp=False, out=sel)

@@ -19,11 +19,12 @@ OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ER
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
-    "omni_abi_version", "omni_status_string", "omni_router_logits",
+    "omni_abi_version", "omni_status_string", "omni_router_logits_workspace",
+    "omni_router_logits",
     "omni_product_topk_workspace", "omni_product_topk", "omni_schedule_max_groups",
     "omni_schedule_workspace", "omni_schedule_tasks", "omni_atomic_forward_mode",
     "omni_atomic_forward_workspace", "omni_atomic_forward", "omni_routed_backward_workspace",
@@ -48,7 +49,9 @@ _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
     "omni_abi_version": (_i, []),
     "omni_status_string": (ctypes.c_char_p, [_i]),
-    "omni_router_logits": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "omni_router_logits_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "omni_router_logits": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                _vp]),
     "omni_product_topk_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "omni_product_topk": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _sz, _vp]),
@@ -130,7 +133,7 @@ def _req(t, name, dtype=None, shape=None):
 
 
 def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None, row_logits=None,
-                  col_logits=None, stream=None):
+                  col_logits=None, workspace=None, stream=None):
     """omni_router_logits: returns (row_logits [L,Nr], col_logits [L,Nc]) float32."""
     L, d = x.shape
     Nr, Nc = wr_t.shape[0], wc_t.shape[0]
@@ -146,9 +149,14 @@ def router_logits(x, wr_t, wc_t, row_bias=None, col_bias=None, row_logits=None,
         col_logits = torch.empty((L, Nc), dtype=torch.float32, device=x.device)
     _req(row_logits, "row_logits", torch.float32, (L, Nr))
     _req(col_logits, "col_logits", torch.float32, (L, Nc))
+    nws = lib().omni_router_logits_workspace(_dtype_code(x), L, d, Nr, Nc)
+    ws = workspace
+    if nws and (ws is None or ws.numel() < nws):
+        ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
     _check("omni_router_logits", lib().omni_router_logits(
         _dtype_code(x), L, d, Nr, Nc, _ptr(x), _ptr(wr_t), _ptr(wc_t), _ptr(row_bias),
-        _ptr(col_bias), _ptr(row_logits), _ptr(col_logits), _stream(stream)))
+        _ptr(col_bias), _ptr(row_logits), _ptr(col_logits), _ptr(ws) if nws else None, nws,
+        _stream(stream)))
     return row_logits, col_logits
 
 

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -33,10 +33,17 @@ const char* omni_status_string(omni_status s) {
   }
 }
 
+size_t omni_router_logits_workspace(omni_dtype dt, int L, int d, int Nr, int Nc) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
+  if (L < 0 || d < 1 || Nr < 1 || Nc < 1) return 0;
+  if (!fits_i32(static_cast<long long>(L) * (Nr + static_cast<long long>(Nc)))) return 0;
+  return omni::router_ws_bytes(dt == OMNI_BF16, L, d, Nr, Nc);
+}
+
 omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc, const void* x,
                                const void* wr_t, const void* wc_t, const float* row_bias,
                                const float* col_bias, float* row_logits, float* col_logits,
-                               hipStream_t stream) {
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
   if (L < 0 || d < 1 || Nr < 1 || Nc < 1) return OMNI_ERR_INVALID_ARG;
   if (!wr_t || !wc_t) return OMNI_ERR_INVALID_ARG;
@@ -49,12 +56,15 @@ omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc, cons
     return OMNI_ERR_INVALID_ARG;
   if (dt == OMNI_BF16 && d % 8 != 0) return OMNI_ERR_UNSUPPORTED;
   if (dt == OMNI_F32 && d % 4 != 0) return OMNI_ERR_UNSUPPORTED;
+  const size_t need = omni_router_logits_workspace(dt, L, d, Nr, Nc);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
   if (L == 0) return OMNI_OK;
   hipError_t e;
   if (dt == OMNI_BF16)
     e = omni::launch_router_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr_t),
                                  static_cast<const uint16_t*>(wc_t), row_bias, col_bias,
-                                 row_logits, col_logits, L, d, Nr, Nc, stream);
+                                 row_logits, col_logits, L, d, Nr, Nc, need > 0 ? ws : nullptr,
+                                 stream);
   else
     e = omni::launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(wr_t),
                                 static_cast<const float*>(wc_t), row_bias, col_bias, row_logits,

@@ -235,7 +235,7 @@ hipError_t launch_flat_router(int bf16, int L, int d, int N, int K, const void* 
   const hipError_t e =
       bf16 ? launch_router_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wf),
                                 static_cast<const uint16_t*>(wf), bias, nullptr, z, z, L, d, N,
-                                0, s)
+                                0, nullptr, s)
            : launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(wf),
                                static_cast<const float*>(wf), bias, nullptr, z, z, L, d, N, 0, s);
   if (e != hipSuccess) return e;

@@ -8,9 +8,11 @@
 namespace omni {
 
 // router.hip
+// ws: split-K partials (router_ws_bytes of them); NULL runs without a split
+size_t router_ws_bytes(int bf16, int L, int d, int Nr, int Nc);
 hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
                               const float* rb, const float* cb, float* zr, float* zc,
-                              int L, int d, int Nr, int Nc, hipStream_t s);
+                              int L, int d, int Nr, int Nc, void* ws, hipStream_t s);
 hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
                              const float* rb, const float* cb, float* zr, float* zc,
                              int L, int d, int Nr, int Nc, hipStream_t s);

@@ -30,6 +30,9 @@ constexpr int RBM = 128, RBN = 128, RBK = 64, RLD = RBK + 8;
 // same 16 hidden units, so one lane holds both halves of a hidden unit in
 // its tiles j and j + 1.
 constexpr int kEpiLogits = 0, kEpiSwiglu = 1;
+// Split-K partial: the raw accumulators of K range blockIdx.y, no bias, into
+// zr + blockIdx.y * L * (Nr + Nc) (summed in order by splitk_reduce_kernel).
+constexpr int kEpiPartial = 2;
 
 __device__ __forceinline__ int swiglu_hidden(int n) { return ((n >> 5) << 4) | (n & 15); }
 
@@ -45,7 +48,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wc, const float* __restrict__ rb,
     const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
-    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out, uint16_t* __restrict__ hout) {
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out, uint16_t* __restrict__ hout,
+    int ksplit) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[RBM * RLD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[RBN * RLD];
 
@@ -60,6 +64,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   const int mt = logical / n_nt, nt = logical - mt * n_nt;
   const int m0 = mt * RBM, n0 = nt * RBN;
   const int NT = Nr + Nc;
+  // K range of this workgroup: all of K, or split-K chunk blockIdx.y
+  const int kb = blockIdx.y * ksplit, ke = min(d, kb + ksplit);
 
   // global -> register staging: 4 x 16 B of A and of B per thread
   const uint16_t* arow[4];
@@ -85,8 +91,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = k0 + ach[i];
-      ra[i] = (arow[i] && k < d) ? *reinterpret_cast<const uint4*>(arow[i] + k) : make_uint4(0, 0, 0, 0);
-      rbv[i] = (brow[i] && k < d) ? *reinterpret_cast<const uint4*>(brow[i] + k) : make_uint4(0, 0, 0, 0);
+      ra[i] = (arow[i] && k < ke) ? *reinterpret_cast<const uint4*>(arow[i] + k) : make_uint4(0, 0, 0, 0);
+      rbv[i] = (brow[i] && k < ke) ? *reinterpret_cast<const uint4*>(brow[i] + k) : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -99,8 +105,8 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   const int wm = wv >> 1, wn = wv & 1;
   const int fr = l & 15, fk = (l >> 4) * 8;
 
-  gload(0);
-  for (int k0 = 0; k0 < d; k0 += RBK) {
+  gload(kb);
+  for (int k0 = kb; k0 < ke; k0 += RBK) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
       *reinterpret_cast<uint4*>(&sB[row * RLD + ach[i]]) = rbv[i];
     }
     __syncthreads();
-    if (k0 + RBK < d) gload(k0 + RBK);
+    if (k0 + RBK < ke) gload(k0 + RBK);
 #pragma unroll
     for (int kk = 0; kk < RBK; kk += 32) {
       bf16x8 af[4], bfr[4];
@@ -144,6 +150,22 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
           if (t < L)
             hout[static_cast<size_t>(t) * Nr + h] =
                 swiglu_bf16(acc[i][2 * jp][q], acc[i][2 * jp + 1][q]);
+        }
+    }
+    return;
+  }
+  if constexpr (EPI == kEpiPartial) {
+    float* part = zr + static_cast<size_t>(blockIdx.y) * L * NT;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + j * 16 + fr;
+      if (n >= NT) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + q;
+          if (t < L) part[static_cast<size_t>(t) * NT + n] = acc[i][j][q];
         }
     }
     return;
@@ -412,19 +434,75 @@ __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
   *out = s + (n < Nr ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f)) + (acc_out ? *out : 0.f);
 }
 
+// Split-K count for the router product (1 = no split): shapes whose 128 x 128
+// tiles number well under one per CU (few tokens, or few grid lines) split
+// K so that about 256 workgroups run; chunks are multiples of 64 and at
+// least 256 long.
+static bool router_big(int L, int d, int NT) {
+  return d % GBK == 0 && ((L + GBM - 1) / GBM) * ((NT + GBN - 1) / GBN) >= 192;
+}
+
+int router_split_count(int L, int d, int NT) {
+  if (L <= 0 || router_big(L, d, NT)) return 1;
+  const int tiles = ((L + RBM - 1) / RBM) * ((NT + RBN - 1) / RBN);
+  if (tiles >= 192) return 1;
+  int S = (256 + tiles - 1) / tiles;
+  const int max_s = d / 256;
+  if (S > max_s) S = max_s;
+  if (S <= 1) return 1;
+  const int chunk = ((d + S - 1) / S + RBK - 1) / RBK * RBK;
+  return (d + chunk - 1) / chunk;
+}
+
+size_t router_ws_bytes(int bf16, int L, int d, int Nr, int Nc) {
+  if (!bf16) return 0;
+  const int S = router_split_count(L, d, Nr + Nc);
+  return S > 1 ? static_cast<size_t>(S) * L * (Nr + Nc) * 4 : 0;
+}
+
+// z[t, n] = bias[n] + sum over the S partials of (t, n), in partial order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
+                                                            int L, int Nr, int Nc,
+                                                            const float* __restrict__ rb,
+                                                            const float* __restrict__ cb,
+                                                            float* __restrict__ zr,
+                                                            float* __restrict__ zc) {
+  const int NT = Nr + Nc;
+  const size_t total = static_cast<size_t>(L) * NT;
+  const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= total) return;
+  const int t = static_cast<int>(id / NT), n = static_cast<int>(id - static_cast<size_t>(t) * NT);
+  float v = 0.f;
+  for (int z = 0; z < S; ++z) v += part[static_cast<size_t>(z) * total + id];
+  if (n < Nr) zr[static_cast<size_t>(t) * Nr + n] = v + (rb ? rb[n] : 0.f);
+  else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = v + (cb ? cb[n - Nr] : 0.f);
+}
+
 hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
                               const float* rb, const float* cb, float* zr, float* zc, int L,
-                              int d, int Nr, int Nc, hipStream_t s) {
+                              int d, int Nr, int Nc, void* ws, hipStream_t s) {
   if (L == 0) return hipSuccess;
-  if (d % GBK == 0) {
-    const int n_mt = (L + GBM - 1) / GBM, n_nt = (Nr + Nc + GBN - 1) / GBN;
+  const int NT = Nr + Nc;
+  if (router_big(L, d, NT)) {
+    const int n_mt = (L + GBM - 1) / GBM, n_nt = (NT + GBN - 1) / GBN;
     router_gemm_bf16_big_kernel<kEpiLogits><<<n_mt * n_nt, 512, 0, s>>>(
         x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr);
     return hipGetLastError();
   }
-  const int n_mt = (L + RBM - 1) / RBM, n_nt = (Nr + Nc + RBN - 1) / RBN;
+  const int n_mt = (L + RBM - 1) / RBM, n_nt = (NT + RBN - 1) / RBN;
+  const int S = ws ? router_split_count(L, d, NT) : 1;
+  if (S > 1) {
+    const int chunk = ((d + S - 1) / S + RBK - 1) / RBK * RBK;
+    float* part = static_cast<float*>(ws);
+    router_gemm_bf16_kernel<kEpiPartial><<<dim3(n_mt * n_nt, S), 256, 0, s>>>(
+        x, wr, wc, nullptr, nullptr, part, part, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr, chunk);
+    const size_t n = static_cast<size_t>(L) * NT;
+    splitk_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+        part, S, L, Nr, Nc, rb, cb, zr, zc);
+    return hipGetLastError();
+  }
   router_gemm_bf16_kernel<kEpiLogits><<<n_mt * n_nt, 256, 0, s>>>(
-      x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr);
+      x, wr, wc, rb, cb, zr, zc, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr, d);
   return hipGetLastError();
 }
 
@@ -455,7 +533,7 @@ hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int 
     } else {
       const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
       router_gemm_bf16_kernel<kEpiLogits><<<n_mt * n_nt, 256, 0, s>>>(
-          pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, n_mt, n_nt, accumulate, nullptr);
+          pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, n_mt, n_nt, accumulate, nullptr, K);
     }
   } else {
     const size_t n = static_cast<size_t>(M) * N;
@@ -504,7 +582,7 @@ hipError_t launch_swiglu_up(int bf16, const void* x, const void* wg, const void*
     } else {
       const int n_mt = (L + RBM - 1) / RBM, n_nt = (n_log + RBN - 1) / RBN;
       router_gemm_bf16_kernel<kEpiSwiglu><<<n_mt * n_nt, 256, 0, s>>>(
-          px, pg, pu, nullptr, nullptr, nullptr, nullptr, L, d, d_ff, 0, n_mt, n_nt, 0, ph);
+          px, pg, pu, nullptr, nullptr, nullptr, nullptr, L, d, d_ff, 0, n_mt, n_nt, 0, ph, d);
     }
   } else {
     const size_t n = static_cast<size_t>(L) * d_ff;

@@ -62,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 8 */
+int omni_abi_version(void);  /* 9 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -83,14 +83,20 @@ const char* omni_status_string(omni_status s);
  * wc_t        [Nc, d] of dt, likewise for grid columns.
  * row_bias    [Nr] float32 or NULL;  col_bias [Nc] float32 or NULL.
  * row_logits  [L, Nr] float32 out;   col_logits [L, Nc] float32 out.
+ * ws          workspace of at least omni_router_logits_workspace(...) bytes,
+ *             256-byte aligned, or NULL with ws_bytes 0 when that is 0.  Shapes
+ *             with few tokens or few grid lines split the contraction over d
+ *             (partial products summed in a fixed order, so the result is
+ *             deterministic); the workspace holds the partials.
  * Requires L >= 0, d >= 1, Nr >= 1, Nc >= 1; for bf16 d % 8 == 0 and
  * x, wr_t, wc_t 16-byte aligned; for f32 d % 4 == 0 and 16-byte aligned.
  */
+size_t omni_router_logits_workspace(omni_dtype dt, int L, int d, int Nr, int Nc);
 omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc,
                                const void* x, const void* wr_t, const void* wc_t,
                                const float* row_bias, const float* col_bias,
-                               float* row_logits, float* col_logits,
-                               hipStream_t stream);
+                               float* row_logits, float* col_logits, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /*
  * omni_product_topk — per-axis log-probabilities, top-K over the product

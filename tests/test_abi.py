@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 8
+    assert lib.omni_abi_version() == 9
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -55,8 +55,9 @@ def test_router_argument_checks(lib):
     f = lib.omni_router_logits
     ok_args = dict(dt=B.OMNI_BF16, L=4, d=64, Nr=8, Nc=8)
 
-    def call(dt=1, L=4, d=64, Nr=8, Nc=8, x=FAKE, wr=FAKE, wc=FAKE, rl=FAKE, cl=FAKE):
-        return f(dt, L, d, Nr, Nc, x, wr, wc, None, None, rl, cl, None)
+    def call(dt=1, L=4, d=64, Nr=8, Nc=8, x=FAKE, wr=FAKE, wc=FAKE, rl=FAKE, cl=FAKE, ws=None,
+             n=0):
+        return f(dt, L, d, Nr, Nc, x, wr, wc, None, None, rl, cl, ws, n, None)
     assert ok_args
     assert call(dt=7) == B.OMNI_ERR_INVALID_ARG
     assert call(L=-1) == B.OMNI_ERR_INVALID_ARG
@@ -68,6 +69,15 @@ def test_router_argument_checks(lib):
     assert call(dt=0, d=66) == B.OMNI_ERR_UNSUPPORTED    # f32 needs d % 4 == 0
     assert call(L=1 << 30, d=64) == B.OMNI_ERR_UNSUPPORTED
     assert call(L=0) == B.OMNI_OK                        # empty batch: nothing enqueued
+    # few tokens: the contraction over d is split and the partials need a workspace
+    nws = lib.omni_router_logits_workspace(1, 256, 2048, 1024, 1024)
+    assert nws == 8 * 256 * 2048 * 4                     # 8 chunks of 256 features
+    assert lib.omni_router_logits_workspace(1, 8192, 2048, 1024, 1024) == 0   # enough tiles
+    assert lib.omni_router_logits_workspace(0, 256, 2048, 1024, 1024) == 0    # float32 path
+    assert call(L=256, d=2048, Nr=1024, Nc=1024) == B.OMNI_ERR_WORKSPACE
+    assert call(L=256, d=2048, Nr=1024, Nc=1024, ws=FAKE, n=nws - 1) == B.OMNI_ERR_WORKSPACE
+    assert call(L=256, d=2048, Nr=1024, Nc=1024, ws=ctypes.c_void_p((1 << 20) + 16),
+                n=nws) == B.OMNI_ERR_WORKSPACE
 
 
 def test_product_topk_argument_checks(lib):

@@ -347,10 +347,15 @@ def test_executor_more_than_64_tasks_per_token(K):
     np.testing.assert_array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("L,d,Nr,Nc", [(77, 40, 24, 40), (300, 200, 96, 33), (513, 2048, 300, 260)])
+@pytest.mark.parametrize("L,d,Nr,Nc", [(77, 40, 24, 40), (300, 200, 96, 33), (513, 2048, 300, 260),
+                                       (77, 1024, 48, 40), (300, 2048, 64, 64),
+                                       (256, 2048, 1024, 1024), (129, 776, 70, 90)])
 def test_router_logits_ragged_shapes(L, d, Nr, Nc):
     # Token and grid-line counts that leave partial tiles, and feature widths
-    # on both bf16 GEMM paths (d % 32 != 0 and d % 32 == 0).
+    # on both bf16 GEMM paths (d % 32 != 0 and d % 32 == 0); the last four
+    # shapes have few tiles, so the contraction is split over d (2 to 8
+    # chunks, the last one short for d = 776).
+    log(f"[router] split into {B.lib().omni_router_logits_workspace(1, L, d, Nr, Nc) // (4 * L * (Nr + Nc))} chunks")
     wl = custom(L=L, d=d, Nr=Nr, Nc=Nc, kprime=4, K=4, B=4, dtype="bf16", index=300 + d)
     inp = make_inputs(wl, ("x", "wr", "wc"))
     rb = (np.arange(Nr, dtype=np.float32) * 0.01).astype(np.float32)
