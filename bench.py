@@ -283,7 +283,7 @@ def main():
                if k in ("wg", "wu", "wd")}
         d_ff = wl.d_ff
         mlp_ws = torch.empty(max(1, B.lib().omni_shared_mlp_workspace(
-            1 if wl.dtype == "bf16" else 0, L, d_ff)), dtype=torch.uint8, device=dev)
+            1 if wl.dtype == "bf16" else 0, L, wl.d, d_ff)), dtype=torch.uint8, device=dev)
         y_layer = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
 
         def shared():

@@ -19,7 +19,7 @@ OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ER
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -65,7 +65,7 @@ _SIGS = {
                                  ctypes.POINTER(ScheduleStruct), _vp, _i, _i, _vp, _sz, _vp]),
     "omni_routed_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
     "omni_routed_backward": (_i, [_i, _i, _i, _i, _i, _i] + [_vp] * 19 + [_sz, _vp]),
-    "omni_shared_mlp_workspace": (_sz, [_i, _i, _i]),
+    "omni_shared_mlp_workspace": (_sz, [_i, _i, _i, _i]),
     "omni_flat_router_workspace": (_sz, [_i, _i, _i]),
     "omni_flat_router_topk": (_i, [_i, _i, _i, _i, _i] + [_vp] * 8 + [_sz, _vp]),
     "omni_atomic_forward_glu": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
@@ -387,7 +387,7 @@ def shared_mlp(x, w_gate, w_up, w_down, y=None, accumulate=False, workspace=None
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
     _req(y, "y", torch.float32, (L, d))
     code = _dtype_code(x)
-    nws = lib().omni_shared_mlp_workspace(code, L, d_ff)
+    nws = lib().omni_shared_mlp_workspace(code, L, d, d_ff)
     ws = workspace
     if ws is None or ws.numel() < nws:
         ws = torch.empty(max(1, nws), dtype=torch.uint8, device=x.device)

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -289,11 +289,16 @@ omni_status omni_routed_backward(omni_dtype dt, int L, int d, int Nr, int Nc, in
       dwc_t, drow_bias, dcol_bias, counts, active, dw, dv, dgate, ws, stream));
 }
 
-size_t omni_shared_mlp_workspace(omni_dtype dt, int L, int d_ff) {
-  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
-  if (L < 0 || d_ff < 1 || !fits_i32(static_cast<long long>(L) * d_ff)) return 0;
+// The hidden activation, then the split-K partials of the down product.
+static size_t mlp_hidden_bytes(omni_dtype dt, int L, int d_ff) {
   const size_t n = static_cast<size_t>(L > 0 ? L : 1) * d_ff * (dt == OMNI_BF16 ? 2 : 4);
   return (n + 255) & ~static_cast<size_t>(255);
+}
+
+size_t omni_shared_mlp_workspace(omni_dtype dt, int L, int d, int d_ff) {
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
+  if (L < 0 || d < 1 || d_ff < 1 || !fits_i32(static_cast<long long>(L) * d_ff)) return 0;
+  return mlp_hidden_bytes(dt, L, d_ff) + omni::gemm_nt_ws_bytes(dt == OMNI_BF16, L, d, d_ff);
 }
 
 omni_status omni_shared_mlp(omni_dtype dt, int L, int d, int d_ff, const void* x,
@@ -311,13 +316,17 @@ omni_status omni_shared_mlp(omni_dtype dt, int L, int d, int d_ff, const void* x
   const void* rows[] = {x, w_gate, w_up, w_down, y};
   for (const void* p : rows)
     if (p && !aligned16(p)) return OMNI_ERR_INVALID_ARG;
-  const size_t need = omni_shared_mlp_workspace(dt, L, d_ff);
+  const size_t need = omni_shared_mlp_workspace(dt, L, d, d_ff);
   if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
   if (L == 0) return OMNI_OK;
   const int bf16 = dt == OMNI_BF16;
   hipError_t e = omni::launch_swiglu_up(bf16, x, w_gate, w_up, ws, L, d, d_ff, stream);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(omni::launch_gemm_nt(bf16, ws, w_down, y, L, d, d_ff, accumulate, stream));
+  void* part = omni::gemm_nt_ws_bytes(bf16, L, d, d_ff) > 0
+                   ? static_cast<char*>(ws) + mlp_hidden_bytes(dt, L, d_ff)
+                   : nullptr;
+  return hip_status(omni::launch_gemm_nt(bf16, ws, w_down, y, L, d, d_ff, accumulate, part,
+                                         stream));
 }
 
 }  // extern "C"

@@ -445,7 +445,7 @@ static SchedBufs sched_bufs(size_t& o, int L, int K, int N) {
 
 namespace {
 struct BwdLayout {
-  size_t bytes, coef, dh, ds, part, dzt, dzt16, xt, cgrad, dz, wrct;
+  size_t bytes, coef, dh, ds, part, dzt, dzt16, xt, cgrad, dz, wrct, gpart;
   int Lp;        // tokens padded to a multiple of 64 (inner dimension of the dWr, dWc product)
   int Rp;        // grid rows + columns padded to a multiple of 64 (that of the dx product)
   SchedBufs es;  // experts, groups of one (the caller's counts / active)
@@ -472,6 +472,10 @@ static BwdLayout bwd_layout(int L, int d, int Nr, int Nc, int K, int bf16) {
   w.Rp = static_cast<int>((nrc + 63) / 64 * 64);
   w.dz = o;    o = a256(o + static_cast<size_t>(L > 0 ? L : 1) * w.Rp * es);
   w.wrct = o;  o = a256(o + static_cast<size_t>(d) * w.Rp * es);
+  // split-K partials of the two router products (they run one after the other)
+  const size_t g1 = gemm_nt_ws_bytes(bf16, L, d, w.Rp);
+  const size_t g2 = gemm_nt_ws_bytes(bf16, static_cast<int>(nrc), d, w.Lp);
+  w.gpart = o; o = a256(o + (g1 > g2 ? g1 : g2));
   const long long N = static_cast<long long>(Nr) * Nc;
   w.es = sched_bufs(o, L, K, static_cast<int>(N));
   w.bytes = o;
@@ -521,7 +525,9 @@ static hipError_t launch_bwd_t(const T* x, const T* wr, const T* wc, const T* w,
         x, w, v, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate, dzt, Lp, dz,
         Rp);
   // router part of dx: dx += [dz_r dz_c] [Wr; Wc], one MFMA product
-  hipError_t e = launch_gemm_nt(bf16, dz, wrct, dx, L, d, Rp, 1, s);
+  void* gpart = ws + lay.gpart;
+  hipError_t e = launch_gemm_nt(bf16, dz, wrct, dx, L, d, Rp, 1,
+                                gemm_nt_ws_bytes(bf16, L, d, Rp) ? gpart : nullptr, s);
   if (e != hipSuccess) return e;
   // router weights: [dWr; dWc] = dz^T x, one MFMA product over the padded tokens
   dz_rows_kernel<<<static_cast<unsigned>((NRC + 3) / 4), 256, 0, s>>>(dzt, NRC, Lp, Nr, dzt16,
@@ -530,7 +536,8 @@ static hipError_t launch_bwd_t(const T* x, const T* wr, const T* wc, const T* w,
                                  static_cast<unsigned>((d + 63) / 64)), 256, 0, s>>>(
       x, L, nullptr, 0, d, Lp, xt);
   e = launch_gemm_nt(bf16, bf16 ? static_cast<const void*>(dzt16) : static_cast<const void*>(dzt),
-                     xt, cgrad, NRC, d, Lp, 0, s);
+                     xt, cgrad, NRC, d, Lp, 0,
+                     gemm_nt_ws_bytes(bf16, NRC, d, Lp) ? gpart : nullptr, s);
   if (e != hipSuccess) return e;
   e = hipMemcpyAsync(dwr, cgrad, static_cast<size_t>(Nr) * d * 4, hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return e;

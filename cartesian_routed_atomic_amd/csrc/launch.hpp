@@ -18,8 +18,11 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc,
                              int L, int d, int Nr, int Nc, hipStream_t s);
 // c[M, N] (+)= a[M, K] b[N, K]^T, row-major, fp32 accumulation; a, b bf16
 // bits (bf16 != 0, K a multiple of 8) or float32 (K a multiple of 4).
+// ws: split-K partials for shapes with few tiles (gemm_nt_ws_bytes of them),
+// or NULL to run without a split.
+size_t gemm_nt_ws_bytes(int bf16, int M, int N, int K);
 hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
-                          int accumulate, hipStream_t s);
+                          int accumulate, void* ws, hipStream_t s);
 // h[L, d_ff] = silu(x Wg^T) * (x Wu^T); x [L, d], wg / wu [d_ff, d]; h is bf16
 // bits (bf16 != 0, d a multiple of 8) or float32 (d a multiple of 4).
 hipError_t launch_swiglu_up(int bf16, const void* x, const void* wg, const void* wu, void* h,

@@ -460,13 +460,14 @@ size_t router_ws_bytes(int bf16, int L, int d, int Nr, int Nc) {
   return S > 1 ? static_cast<size_t>(S) * L * (Nr + Nc) * 4 : 0;
 }
 
-// z[t, n] = bias[n] + sum over the S partials of (t, n), in partial order.
+// z[t, n] = bias[n] + sum over the S partials of (t, n), in partial order
+// (added to z as it stands when acc_out).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
                                                             int L, int Nr, int Nc,
                                                             const float* __restrict__ rb,
                                                             const float* __restrict__ cb,
                                                             float* __restrict__ zr,
-                                                            float* __restrict__ zc) {
+                                                            float* __restrict__ zc, int acc_out) {
   const int NT = Nr + Nc;
   const size_t total = static_cast<size_t>(L) * NT;
   const size_t id = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -474,8 +475,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int t = static_cast<int>(id / NT), n = static_cast<int>(id - static_cast<size_t>(t) * NT);
   float v = 0.f;
   for (int z = 0; z < S; ++z) v += part[static_cast<size_t>(z) * total + id];
-  if (n < Nr) zr[static_cast<size_t>(t) * Nr + n] = v + (rb ? rb[n] : 0.f);
-  else zc[static_cast<size_t>(t) * Nc + (n - Nr)] = v + (cb ? cb[n - Nr] : 0.f);
+  float* out = n < Nr ? zr + static_cast<size_t>(t) * Nr + n
+                      : zc + static_cast<size_t>(t) * Nc + (n - Nr);
+  *out = v + (n < Nr ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f)) + (acc_out ? *out : 0.f);
 }
 
 hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,
@@ -498,7 +500,7 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint1
         x, wr, wc, nullptr, nullptr, part, part, L, d, Nr, Nc, n_mt, n_nt, 0, nullptr, chunk);
     const size_t n = static_cast<size_t>(L) * NT;
     splitk_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-        part, S, L, Nr, Nc, rb, cb, zr, zc);
+        part, S, L, Nr, Nc, rb, cb, zr, zc, 0);
     return hipGetLastError();
   }
   router_gemm_bf16_kernel<kEpiLogits><<<n_mt * n_nt, 256, 0, s>>>(
@@ -519,19 +521,34 @@ hipError_t launch_router_f32(const float* x, const float* wr, const float* wc, c
 // C[m][n] = sum_k A[m][k] B[n][k] (A [M, K], B [N, K], C [M, N] float32, all
 // row-major): the 128 x 128 MFMA kernel (bf16, K a multiple of 8) or the
 // float32 kernel, used as plain products by the backward pass.
+size_t gemm_nt_ws_bytes(int bf16, int M, int N, int K) {
+  if (!bf16 || M <= 0 || N <= 0) return 0;
+  const int S = router_split_count(M, K, N);
+  return S > 1 ? static_cast<size_t>(S) * M * N * 4 : 0;
+}
+
 hipError_t launch_gemm_nt(int bf16, const void* a, const void* b, float* c, int M, int N, int K,
-                          int accumulate, hipStream_t s) {
+                          int accumulate, void* ws, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (bf16) {
     const uint16_t* pa = static_cast<const uint16_t*>(a);
     const uint16_t* pb = static_cast<const uint16_t*>(b);
-    const int big_tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
-    if (K % GBK == 0 && big_tiles >= 192) {  // the large tile only where it still fills the chip
-      router_gemm_bf16_big_kernel<kEpiLogits><<<big_tiles, 512, 0, s>>>(
+    const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
+    const int S = ws ? router_split_count(M, K, N) : 1;
+    if (router_big(M, K, N)) {  // the large tile only where it still fills the chip
+      router_gemm_bf16_big_kernel<kEpiLogits><<<((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN),
+                                               512, 0, s>>>(
           pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, (M + GBM - 1) / GBM,
           (N + GBN - 1) / GBN, accumulate, nullptr);
+    } else if (S > 1) {  // few tiles: split K, partials summed in order
+      const int chunk = ((K + S - 1) / S + RBK - 1) / RBK * RBK;
+      float* part = static_cast<float*>(ws);
+      router_gemm_bf16_kernel<kEpiPartial><<<dim3(n_mt * n_nt, S), 256, 0, s>>>(
+          pa, pb, pb, nullptr, nullptr, part, part, M, K, N, 0, n_mt, n_nt, 0, nullptr, chunk);
+      const size_t n = static_cast<size_t>(M) * N;
+      splitk_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+          part, S, M, N, 0, nullptr, nullptr, c, c, accumulate);
     } else {
-      const int n_mt = (M + RBM - 1) / RBM, n_nt = (N + RBN - 1) / RBN;
       router_gemm_bf16_kernel<kEpiLogits><<<n_mt * n_nt, 256, 0, s>>>(
           pa, pb, pb, nullptr, nullptr, c, c, M, K, N, 0, n_mt, n_nt, accumulate, nullptr, K);
     }

@@ -62,7 +62,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 9 */
+int omni_abi_version(void);  /* 10 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -353,12 +353,13 @@ omni_status omni_routed_backward(omni_dtype dt, int L, int d, int Nr, int Nc, in
  * its accumulate flag after this one).  The bf16 path runs both products on
  * MFMA with fp32 accumulation and keeps the hidden activation in bf16; the
  * float32 path computes it in float32.
- * ws / ws_bytes: at least omni_shared_mlp_workspace(dt, L, d_ff) bytes,
- * 256-byte aligned (the hidden activation, L * d_ff elements of dt).
+ * ws / ws_bytes: at least omni_shared_mlp_workspace(dt, L, d, d_ff) bytes,
+ * 256-byte aligned (the hidden activation, L * d_ff elements of dt, and for
+ * few tokens the split-K partials of the down product).
  * Requires d and d_ff multiples of 8 (bf16) or 4 (float32), else
  * UNSUPPORTED; 16-byte aligned arrays.  Deterministic.
  */
-size_t omni_shared_mlp_workspace(omni_dtype dt, int L, int d_ff);
+size_t omni_shared_mlp_workspace(omni_dtype dt, int L, int d, int d_ff);
 omni_status omni_shared_mlp(omni_dtype dt, int L, int d, int d_ff, const void* x,
                             const void* w_gate, const void* w_up, const void* w_down, float* y,
                             int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);

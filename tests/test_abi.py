@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 9
+    assert lib.omni_abi_version() == 10
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -203,11 +203,14 @@ def test_routed_backward_argument_checks(lib):
 
 def test_shared_mlp_argument_checks(lib):
     f = lib.omni_shared_mlp
-    nws = lib.omni_shared_mlp_workspace(1, 4, 256)
-    assert nws == 4 * 256 * 2
-    assert lib.omni_shared_mlp_workspace(0, 4, 256) == 4 * 256 * 4
-    assert lib.omni_shared_mlp_workspace(1, 4, 0) == 0
-    assert lib.omni_shared_mlp_workspace(2, 4, 256) == 0
+    nws = lib.omni_shared_mlp_workspace(1, 4, 128, 256)
+    assert nws == 4 * 256 * 2                 # the hidden activation; no split over d_ff = 256
+    assert lib.omni_shared_mlp_workspace(0, 4, 128, 256) == 4 * 256 * 4
+    assert lib.omni_shared_mlp_workspace(1, 4, 128, 0) == 0
+    assert lib.omni_shared_mlp_workspace(2, 4, 128, 256) == 0
+    # few tokens, long hidden width: the down product is split, partials after the hidden
+    big = lib.omni_shared_mlp_workspace(1, 256, 2048, 5632)
+    assert big == 256 * 5632 * 2 + 8 * 256 * 2048 * 4
 
     def call(dt=1, L=4, d=128, d_ff=256, x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, y=FAKE, ws=FAKE,
              n=nws):
@@ -225,7 +228,7 @@ def test_shared_mlp_argument_checks(lib):
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
     # an empty batch needs no x or y and enqueues nothing
-    assert call(L=0, x=None, y=None, n=lib.omni_shared_mlp_workspace(1, 0, 256)) == B.OMNI_OK
+    assert call(L=0, x=None, y=None, n=lib.omni_shared_mlp_workspace(1, 0, 128, 256)) == B.OMNI_OK
 
 
 def test_atomic_forward_glu_argument_checks(lib):

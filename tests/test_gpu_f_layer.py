@@ -31,6 +31,9 @@ CASES = {
     "small": WORKLOADS["small"],
     "one_token": custom(L=1, d=256, Nr=8, Nc=8, kprime=4, K=4, B=4, dtype="bf16", index=403,
                         dff=64),
+    # few tokens: the down product is split over d_ff (8 chunks)
+    "decode_shape": custom(L=256, d=2048, Nr=16, Nc=16, kprime=4, K=4, B=4, dtype="bf16",
+                           index=405, dff=5632),
 }
 # the routed branch needs d = 64 * 2^p: a ragged layer case of its own
 LAYER_CASES = {
