@@ -107,3 +107,16 @@ def test_flat_router_edge_cases():
     idx, _, gate = OV.flat_topk(logp, 6)
     assert all(sorted(r) == list(range(6)) for r in idx.tolist())
     np.testing.assert_allclose(gate.sum(axis=1), 1, rtol=1e-6)
+
+
+def test_flat_router_bias_is_a_log_prior():
+    # Wf = 0 and bias = log p: the logits are the bias, so log p comes back
+    # (softmax of log p is p) and the top-K follows p
+    rng = np.random.default_rng(8)
+    p = rng.random(12) + 0.05
+    p /= p.sum()
+    x = rng.standard_normal((3, 8)).astype(np.float32)
+    logp = OV.flat_router_logp(x, np.zeros((12, 8)), np.log(p).astype(np.float32))
+    np.testing.assert_allclose(logp, np.tile(np.log(p), (3, 1)), rtol=0, atol=2e-6)
+    idx, _, _ = OV.flat_topk(logp, 4)
+    assert (idx == np.argsort(-p, kind="stable")[:4]).all()
