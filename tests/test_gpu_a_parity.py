@@ -213,9 +213,15 @@ def _zipf_ids(L, K, N, s, seed):
                                           (513, 64, 1 << 20, 64, "uniform"),
                                           (2000, 32, 20000, 4, "zipf"),
                                           (1, 1, 1, 1, "uniform"),
-                                          (70000, 3, 210000, 1, "uniform")])
+                                          (70000, 3, 210000, 1, "uniform"),
+                                          (256, 64, 1 << 20, 1, "uniform"),
+                                          (256, 64, 1 << 20, 64, "zipf"),
+                                          (257, 64, 1 << 20, 64, "uniform"),
+                                          (100, 10, (1 << 20) + 1, 4, "uniform")])
 def test_schedule_direct_is_bit_exact(L, K, N, Bg, kind):
-    # Ragged task tiles, one to three radix passes, hot experts.
+    # Ragged task tiles, one to three radix passes, hot experts; the decode
+    # shape (16384 tasks over 2^20 experts) with B = 1, as the backward runs
+    # it (16384 groups: two passes), hot experts on 2^20 ids, 2^20 + 1 ids.
     log(f"[schedule] L={L} K={K} N={N} B={Bg} {kind}")
     if kind == "zipf":
         idx = _zipf_ids(L, K, N, 1.1, seed=L)
@@ -233,10 +239,13 @@ def test_schedule_direct_is_bit_exact(L, K, N, Bg, kind):
                                           (37, 5, 1 << 20, 256, "uniform"),
                                           (9, 3, 10, 1, "uniform"),
                                           (70000, 3, 210000, 1, "uniform"),
-                                          (40, 4, 100, 1000, "uniform")])
+                                          (40, 4, 100, 1000, "uniform"),
+                                          (256, 64, 1 << 20, 16, "uniform"),
+                                          (256, 64, 1 << 20, 15, "uniform")])
 def test_window_schedule_is_bit_exact(L, K, N, Bg, kind):
     # fixed id windows: every window a group, empty ones included (up to
-    # 210,000 groups: three radix passes), one window holding every expert
+    # 210,000 groups: three radix passes), one window holding every expert;
+    # 65536 and 69906 windows over 2^20 ids
     log(f"[schedule window] L={L} K={K} N={N} B={Bg} {kind}")
     if kind == "zipf":
         idx = _zipf_ids(L, K, N, 1.1, seed=L + 1)
