@@ -248,9 +248,9 @@ omni_status omni_flat_router_topk(omni_dtype dt, int L, int d, int N, int K, con
   if (dt == OMNI_BF16 && d % 8 != 0) return OMNI_ERR_UNSUPPORTED;
   if (dt == OMNI_F32 && d % 4 != 0) return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(wf)) return OMNI_ERR_INVALID_ARG;
+  if (L == 0) return OMNI_OK;
   const size_t need = omni_flat_router_workspace(dt, L, N);
   if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
-  if (L == 0) return OMNI_OK;
   return hip_status(omni::launch_flat_router(dt == OMNI_BF16, L, d, N, K, x, wf, bias,
                                              expert_idx, score, gate, logp, ws, stream));
 }
@@ -316,9 +316,9 @@ omni_status omni_shared_mlp(omni_dtype dt, int L, int d, int d_ff, const void* x
   const void* rows[] = {x, w_gate, w_up, w_down, y};
   for (const void* p : rows)
     if (p && !aligned16(p)) return OMNI_ERR_INVALID_ARG;
+  if (L == 0) return OMNI_OK;
   const size_t need = omni_shared_mlp_workspace(dt, L, d, d_ff);
   if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
-  if (L == 0) return OMNI_OK;
   const int bf16 = dt == OMNI_BF16;
   hipError_t e = omni::launch_swiglu_up(bf16, x, w_gate, w_up, ws, L, d, d_ff, stream);
   if (e != hipSuccess) return hip_status(e);

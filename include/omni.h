@@ -36,6 +36,8 @@
  *   - Tie rule everywhere: larger value first, then lower index; values are
  *     compared as float32 numbers (-0 == +0).
  *   - L == 0 is accepted and enqueues only what writes the (empty) outputs.
+ *     A call that then enqueues nothing takes a null workspace; the backward
+ *     still writes its (zero) router gradients through its workspace.
  */
 #ifndef OMNI_H
 #define OMNI_H

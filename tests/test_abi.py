@@ -199,6 +199,8 @@ def test_routed_backward_argument_checks(lib):
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
+    # no tokens: still zero router gradients to write, through the workspace
+    assert call(L=0, x=None, dy=None, ws=None, n=0) == B.OMNI_ERR_WORKSPACE
 
 
 def test_shared_mlp_argument_checks(lib):
@@ -229,6 +231,7 @@ def test_shared_mlp_argument_checks(lib):
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == B.OMNI_ERR_WORKSPACE
     # an empty batch needs no x or y and enqueues nothing
     assert call(L=0, x=None, y=None, n=lib.omni_shared_mlp_workspace(1, 0, 128, 256)) == B.OMNI_OK
+    assert call(L=0, x=None, y=None, ws=None, n=0) == B.OMNI_OK
 
 
 def test_atomic_forward_glu_argument_checks(lib):
@@ -269,3 +272,4 @@ def test_flat_router_argument_checks(lib):
     assert call(d=132) == B.OMNI_ERR_UNSUPPORTED
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(L=0, x=None, idx=None, n=lib.omni_flat_router_workspace(1, 0, 1000)) == B.OMNI_OK
+    assert call(L=0, x=None, idx=None, ws=None, n=0) == B.OMNI_OK

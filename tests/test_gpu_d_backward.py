@@ -75,3 +75,23 @@ def test_backward_is_deterministic():
     _, _, _, g2 = _run(wl, seed=1)
     for k, v in r1.items():
         np.testing.assert_array_equal(v.view(np.uint8), cut(k, host(g2[k])).view(np.uint8))
+
+
+def test_backward_of_an_empty_batch():
+    # No tokens: the router gradients are sums over no tokens (zero), no
+    # expert is active; outputs prefilled with NaN / -1 must be overwritten.
+    wl = custom(L=40, d=128, Nr=16, Nc=16, kprime=4, K=4, B=1, dtype="bf16", index=305)
+    t = {k: dev(v) for k, v in make_inputs(wl).items()}
+    K, d = wl.K, wl.d
+    empty = lambda shape, dtype: torch.empty(shape, dtype=dtype, device="cuda")
+    nan = lambda shape: torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    out = {"dwr": nan((wl.Nr, d)), "dwc": nan((wl.Nc, d)), "drb": nan((wl.Nr,)),
+           "dcb": nan((wl.Nc,)),
+           "counts": torch.full((2,), -1, dtype=torch.int32, device="cuda")}
+    g = B.routed_backward(t["x"][:0], t["wr"], t["wc"], t["w"], t["v"],
+                          empty((0, K), torch.int32), empty((0, K), torch.float32),
+                          empty((0, d), torch.float32), out=out)
+    torch.cuda.synchronize()
+    assert host(g["counts"]).tolist() == [0, 0]
+    for k in ("dwr", "dwc", "drb", "dcb"):
+        np.testing.assert_array_equal(host(g[k]), 0.0)
