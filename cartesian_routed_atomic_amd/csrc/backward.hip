@@ -67,7 +67,8 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
 constexpr int kBwdRing = 4;  // row slots per wave: three in flight
 constexpr int kSegEpl = 16;  // row elements per lane in the dV / dW reduction
 
-template <typename T, int EPL>
+// NT: the W and V rows carry the nontemporal hint (stream_rows).
+template <typename T, int EPL, bool NT>
 __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ V,
     const int32_t* __restrict__ expert_idx,
@@ -97,14 +98,14 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
   float my_u = 0.f;
 #pragma unroll
   for (int s = 0; s < kBwdRing - 1; ++s)
-    if (s < K) f[s].load(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
+    if (s < K) f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
   for (int i = 0; i < K; i += kBwdRing) {
 #pragma unroll
     for (int s = 0; s < kBwdRing; ++s) {
       const int k = i + s;
       if (k >= K) break;
       if (k + kBwdRing - 1 < K)
-        f[(s + kBwdRing - 1) % kBwdRing].load(
+        f[(s + kBwdRing - 1) % kBwdRing].template fetch<NT>(
             V + static_cast<size_t>(rdlane(my_e, k + kBwdRing - 1)) * d, l);
       float p = 0.f;
 #pragma unroll
@@ -121,14 +122,14 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
   float my_dh = 0.f, my_dg = 0.f, my_c = 0.f;
 #pragma unroll
   for (int s = 0; s < kBwdRing - 1; ++s)
-    if (s < K) f[s].load(W + static_cast<size_t>(rdlane(my_e, s)) * d, l);
+    if (s < K) f[s].template fetch<NT>(W + static_cast<size_t>(rdlane(my_e, s)) * d, l);
   for (int i = 0; i < K; i += kBwdRing) {
 #pragma unroll
     for (int s = 0; s < kBwdRing; ++s) {
       const int k = i + s;
       if (k >= K) break;
       if (k + kBwdRing - 1 < K)
-        f[(s + kBwdRing - 1) % kBwdRing].load(
+        f[(s + kBwdRing - 1) % kBwdRing].template fetch<NT>(
             W + static_cast<size_t>(rdlane(my_e, k + kBwdRing - 1)) * d, l);
       const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
       const float g = rdlane(my_g, k), u = rdlane(my_u, k);
@@ -520,8 +521,12 @@ static hipError_t launch_bwd_t(const T* x, const T* wr, const T* wc, const T* w,
   transpose_pad_kernel<T><<<dim3(static_cast<unsigned>(Rp / 64),
                                  static_cast<unsigned>((d + 63) / 64)), 256, 0, s>>>(
       wr, Nr, wc, Nc, d, Rp, wrct);
-  if (L > 0)
-    bwd_token_kernel<T, EPL><<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(
+  if (L > 0 && stream_rows(M, N))
+    bwd_token_kernel<T, EPL, true><<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(
+        x, w, v, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate, dzt, Lp, dz,
+        Rp);
+  else if (L > 0)
+    bwd_token_kernel<T, EPL, false><<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(
         x, w, v, expert_idx, gate, dy, L, K, d, N, Nr, Nc, dx, coef, dh, ds, dgate, dzt, Lp, dz,
         Rp);
   // router part of dx: dx += [dz_r dz_c] [Wr; Wc], one MFMA product

@@ -51,6 +51,8 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
 
 // execute.hip
 size_t atomic_forward_ws_bytes(int L, int K);
+// true: read expert rows with the nontemporal hint (M tasks over N experts)
+bool stream_rows(long long M, long long N);
 bool token_centric_supported(int bf16, int d);
 int auto_exec_mode(int bf16, int L, int d, int K);  // 1 expert-centric, 2 token-centric
 hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,

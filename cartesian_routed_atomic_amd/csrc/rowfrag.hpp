@@ -7,10 +7,25 @@
 namespace omni {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// A plain load, or (NT) one with the nontemporal hint.  Rows that a kernel
+// reads once (expert rows, a token's own x row) are streamed with the hint so
+// they do not displace what is reused from the caches (x rows shared by a
+// run of tasks, y, the task lists).
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
 // A row fragment of one lane: EPL elements held raw (as loaded) so a load
 // can stay in flight until the first use; element q = c * VEC + j maps to
-// row[c * 64 * VEC + lane * VEC + j].
+// row[c * 64 * VEC + lane * VEC + j].  load() caches as usual; stream()
+// carries the nontemporal hint.
 template <typename T, int EPL> struct RowFrag;
 
 template <int EPL> struct RowFrag<uint16_t, EPL> {  // bfloat16 bits
@@ -18,16 +33,28 @@ template <int EPL> struct RowFrag<uint16_t, EPL> {  // bfloat16 bits
   static constexpr int NCH = EPL / VEC;
   static constexpr int NW = (EPL + 1) / 2;
   uint32_t w[NW];
-  __device__ __forceinline__ void load(const uint16_t* row, int l) {
+  template <bool NT>
+  __device__ __forceinline__ void fetch(const uint16_t* row, int l) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const uint16_t* p = row + c * 64 * VEC + l * VEC;
-      if constexpr (VEC == 8) *reinterpret_cast<uint4*>(&w[c * 4]) = *reinterpret_cast<const uint4*>(p);
-      else if constexpr (VEC == 4) *reinterpret_cast<uint2*>(&w[c * 2]) = *reinterpret_cast<const uint2*>(p);
-      else if constexpr (VEC == 2) w[c] = *reinterpret_cast<const uint32_t*>(p);
-      else w[0] = static_cast<uint32_t>(*p);
+      if constexpr (VEC == 8) {
+        const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[c * 4 + j] = v[j];
+      } else if constexpr (VEC == 4) {
+        const u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(p));
+        w[c * 2] = v[0];
+        w[c * 2 + 1] = v[1];
+      } else if constexpr (VEC == 2) {
+        w[c] = ld<NT>(reinterpret_cast<const uint32_t*>(p));
+      } else {
+        w[0] = static_cast<uint32_t>(ld<NT>(p));
+      }
     }
   }
+  __device__ __forceinline__ void load(const uint16_t* row, int l) { fetch<false>(row, l); }
+  __device__ __forceinline__ void stream(const uint16_t* row, int l) { fetch<true>(row, l); }
   __device__ __forceinline__ float get(int q) const {
     if constexpr (VEC == 1) return bf_lo(w[0]);
     else return (q & 1) ? bf_hi(w[q >> 1]) : bf_lo(w[q >> 1]);
@@ -38,15 +65,26 @@ template <int EPL> struct RowFrag<float, EPL> {
   static constexpr int VEC = EPL < 4 ? EPL : 4;
   static constexpr int NCH = EPL / VEC;
   float f[EPL];
-  __device__ __forceinline__ void load(const float* row, int l) {
+  template <bool NT>
+  __device__ __forceinline__ void fetch(const float* row, int l) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const float* p = row + c * 64 * VEC + l * VEC;
-      if constexpr (VEC == 4) *reinterpret_cast<float4*>(&f[c * 4]) = *reinterpret_cast<const float4*>(p);
-      else if constexpr (VEC == 2) *reinterpret_cast<float2*>(&f[c * 2]) = *reinterpret_cast<const float2*>(p);
-      else f[0] = *p;
+      if constexpr (VEC == 4) {
+        const f32x4 v = ld<NT>(reinterpret_cast<const f32x4*>(p));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[c * 4 + j] = v[j];
+      } else if constexpr (VEC == 2) {
+        const f32x2 v = ld<NT>(reinterpret_cast<const f32x2*>(p));
+        f[c * 2] = v[0];
+        f[c * 2 + 1] = v[1];
+      } else {
+        f[0] = ld<NT>(p);
+      }
     }
   }
+  __device__ __forceinline__ void load(const float* row, int l) { fetch<false>(row, l); }
+  __device__ __forceinline__ void stream(const float* row, int l) { fetch<true>(row, l); }
   __device__ __forceinline__ float get(int q) const { return f[q]; }
 };
 
