@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
       }
     }
   }
-  store_row<T, EPL>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
+  store_row<T, EPL, true>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
 }
 
 // A task of a token's list: expert id and gate, at flat position t*K + k.
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
       }
     }
   }
-  store_row<T, EPL>(acc, y + static_cast<size_t>(t) * d, accumulate);
+  store_row<T, EPL, true>(acc, y + static_cast<size_t>(t) * d, accumulate);
 }
 
 static inline int clampi(long long v, int lo, int hi) {

@@ -118,8 +118,10 @@ __device__ __forceinline__ float rdlane(float v, int i) {
 }
 
 // Store (or add) a lane's accumulators to its columns of a y row, in the
-// RowFrag element layout, with 16-byte stores where the layout allows.
-template <typename T, int EPL>
+// RowFrag element layout, with 16-byte stores where the layout allows.  NT:
+// the stores carry the nontemporal hint (the executor's y rows: written once,
+// read by no later kernel of the call).
+template <typename T, int EPL, bool NT>
 __device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __restrict__ yrow,
                                           int accumulate) {
   constexpr int VEC = RowFrag<T, EPL>::VEC, NCH = RowFrag<T, EPL>::NCH;
@@ -136,11 +138,20 @@ __device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __rest
           const float4 o = *reinterpret_cast<const float4*>(p + j);
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
         }
-        *reinterpret_cast<float4*>(p + j) = v;
+        if constexpr (NT) {
+          const f32x4 nv = {v.x, v.y, v.z, v.w};
+          __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(p + j));
+        } else {
+          *reinterpret_cast<float4*>(p + j) = v;
+        }
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) p[q] = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
+      for (int q = 0; q < VEC; ++q) {
+        const float v = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
+        if constexpr (NT) __builtin_nontemporal_store(v, p + q);
+        else p[q] = v;
+      }
     }
   }
 }
