@@ -34,7 +34,8 @@ EXEC_SRCS = [os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
 EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
-    "token": "omni_atomic_forward, token-centric: unpermute_kernel + token_kernel",
+    "token": "omni_atomic_forward, token-centric: token_kernel (token lists read from the "
+             "flattened selection the schedule carries)",
 }
 
 

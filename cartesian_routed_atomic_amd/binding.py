@@ -19,7 +19,7 @@ OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ER
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -42,7 +42,7 @@ class OmniError(RuntimeError):
 class ScheduleStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("counts", "active", "group_offsets", "task_token", "task_expert",
-                 "task_gate", "task_index")]
+                 "task_gate", "task_index", "flat_expert", "flat_gate")]
 
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -211,11 +211,16 @@ class Schedule:
     task_gate: torch.Tensor
     task_index: torch.Tensor | None
     workspace: torch.Tensor | None
+    # the selection the tasks were built from, in flatten order (set by
+    # schedule_tasks; the token-centric executor reads the token lists from
+    # it; None makes that executor invert the sorted order instead)
+    flat_expert: torch.Tensor | None = None
+    flat_gate: torch.Tensor | None = None
 
     def struct(self):
         return ScheduleStruct(*(None if t is None else t.data_ptr() for t in (
             self.counts, self.active, self.group_offsets, self.task_token, self.task_expert,
-            self.task_gate, self.task_index)))
+            self.task_gate, self.task_index, self.flat_expert, self.flat_gate)))
 
 
 def _grouping(grouping):
@@ -260,6 +265,7 @@ def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None, grouping="ac
     _check("omni_schedule_tasks", lib().omni_schedule_tasks(
         L, K, N, B, _grouping(grouping), _ptr(expert_idx), _ptr(gate), ctypes.byref(st), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(stream)))
+    sched.flat_expert, sched.flat_gate = expert_idx, gate
     return sched
 
 

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -184,6 +184,8 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
   if (M > 0 && (!sched->task_token || !sched->task_expert || !sched->task_gate ||
                 !sched->task_index))
     return OMNI_ERR_INVALID_ARG;
+  if ((sched->flat_expert == nullptr) != (sched->flat_gate == nullptr))
+    return OMNI_ERR_INVALID_ARG;
   if (d < 64 || d > 4096 || (d & (d - 1)) != 0) return OMNI_ERR_UNSUPPORTED;
   const int bf16 = dt == OMNI_BF16;
   const int form = mode == OMNI_EXEC_AUTO ? omni::auto_exec_mode(bf16, L, d, K) : mode;
@@ -197,7 +199,8 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
   return hip_status(omni::launch_atomic_forward(bf16, form, L, d, N, K, x, w, v,
                                                 sched->task_token, sched->task_expert,
-                                                sched->task_gate, sched->task_index, y,
+                                                sched->task_gate, sched->task_index,
+                                                sched->flat_expert, sched->flat_gate, y,
                                                 accumulate != 0, ws, stream));
 }
 
@@ -212,6 +215,8 @@ omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, i
   if (L > 0 && (!x || !y)) return OMNI_ERR_INVALID_ARG;
   if (M > 0 && (!sched->task_expert || !sched->task_gate || !sched->task_index))
     return OMNI_ERR_INVALID_ARG;
+  if ((sched->flat_expert == nullptr) != (sched->flat_gate == nullptr))
+    return OMNI_ERR_INVALID_ARG;
   const int bf16 = dt == OMNI_BF16;
   if (!omni::token_centric_supported(bf16, d)) return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(u) || !aligned16(v))
@@ -223,7 +228,8 @@ omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, i
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
   return hip_status(omni::launch_atomic_forward_glu(bf16, L, d, N, K, x, w, u, v,
                                                     sched->task_expert, sched->task_gate,
-                                                    sched->task_index, y, accumulate != 0, ws,
+                                                    sched->task_index, sched->flat_expert,
+                                                    sched->flat_gate, y, accumulate != 0, ws,
                                                     stream));
 }
 

@@ -22,7 +22,9 @@
 // float32 atomic add into y per task, which measured about twice as slow on
 // MI355X as reading the repeated V rows again.
 //
-// Token-centric form (the Dynamic Expert Assembly view of §2.1), one kernel:
+// Token-centric form (the Dynamic Expert Assembly view of §2.1), one kernel
+// when the caller hands over the flattened selection (the token lists in
+// flatten order), else one more that inverts the schedule's sorted order:
 //   one wave per token holds x_t in registers, streams the token's K W rows
 //   (pass A: h_k, coef_k) and then its K V rows (pass B: y_t += coef_k V[e]).
 //   It reads every W and V row once per task, like phase 1 + phase 2 above,
@@ -152,25 +154,22 @@ __global__ __launch_bounds__(256) void gather_kernel(
   store_row<T, EPL, true>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
 }
 
-// A task of a token's list: expert id and gate, at flat position t*K + k.
-struct TokTask {
-  int32_t e;
-  float g;
-};
-
-// Inverse of the schedule's task permutation: the (e, g) list of every token
-// in top-K order.  Ids outside their range (only from a corrupted schedule)
-// are mapped to expert 0 so every later access stays in bounds.
+// Inverse of the schedule's task permutation: each token's (expert, gate)
+// list in flatten order m = t*K + k, into le / lg.  Ids outside their range
+// (only from a corrupted schedule) are mapped to expert 0 so every later
+// access stays in bounds.
 __global__ __launch_bounds__(256) void unpermute_kernel(const int32_t* __restrict__ texp,
                                                         const float* __restrict__ tgate,
                                                         const int32_t* __restrict__ tidx, int M,
-                                                        int N, TokTask* __restrict__ lists) {
+                                                        int N, int32_t* __restrict__ le,
+                                                        float* __restrict__ lg) {
   const int m = blockIdx.x * 256 + threadIdx.x;
   if (m >= M) return;
   const int i = tidx[m];
   if (static_cast<unsigned>(i) >= static_cast<unsigned>(M)) return;
   const int e = texp[m];
-  lists[i] = TokTask{static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0, tgate[m]};
+  le[i] = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
+  lg[i] = tgate[m];
 }
 
 constexpr int kTokRing = 6;  // row slots per wave in the token-centric kernel: five in flight
@@ -206,8 +205,8 @@ __device__ __forceinline__ float token_dots(const RowFrag<T, EPL>& xf, const T* 
 template <typename T, int EPL, bool GLU, bool NT>
 __global__ __launch_bounds__(256, 3) void token_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
-    const T* __restrict__ V, const TokTask* __restrict__ lists, int L, int K, int d, int N,
-    float* __restrict__ y, int accumulate) {
+    const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
+    int K, int d, int N, float* __restrict__ y, int accumulate) {
   using Frag = RowFrag<T, EPL>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
@@ -223,9 +222,10 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
     int my_e = 0;
     float my_g = 0.f;
     if (l < n) {
-      const TokTask tk = lists[static_cast<size_t>(t) * K + k0 + l];
-      my_e = static_cast<unsigned>(tk.e) < static_cast<unsigned>(N) ? tk.e : 0;
-      my_g = tk.g;
+      const size_t o = static_cast<size_t>(t) * K + k0 + l;
+      const int e = le[o];
+      my_e = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
+      my_g = lg[o];
     }
     // pass A: h_k = x_t . W[e_k]; h_k ends in lane k
     const float my_h = token_dots<T, EPL, NT>(xf, W, my_e, n, d, l, f);
@@ -318,21 +318,31 @@ size_t atomic_forward_ws_bytes(int L, int K) {
   return 2 * ((m + 255) & ~static_cast<size_t>(255));
 }
 
+// The token lists: the caller's flattened selection (fe, fg) when given,
+// else the schedule inverted into the workspace (ws: M ids, then M gates).
 template <typename T, bool GLU, bool NT>
 static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const int32_t* te,
-                           const float* tg, const int32_t* ti, int M, int d, int L, int K, int N,
-                           TokTask* lists, float* y, int accumulate, hipStream_t s) {
-  unpermute_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(te, tg, ti, M, N,
-                                                                          lists);
+                           const float* tg, const int32_t* ti, const int32_t* fe,
+                           const float* fg, int M, int d, int L, int K, int N, void* ws, float* y,
+                           int accumulate, hipStream_t s) {
+  if (!fe) {
+    int32_t* le = static_cast<int32_t*>(ws);
+    float* lg = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         atomic_forward_ws_bytes(L, K) / 2);
+    unpermute_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(te, tg, ti, M, N, le,
+                                                                            lg);
+    fe = le;
+    fg = lg;
+  }
   const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
   // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
   switch (d) {
-#define OMNI_TOK(D_, EPL_) case D_: token_kernel<T, EPL_, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, lists, L, K, d, N, y, accumulate); break;
+#define OMNI_TOK(D_, EPL_) case D_: token_kernel<T, EPL_, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y, accumulate); break;
     OMNI_TOK(64, 1) OMNI_TOK(128, 2) OMNI_TOK(256, 4) OMNI_TOK(512, 8) OMNI_TOK(1024, 16)
 #undef OMNI_TOK
     case 2048:
       if constexpr (sizeof(T) == 2) {
-        token_kernel<T, 32, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, lists, L, K, d, N, y,
+        token_kernel<T, 32, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y,
                                                           accumulate);
         break;
       }
@@ -369,7 +379,8 @@ int auto_exec_mode(int bf16, int L, int d, int K) {
 hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,
                                  const void* w, const void* v, const int32_t* task_token,
                                  const int32_t* task_expert, const float* task_gate,
-                                 const int32_t* task_index, float* y, bool accumulate, void* ws,
+                                 const int32_t* task_index, const int32_t* flat_expert,
+                                 const float* flat_gate, float* y, bool accumulate, void* ws,
                                  hipStream_t s) {
   if (L == 0) return hipSuccess;
   const int M = L * K;
@@ -385,24 +396,26 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
   const bool nt = stream_rows(M, N);
   bool ok;
   if (mode == 2) {
-    TokTask* lists = static_cast<TokTask*>(ws);
     if (bf16) {
       const auto* xb = static_cast<const uint16_t*>(x);
       const auto* wb = static_cast<const uint16_t*>(w);
       const auto* vb = static_cast<const uint16_t*>(v);
       ok = nt ? dispatch_token<uint16_t, false, true>(xb, wb, nullptr, vb, task_expert, task_gate,
-                                                      task_index, M, d, L, K, N, lists, y, acc, s)
+                                                      task_index, flat_expert, flat_gate, M, d, L,
+                                                      K, N, ws, y, acc, s)
               : dispatch_token<uint16_t, false, false>(xb, wb, nullptr, vb, task_expert,
-                                                       task_gate, task_index, M, d, L, K, N,
-                                                       lists, y, acc, s);
+                                                       task_gate, task_index, flat_expert,
+                                                       flat_gate, M, d, L, K, N, ws, y, acc, s);
     } else {
       const auto* xf = static_cast<const float*>(x);
       const auto* wf = static_cast<const float*>(w);
       const auto* vf = static_cast<const float*>(v);
       ok = nt ? dispatch_token<float, false, true>(xf, wf, nullptr, vf, task_expert, task_gate,
-                                                   task_index, M, d, L, K, N, lists, y, acc, s)
+                                                   task_index, flat_expert, flat_gate, M, d, L, K,
+                                                   N, ws, y, acc, s)
               : dispatch_token<float, false, false>(xf, wf, nullptr, vf, task_expert, task_gate,
-                                                    task_index, M, d, L, K, N, lists, y, acc, s);
+                                                    task_index, flat_expert, flat_gate, M, d, L,
+                                                    K, N, ws, y, acc, s);
     }
   } else {
     float* coef = static_cast<float*>(ws);
@@ -435,7 +448,8 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
 hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const void* x,
                                      const void* w, const void* u, const void* v,
                                      const int32_t* task_expert, const float* task_gate,
-                                     const int32_t* task_index, float* y, bool accumulate,
+                                     const int32_t* task_index, const int32_t* flat_expert,
+                                     const float* flat_gate, float* y, bool accumulate,
                                      void* ws, hipStream_t s) {
   if (L == 0) return hipSuccess;
   if (!token_centric_supported(bf16, d)) return hipErrorInvalidValue;
@@ -449,7 +463,6 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
     return hipGetLastError();
   }
   const int acc = accumulate ? 1 : 0;
-  TokTask* lists = static_cast<TokTask*>(ws);
   const bool nt = stream_rows(M, N);
   bool ok;
   if (bf16) {
@@ -458,18 +471,22 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
     const auto* ub = static_cast<const uint16_t*>(u);
     const auto* vb = static_cast<const uint16_t*>(v);
     ok = nt ? dispatch_token<uint16_t, true, true>(xb, wb, ub, vb, task_expert, task_gate,
-                                                   task_index, M, d, L, K, N, lists, y, acc, s)
+                                                   task_index, flat_expert, flat_gate, M, d, L, K,
+                                                   N, ws, y, acc, s)
             : dispatch_token<uint16_t, true, false>(xb, wb, ub, vb, task_expert, task_gate,
-                                                    task_index, M, d, L, K, N, lists, y, acc, s);
+                                                    task_index, flat_expert, flat_gate, M, d, L,
+                                                    K, N, ws, y, acc, s);
   } else {
     const auto* xf = static_cast<const float*>(x);
     const auto* wf = static_cast<const float*>(w);
     const auto* uf = static_cast<const float*>(u);
     const auto* vf = static_cast<const float*>(v);
     ok = nt ? dispatch_token<float, true, true>(xf, wf, uf, vf, task_expert, task_gate,
-                                                task_index, M, d, L, K, N, lists, y, acc, s)
+                                                task_index, flat_expert, flat_gate, M, d, L, K, N,
+                                                ws, y, acc, s)
             : dispatch_token<float, true, false>(xf, wf, uf, vf, task_expert, task_gate,
-                                                 task_index, M, d, L, K, N, lists, y, acc, s);
+                                                 task_index, flat_expert, flat_gate, M, d, L, K,
+                                                 N, ws, y, acc, s);
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

@@ -55,16 +55,20 @@ size_t atomic_forward_ws_bytes(int L, int K);
 bool stream_rows(long long M, long long N);
 bool token_centric_supported(int bf16, int d);
 int auto_exec_mode(int bf16, int L, int d, int K);  // 1 expert-centric, 2 token-centric
+// flat_expert / flat_gate: the selection in flatten order, or NULL (the
+// token-centric form then inverts the sorted order through task_index)
 hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,
                                  const void* w, const void* v, const int32_t* task_token,
                                  const int32_t* task_expert, const float* task_gate,
-                                 const int32_t* task_index, float* y, bool accumulate, void* ws,
+                                 const int32_t* task_index, const int32_t* flat_expert,
+                                 const float* flat_gate, float* y, bool accumulate, void* ws,
                                  hipStream_t s);
 // SwiGLU-gated variant (third matrix u), token-centric form only
 hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const void* x,
                                      const void* w, const void* u, const void* v,
                                      const int32_t* task_expert, const float* task_gate,
-                                     const int32_t* task_index, float* y, bool accumulate,
+                                     const int32_t* task_index, const int32_t* flat_expert,
+                                     const float* flat_gate, float* y, bool accumulate,
                                      void* ws, hipStream_t s);
 
 // flat_router.hip: the d x N router baseline

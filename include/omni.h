@@ -64,7 +64,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 10 */
+int omni_abi_version(void);  /* 11 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -168,6 +168,15 @@ typedef enum omni_grouping {
  *                          sorted by (group, token), ties in flatten order.
  *   task_index    [L*K] int32: flat id m = t*K + k of each sorted task, or
  *                          NULL if not wanted.
+ *   flat_expert   [L*K] int32, flat_gate [L*K] float32, optional (NULL, or
+ *                          both set): the flattened selection the tasks were
+ *                          built from, in flatten order m = t*K + k (the
+ *                          expert_idx / gate given to omni_schedule_tasks).
+ *                          omni_schedule_tasks neither reads nor writes them;
+ *                          the token-centric executor reads each token's list
+ *                          from them instead of inverting the sorted order.
+ *                          They must hold the arrays the schedule was built
+ *                          from, else y is unspecified.
  */
 typedef struct omni_schedule {
   int32_t* counts;
@@ -177,6 +186,8 @@ typedef struct omni_schedule {
   int32_t* task_expert;
   float* task_gate;
   int32_t* task_index;
+  const int32_t* flat_expert;
+  const float* flat_gate;
 } omni_schedule;
 
 /* G above: the number of groups the schedule can hold (0 for invalid args). */
@@ -223,8 +234,10 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *     schedule's (group, token) order and computes c = g * silu(x_t . W[e])
  *     per task, the second gathers y_t = sum_k c_tk V[e_tk] per token, so y
  *     is written once, without atomics.
- *   OMNI_EXEC_TOKEN_CENTRIC: the schedule is inverted into per-token task
- *     lists, then one wave per token assembles its experts: x_t stays in
+ *   OMNI_EXEC_TOKEN_CENTRIC: the per-token task lists are the schedule's
+ *     flat_expert / flat_gate when present, else the schedule's sorted order
+ *     inverted through task_index (one more kernel); then one wave per
+ *     token assembles its experts: x_t stays in
  *     registers, the token's W rows give the K coefficients, its V rows are
  *     summed into y_t.  Needs d * element size <= 4096 bytes (else
  *     UNSUPPORTED).

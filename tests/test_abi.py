@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 10
+    assert lib.omni_abi_version() == 11
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -160,6 +160,11 @@ def test_atomic_forward_argument_checks(lib):
     assert call() == B.OMNI_ERR_WORKSPACE                  # L*K tasks need a workspace
     noidx = B.ScheduleStruct(*([1 << 20] * 6 + [0]))
     assert call(s=noidx) == B.OMNI_ERR_INVALID_ARG          # task_index is required
+    # the flattened selection: both arrays or neither
+    half = B.ScheduleStruct(*([1 << 20] * 8 + [0]))
+    assert call(s=half) == B.OMNI_ERR_INVALID_ARG
+    both = B.ScheduleStruct(*([1 << 20] * 9))
+    assert call(s=both) == B.OMNI_ERR_WORKSPACE
     assert lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256) >= 8 * 8192 * 64
 
 
@@ -245,6 +250,7 @@ def test_atomic_forward_glu_argument_checks(lib):
     assert call(dt=2) == B.OMNI_ERR_INVALID_ARG
     assert call(u=None) == B.OMNI_ERR_INVALID_ARG
     assert call(s=None) == B.OMNI_ERR_INVALID_ARG
+    assert call(s=B.ScheduleStruct(*([1 << 20] * 7 + [0, 1 << 20]))) == B.OMNI_ERR_INVALID_ARG
     assert call(x=None) == B.OMNI_ERR_INVALID_ARG
     assert call(u=MIS) == B.OMNI_ERR_INVALID_ARG
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED

@@ -36,7 +36,17 @@ def test_full_size_parity(name):
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int32), out["y"].view(torch.int32))
     log(f"  y of the {auto}-centric (auto) and {other}-centric forms bit-identical")
-    del t, y2
+    # the token-centric form with its lists inverted from the sorted schedule
+    # instead of read from the flattened selection: the same bits
+    s = out["schedule"]
+    flat = (s.flat_expert, s.flat_gate)
+    s.flat_expert = s.flat_gate = None
+    y3 = B.atomic_forward(t["x"], t["w"], t["v"], s, mode="token")
+    s.flat_expert, s.flat_gate = flat
+    torch.cuda.synchronize()
+    assert torch.equal(y3.view(torch.int32), out["y"].view(torch.int32))
+    log("  token lists from the selection and from the schedule give bit-identical y")
+    del t, y2, y3
     log(f"  gpu done {time.time() - t0:.1f}s")
     check_router(inp, out)
     rng = np.random.default_rng(0)

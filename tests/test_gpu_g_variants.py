@@ -39,7 +39,15 @@ def test_glu_expert_parity(name):
     y0 = np.random.default_rng(wl.index).standard_normal((wl.L, wl.d)).astype(np.float32)
     y2 = B.atomic_forward_glu(t["x"], t["w"], t["u"], t["v"], out["schedule"], y=dev(y0),
                               accumulate=True)
+    # token lists inverted from the sorted schedule instead of read from the
+    # flattened selection: the same bits
+    s = out["schedule"]
+    flat = (s.flat_expert, s.flat_gate)
+    s.flat_expert = s.flat_gate = None
+    y3 = B.atomic_forward_glu(t["x"], t["w"], t["u"], t["v"], s)
+    s.flat_expert, s.flat_gate = flat
     torch.cuda.synchronize()
+    assert torch.equal(y3.view(torch.int32), y.view(torch.int32))
     idx, gate = host(out["expert_idx"]), host(out["gate"])
     toks = np.arange(wl.L) if wl.L <= 512 else np.sort(
         np.random.default_rng(3).choice(wl.L, 128, replace=False))
