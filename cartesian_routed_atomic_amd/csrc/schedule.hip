@@ -28,6 +28,11 @@ namespace omni {
 
 constexpr int kTile = 4096;   // experts per flag tile (256 threads x 16)
 constexpr int kSTile = 2048;  // tasks per sort tile (512 threads x 4)
+// Up to this many sort tiles (65,536 tasks) the down-sweep reads its digit
+// rows of tile counts itself, one round of loads; measured: decode (8 tiles)
+// 31 -> 27 us per schedule, tiny 30 -> 25 us; at 64 tiles (two rounds) it
+// lost 3 us to the separate scan.
+constexpr int kFuseTiles = 32;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -195,26 +200,53 @@ __global__ __launch_bounds__(64) void radix_rowscan_kernel(int* __restrict__ his
 // elements 64 at a time: lanes with the same digit find each other with 8
 // ballots, the lowest of them bumps the wave's running count.  The last
 // effective pass also writes the task arrays.
+// fused != 0 (few tiles): hist holds the raw tile counts and each block sums
+// its digit rows itself (no radix_rowscan_kernel launch); a single-pass sort
+// then also writes the group offsets (G + 1 entries, spread over the blocks:
+// off[g] = tasks in groups below g), so no offsets_kernel launch either.
 __global__ __launch_bounds__(512) void radix_down_kernel(
     const int* __restrict__ kin, const int* __restrict__ vin, int M, int pass, int n_tt,
     const int* __restrict__ hist, const int* __restrict__ dtot, const int* __restrict__ counts,
     int* __restrict__ kout, int* __restrict__ vout, int K,
     const int32_t* __restrict__ expert_idx, const float* __restrict__ gate,
     int32_t* __restrict__ task_token, int32_t* __restrict__ task_expert,
-    float* __restrict__ task_gate, int32_t* __restrict__ task_index) {
+    float* __restrict__ task_gate, int32_t* __restrict__ task_index, int fused, int G,
+    int32_t* __restrict__ group_offsets) {
   const int eff = effective_passes(counts[1]);
   if (pass >= eff) return;
   const bool last = pass == eff - 1;
   constexpr int kW = 8, kR = kSTile / (kW * 64);
   __shared__ uint32_t wh[kW][256];
   __shared__ uint32_t goff[256];
+  __shared__ uint32_t tpre[256];
   __shared__ uint32_t red[4];
   const int tid = threadIdx.x, w = tid >> 6, l = lane();
   for (int q = 0; q < kW; ++q)
     if (tid < 256) wh[q][tid] = 0;
   // digit base: exclusive scan of the digit totals (first 4 waves, 64 each)
   if (tid < 256) {
-    const uint32_t v = static_cast<uint32_t>(dtot[tid]);
+    uint32_t v, before;
+    if (fused) {  // this digit's tiles before this block, and all of them
+      const int* row = hist + static_cast<size_t>(tid) * n_tt;
+      uint32_t all = 0;
+      before = 0;
+      for (int b0 = 0; b0 < n_tt; b0 += 32) {  // 32 loads in flight per round
+        uint32_t c[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          c[j] = b0 + j < n_tt ? static_cast<uint32_t>(row[b0 + j]) : 0u;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          before += b0 + j < static_cast<int>(blockIdx.x) ? c[j] : 0u;
+          all += c[j];
+        }
+      }
+      v = all;
+    } else {
+      v = static_cast<uint32_t>(dtot[tid]);
+      before = static_cast<uint32_t>(hist[tid * n_tt + blockIdx.x]);
+    }
+    tpre[tid] = before;
     const uint32_t inc = wave_inclusive_scan(v);
     if (l == 63) red[w] = inc;
     goff[tid] = inc - v;
@@ -223,8 +255,15 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
   if (tid < 256) {
     uint32_t add = 0;
     for (int q = 0; q < w; ++q) add += red[q];
-    goff[tid] += add + static_cast<uint32_t>(hist[tid * n_tt + blockIdx.x]);
+    goff[tid] += add;
   }
+  __syncthreads();
+  if (fused && eff == 1) {  // single pass: the digit is the group
+    for (long long g = static_cast<long long>(blockIdx.x) * 512 + tid; g <= G;
+         g += static_cast<long long>(gridDim.x) * 512)
+      group_offsets[g] = g < 256 ? static_cast<int>(goff[g]) : M;
+  }
+  if (tid < 256) goff[tid] += tpre[tid];
   __syncthreads();
   const int shift = 8 * pass;
   const int base = blockIdx.x * kSTile + w * (kR * 64);
@@ -353,20 +392,27 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
   // pass 0 reads the group keys it computes itself (key0) and identity values
   int* kb[2] = {key0, key1};
   int* vb[2] = {val0, val1};
+  // few sort tiles: the down-sweep scans the tile counts itself
+  const int fused = lay.n_ttiles <= kFuseTiles ? 1 : 0;
   for (int p = 0; p < lay.passes; ++p) {
     int* kin = kb[p & 1];
     const int* vin = p == 0 ? nullptr : vb[p & 1];
     radix_up_kernel<<<lay.n_ttiles, 512, 0, s>>>(kin, expert_idx, rank, key0, M, N, B, window,
                                                  p, lay.n_ttiles, counts, hist);
-    radix_rowscan_kernel<<<256, 64, 0, s>>>(hist, lay.n_ttiles, p, counts, dtot);
+    if (!fused) radix_rowscan_kernel<<<256, 64, 0, s>>>(hist, lay.n_ttiles, p, counts, dtot);
     radix_down_kernel<<<lay.n_ttiles, 512, 0, s>>>(
         kin, vin, M, p, lay.n_ttiles, hist, dtot, counts, kb[(p + 1) & 1], vb[(p + 1) & 1], K,
-        expert_idx, gate, task_token, task_expert, task_gate, task_index);
+        expert_idx, gate, task_token, task_expert, task_gate, task_index, fused,
+        lay.max_groups, group_offsets);
   }
-  // the last effective pass p leaves its sorted keys in kb[(p + 1) & 1]
-  const long long nthr = M > lay.max_groups + 1 ? M : lay.max_groups + 1;
-  offsets_kernel<<<blocks_for(nthr, 256), 256, 0, s>>>(key1, key0, M, lay.max_groups, counts,
-                                                       group_offsets);
+  // A fused single-pass sort has written the offsets; with more possible
+  // passes the offsets come from the sorted keys (the last effective pass p
+  // leaves them in kb[(p + 1) & 1]).
+  if (!fused || lay.passes > 1) {
+    const long long nthr = M > lay.max_groups + 1 ? M : lay.max_groups + 1;
+    offsets_kernel<<<blocks_for(nthr, 256), 256, 0, s>>>(key1, key0, M, lay.max_groups, counts,
+                                                         group_offsets);
+  }
   return hipGetLastError();
 }
 
