@@ -27,6 +27,7 @@
 namespace omni {
 
 constexpr int kTile = 4096;   // experts per flag tile (256 threads x 16)
+constexpr int kInlineCountTiles = 8;  // up to 32,768 experts: no separate tile-count launch
 constexpr int kSTile = 2048;  // tasks per sort tile (512 threads x 4)
 // Up to this many sort tiles (65,536 tasks) the down-sweep reads its digit
 // rows of tile counts itself, one round of loads; measured: decode (8 tiles)
@@ -105,11 +106,14 @@ __device__ __forceinline__ int flag_count(uint4 v) {
 __global__ __launch_bounds__(256) void tile_count_kernel(const uint8_t* __restrict__ flags,
                                                          int* __restrict__ tile_cnt) {
   __shared__ int red[4];
-  const uint4 v = reinterpret_cast<const uint4*>(flags + static_cast<size_t>(blockIdx.x) * kTile)[threadIdx.x];
+  const uint4 v =
+      reinterpret_cast<const uint4*>(flags + static_cast<size_t>(blockIdx.x) * kTile)[threadIdx.x];
   const int s = block_sum256(flag_count(v), red);
   if (threadIdx.x == 0) tile_cnt[blockIdx.x] = s;
 }
 
+// tile_cnt == NULL (few tiles): each block counts the flags of the tiles
+// before it itself, in place of tile_count_kernel's per-tile counts.
 __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ flags, int N,
                                                    const int* __restrict__ tile_cnt, int n_tiles,
                                                    int B, int window, int* __restrict__ rank,
@@ -119,7 +123,13 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ f
   __shared__ int wpre[4];
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = lane();
   int part = 0;
-  for (int i = tid; i < b; i += 256) part += tile_cnt[i];
+  if (tile_cnt) {
+    for (int i = tid; i < b; i += 256) part += tile_cnt[i];
+  } else {
+    for (int i = 0; i < b; ++i)
+      part += flag_count(
+          reinterpret_cast<const uint4*>(flags + static_cast<size_t>(i) * kTile)[tid]);
+  }
   const int off = block_sum256(part, red);
   const uint4 v = reinterpret_cast<const uint4*>(flags + static_cast<size_t>(b) * kTile)[tid];
   const int c = flag_count(v);
@@ -385,9 +395,11 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
   zero16_kernel<<<blocks_for(static_cast<long long>(n16), 256), 256, 0, s>>>(
       reinterpret_cast<uint4*>(flags), n16);
   mark_kernel<<<blocks_for(M, 256), 256, 0, s>>>(expert_idx, M, N, flags);
-  tile_count_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, tile_cnt);
-  rank_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, N, tile_cnt, lay.n_ftiles, B, window, rank,
-                                           active, counts);
+  // few expert tiles: rank_kernel counts the flags before its tile itself
+  const bool count_inline = lay.n_ftiles <= kInlineCountTiles;
+  if (!count_inline) tile_count_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, tile_cnt);
+  rank_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, N, count_inline ? nullptr : tile_cnt,
+                                           lay.n_ftiles, B, window, rank, active, counts);
   // pass p reads (key, val) from buffer p & 1 and writes buffer (p + 1) & 1;
   // pass 0 reads the group keys it computes itself (key0) and identity values
   int* kb[2] = {key0, key1};
