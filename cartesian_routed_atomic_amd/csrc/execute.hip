@@ -318,6 +318,98 @@ size_t atomic_forward_ws_bytes(int L, int K) {
   return 2 * ((m + 255) & ~static_cast<size_t>(255));
 }
 
+constexpr int kSplitRing = 8;  // pass-B row-slice slots per wave in token_split_kernel
+
+// Token-centric form for few tokens: one workgroup of WS waves per token.
+// Pass A splits the token's tasks over the waves; each wave computes whole-row
+// dot products for its share exactly as token_kernel does (x_t in registers,
+// the W rows through the ring).  The coefficients meet in LDS.  Pass B splits
+// the columns of y over the waves; each wave sums all of the token's tasks
+// over its columns in k order.  Every coefficient and every y element goes
+// through the same operations in the same order as in token_kernel, so y is
+// bit-identical to it; the split only gives the chip WS times more waves.
+template <typename T, int EPL, int WS, bool GLU, bool NT>
+__global__ __launch_bounds__(64 * WS) void token_split_kernel(
+    const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
+    const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
+    int K, int d, int N, float* __restrict__ y, int accumulate) {
+  static_assert(EPL % WS == 0, "every wave needs at least one element per lane");
+  constexpr int EPLB = EPL / WS;  // pass-B elements per lane
+  using Frag = RowFrag<T, EPL>;
+  using FragB = RowFrag<T, EPLB>;
+  __shared__ float sc[64];
+  __shared__ int se[64];
+  const int t = blockIdx.x;
+  const int w = threadIdx.x >> 6, l = lane();
+  if (t >= L) return;  // the whole workgroup leaves together
+  Frag xf;
+  xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
+  const int col0 = w * 64 * EPLB;
+  float acc[EPLB];
+#pragma unroll
+  for (int q = 0; q < EPLB; ++q) acc[q] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int n = min(64, K - k0);
+    const int per = (n + WS - 1) / WS;
+    const int a0 = w * per;
+    const int na = max(0, min(per, n - a0));  // this wave's tasks: [a0, a0 + na)
+    if (na > 0) {  // uniform over the wave
+      int my_e = 0;
+      float my_g = 0.f;
+      if (l < na) {
+        const size_t o = static_cast<size_t>(t) * K + k0 + a0 + l;
+        const int e = le[o];
+        my_e = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
+        my_g = lg[o];
+      }
+      Frag f[kTokRing];
+      const float my_h = token_dots<T, EPL, NT>(xf, W, my_e, na, d, l, f);
+      float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
+      if constexpr (GLU) my_c *= token_dots<T, EPL, NT>(xf, U, my_e, na, d, l, f);
+      if (l < na) {
+        sc[a0 + l] = my_c;
+        se[a0 + l] = my_e;
+      }
+    }
+    __syncthreads();
+    const int my_e = l < n ? se[l] : 0;
+    const float my_c = l < n ? sc[l] : 0.f;
+    FragB g[kSplitRing];
+#pragma unroll
+    for (int s = 0; s < kSplitRing - 1; ++s)
+      if (s < n)
+        g[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d + col0, l);
+    for (int i = 0; i < n; i += kSplitRing) {
+#pragma unroll
+      for (int s = 0; s < kSplitRing; ++s) {
+        const int ii = i + s;
+        if (ii >= n) break;
+        if (ii + kSplitRing - 1 < n)
+          g[(s + kSplitRing - 1) % kSplitRing].template fetch<NT>(
+              V + static_cast<size_t>(rdlane(my_e, ii + kSplitRing - 1)) * d + col0, l);
+        const float c = rdlane(my_c, ii);
+#pragma unroll
+        for (int q = 0; q < EPLB; ++q) acc[q] = fmaf(c, g[s].get(q), acc[q]);
+      }
+    }
+    __syncthreads();  // the next chunk's coefficients overwrite sc / se
+  }
+  store_row<T, EPLB, true>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
+}
+
+// Waves per token for the token-centric form: 1 (token_kernel) from 4096
+// tokens up; below, enough for about 8192 waves, at most 8, and at most one
+// per 64 columns.  Measured (token form, us per call): decode (L = 256,
+// d = 2048) 33.9 / 25.2 / 23.6 / 22.2 with 1 / 2 / 4 / 8 waves per token;
+// small (L = 4096, d = 1024) 74.1 / 75.3 / 73.9 / 79.4; mid and large lose
+// 4-95 % with any split.
+static int token_split_waves(int L, int d) {
+  if (L >= 4096) return 1;
+  int ws = 1;
+  while (ws < 8 && static_cast<long long>(L) * ws < 8192 && d / (64 * ws * 2) >= 1) ws *= 2;
+  return ws;
+}
+
 // The token lists: the caller's flattened selection (fe, fg) when given,
 // else the schedule inverted into the workspace (ws: M ids, then M gates).
 template <typename T, bool GLU, bool NT>
@@ -333,6 +425,33 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
                                                                             lg);
     fe = le;
     fg = lg;
+  }
+  const int nw = token_split_waves(L, d);
+  if (nw > 1) {
+    const unsigned grid = static_cast<unsigned>(L);
+#define OMNI_SPLIT(EPL_, WS_)                                                                   \
+  token_split_kernel<T, EPL_, WS_, GLU, NT><<<grid, 64 * WS_, 0, s>>>(x, w, u, v, fe, fg, L, K, \
+                                                                       d, N, y, accumulate)
+#define OMNI_SPLIT_WS(EPL_)                                                                     \
+  if (nw == 2) { if constexpr (EPL_ >= 2) OMNI_SPLIT(EPL_, 2); }                                \
+  else if (nw == 4) { if constexpr (EPL_ >= 4) OMNI_SPLIT(EPL_, 4); }                           \
+  else { if constexpr (EPL_ >= 8) OMNI_SPLIT(EPL_, 8); }
+    switch (d) {
+      case 128: OMNI_SPLIT_WS(2) break;
+      case 256: OMNI_SPLIT_WS(4) break;
+      case 512: OMNI_SPLIT_WS(8) break;
+      case 1024: OMNI_SPLIT_WS(16) break;
+      case 2048:
+        if constexpr (sizeof(T) == 2) {
+          OMNI_SPLIT_WS(32)
+          break;
+        }
+        return false;
+      default: return false;
+    }
+#undef OMNI_SPLIT_WS
+#undef OMNI_SPLIT
+    return true;
   }
   const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
   // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
@@ -370,9 +489,13 @@ bool stream_rows(long long M, long long N) {
 int auto_exec_mode(int bf16, int L, int d, int K) {
   (void)K;
   // One wave per token keeps 3072 waves resident (3 per SIMD); it beat the
-  // two-kernel form from L = 8192 tokens of d = 2048 up (2.7 resident rounds),
-  // and lost at L = 4096, d = 1024 and at L = 256.
-  if (L >= 8192 && d >= 1024 && token_centric_supported(bf16, d)) return 2;
+  // two-kernel form from L = 8192 tokens of d = 2048 up (2.7 resident rounds)
+  // and lost at L = 4096, d = 1024.  Below 4096 tokens each token is split
+  // over several waves (token_split_kernel), which beat the two-kernel form
+  // at L = 256, d = 2048 (22 against 27 us) and L = 64, d = 128 (12.5
+  // against 15 us).
+  if (!token_centric_supported(bf16, d)) return 1;
+  if ((L >= 8192 && d >= 1024) || L < 4096) return 2;
   return 1;
 }
 

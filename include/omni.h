@@ -237,10 +237,11 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *   OMNI_EXEC_TOKEN_CENTRIC: the per-token task lists are the schedule's
  *     flat_expert / flat_gate when present, else the schedule's sorted order
  *     inverted through task_index (one more kernel); then one wave per
- *     token assembles its experts: x_t stays in
- *     registers, the token's W rows give the K coefficients, its V rows are
- *     summed into y_t.  Needs d * element size <= 4096 bytes (else
- *     UNSUPPORTED).
+ *     token assembles its experts: x_t stays in registers, the token's W
+ *     rows give the K coefficients, its V rows are summed into y_t.  Below
+ *     4096 tokens each token gets several waves: its tasks are split over
+ *     them for the coefficients, the columns of y_t for the sum.  Needs
+ *     d * element size <= 4096 bytes (else UNSUPPORTED).
  *   OMNI_EXEC_AUTO: the form omni_atomic_forward_mode() names for the shape
  *     (the one that measured faster on MI355X).
  * Both forms evaluate every coefficient and every y element with the same

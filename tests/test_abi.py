@@ -170,12 +170,14 @@ def test_atomic_forward_argument_checks(lib):
 
 def test_atomic_forward_auto_mode(lib):
     mode = lib.omni_atomic_forward_mode
-    # the measured crossover: token-centric from L = 8192 tokens of d >= 1024
+    # the measured crossovers: token-centric from L = 8192 tokens of d >= 1024,
+    # and below 4096 tokens (each token split over several waves)
     assert mode(1, 8192, 2048, 1 << 20, 64, 256) == 2      # large
     assert mode(1, 16384, 2048, 1 << 18, 64, 128) == 2     # mid
     assert mode(1, 4096, 1024, 1 << 14, 32, 64) == 1       # small
-    assert mode(1, 256, 2048, 1 << 20, 64, 64) == 1        # decode
-    assert mode(0, 64, 128, 1024, 8, 16) == 1              # tiny float32
+    assert mode(1, 256, 2048, 1 << 20, 64, 64) == 2        # decode
+    assert mode(0, 64, 128, 1024, 8, 16) == 2              # tiny float32
+    assert mode(0, 64, 2048, 1024, 8, 16) == 1             # float32 row over 4 KiB
     assert mode(1, 8192, 4096, 1 << 20, 64, 256) == 1      # row over 4 KiB
     assert mode(0, 8192, 2048, 1 << 20, 64, 256) == 1      # float32 row over 4 KiB
     assert mode(3, 8192, 2048, 1 << 20, 64, 256) == 0      # bad dtype
