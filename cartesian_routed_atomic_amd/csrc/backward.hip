@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
   const float my_ds = my_g * (my_dg - gdg);
 
   const int my_ri = my_e / Nc, my_ci = my_e - (my_e / Nc) * Nc;
-  store_row<T, EPL, false>(acc, dx + static_cast<size_t>(t) * d, 0);
+  store_row<T, EPL, kStorePlain>(acc, dx + static_cast<size_t>(t) * d, 0);
   // the token's logit gradients: dz_r[t, i] is the sum of dS over the token's
   // tasks in grid row i (summed in task order, stored by the first such task),
   // dz_c likewise; written to row t of dz (grid rows, then grid columns, for
@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256) void seg_reduce_kernel(
           dst_v = part + static_cast<size_t>((2 * wv + slot) * 2) * d + col0;
           dst_w = dst_v + d;
         }
-        store_row<float, EPL, false>(av, dst_v, 0);
-        store_row<T, EPL, false>(aw, dst_w, 0);
+        store_row<float, EPL, kStorePlain>(av, dst_v, 0);
+        store_row<T, EPL, kStorePlain>(aw, dst_w, 0);
 #pragma unroll
         for (int q = 0; q < EPL; ++q) av[q] = aw[q] = 0.f;
         seg_start = k + 1;
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(
     const int ce = min((c + 1) * 64, M);
     if (ce >= M || out_row_of(task_expert, rank, ce, n_ids, n_rows) != row) break;
   }
-  store_row<float, EPL, false>(tv, dv + static_cast<size_t>(row) * d + col0, 0);
-  store_row<T, EPL, false>(tw, dw + static_cast<size_t>(row) * d + col0, 0);
+  store_row<float, EPL, kStorePlain>(tv, dv + static_cast<size_t>(row) * d + col0, 0);
+  store_row<T, EPL, kStorePlain>(tw, dw + static_cast<size_t>(row) * d + col0, 0);
 }
 
 // ------------------------------------------------------------ host side

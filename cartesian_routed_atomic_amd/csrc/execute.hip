@@ -151,7 +151,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
       }
     }
   }
-  store_row<T, EPL, true>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
+  store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
+                                                  accumulate);
 }
 
 // Inverse of the schedule's task permutation: each token's (expert, gate)
@@ -250,7 +251,8 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
       }
     }
   }
-  store_row<T, EPL, true>(acc, y + static_cast<size_t>(t) * d, accumulate);
+  store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d,
+                                                  accumulate);
 }
 
 static inline int clampi(long long v, int lo, int hi) {
@@ -394,7 +396,8 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     }
     __syncthreads();  // the next chunk's coefficients overwrite sc / se
   }
-  store_row<T, EPLB, true>(acc, y + static_cast<size_t>(t) * d + col0, accumulate);
+  store_row<T, EPLB, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
+                                                   accumulate);
 }
 
 // Waves per token for the token-centric form: 1 (token_kernel) from 4096

@@ -117,11 +117,21 @@ __device__ __forceinline__ float rdlane(float v, int i) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
 }
 
+// How store_row writes an output row (measured on MI355X, with the random
+// 4 KiB expert-row reads of the executor running beside the writes):
+//   kStorePlain   ordinary stores (the backward: its rows are re-read soon,
+//                 and its 6.7 GB dW / dV stream lost 9 % with either hint);
+//   kStoreNT      the nontemporal hint (executor y rows in most shapes);
+//   kStoreDevice  buffer stores with the sc1 scope bit (executor y rows where
+//                 the expert rows are streamed: 2 % faster than kStoreNT
+//                 there, 9 % slower at heavy expert reuse).
+// kStoreDevice builds a buffer descriptor from yrow, so yrow must be the
+// same in every lane of the wave (one output row or row slice per wave).
+enum StorePolicy { kStorePlain = 0, kStoreNT = 1, kStoreDevice = 2 };
+
 // Store (or add) a lane's accumulators to its columns of a y row, in the
-// RowFrag element layout, with 16-byte stores where the layout allows.  NT:
-// the stores carry the nontemporal hint (the executor's y rows: written once,
-// read by no later kernel of the call).
-template <typename T, int EPL, bool NT>
+// RowFrag element layout, with 16-byte stores where the layout allows.
+template <typename T, int EPL, int POL>
 __device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __restrict__ yrow,
                                           int accumulate) {
   constexpr int VEC = RowFrag<T, EPL>::VEC, NCH = RowFrag<T, EPL>::NCH;
@@ -138,7 +148,14 @@ __device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __rest
           const float4 o = *reinterpret_cast<const float4*>(p + j);
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
         }
-        if constexpr (NT) {
+        if constexpr (POL == kStoreDevice) {
+          const __amdgpu_buffer_rsrc_t rs =
+              __builtin_amdgcn_make_buffer_rsrc(yrow, 0, NCH * 64 * VEC * 4, 0x00020000);
+          const u32x4 nv = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                            __float_as_uint(v.w)};
+          __builtin_amdgcn_raw_buffer_store_b128(nv, rs, (c * 64 * VEC + l * VEC + j) * 4, 0,
+                                                 16 /* sc1 */);
+        } else if constexpr (POL == kStoreNT) {
           const f32x4 nv = {v.x, v.y, v.z, v.w};
           __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(p + j));
         } else {
@@ -149,7 +166,7 @@ __device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __rest
 #pragma unroll
       for (int q = 0; q < VEC; ++q) {
         const float v = acc[c * VEC + q] + (accumulate ? p[q] : 0.f);
-        if constexpr (NT) __builtin_nontemporal_store(v, p + q);
+        if constexpr (POL != kStorePlain) __builtin_nontemporal_store(v, p + q);
         else p[q] = v;
       }
     }
