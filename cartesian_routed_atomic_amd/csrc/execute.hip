@@ -178,27 +178,51 @@ constexpr int kTokRing = 6;  // row slots per wave in the token-centric kernel: 
 // h_k = x_t . M[e_k] for the n tasks of a chunk (expert e_k in lane k),
 // streamed through the row ring with kTokRing - 1 rows in flight; h_k ends
 // in lane k.
-template <typename T, int EPL, bool NT>
+template <typename T, int EPL, bool NT, int RING>
 __device__ __forceinline__ float token_dots(const RowFrag<T, EPL>& xf, const T* __restrict__ M,
                                             int my_e, int n, int d, int l,
-                                            RowFrag<T, EPL> (&f)[kTokRing]) {
+                                            RowFrag<T, EPL> (&f)[RING]) {
   float my_h = 0.f;
 #pragma unroll
-  for (int s = 0; s < kTokRing - 1; ++s)
+  for (int s = 0; s < RING - 1; ++s)
     if (s < n) f[s].template fetch<NT>(M + static_cast<size_t>(rdlane(my_e, s)) * d, l);
-  for (int i = 0; i < n; i += kTokRing) {
+  for (int i = 0; i < n; i += RING) {
 #pragma unroll
-    for (int s = 0; s < kTokRing; ++s) {
+    for (int s = 0; s < RING; ++s) {
       const int ii = i + s;
       if (ii >= n) break;
-      if (ii + kTokRing - 1 < n)
-        f[(s + kTokRing - 1) % kTokRing].template fetch<NT>(
-            M + static_cast<size_t>(rdlane(my_e, ii + kTokRing - 1)) * d, l);
+      if (ii + RING - 1 < n)
+        f[(s + RING - 1) % RING].template fetch<NT>(
+            M + static_cast<size_t>(rdlane(my_e, ii + RING - 1)) * d, l);
       const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
       if (l == ii) my_h = h;
     }
   }
   return my_h;
+}
+
+// y_t (+)= sum_k c_k V[e_k] over the n tasks of a chunk (c_k, e_k in lane k),
+// the V rows streamed through the ring, fp32 accumulation in k order.
+template <typename T, int EPL, bool NT, int RING>
+__device__ __forceinline__ void token_gather(const T* __restrict__ V, int my_e, float my_c, int n,
+                                             int d, int l, RowFrag<T, EPL> (&f)[RING],
+                                             float (&acc)[EPL]) {
+#pragma unroll
+  for (int s = 0; s < RING - 1; ++s)
+    if (s < n) f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
+  for (int i = 0; i < n; i += RING) {
+#pragma unroll
+    for (int s = 0; s < RING; ++s) {
+      const int ii = i + s;
+      if (ii >= n) break;
+      if (ii + RING - 1 < n)
+        f[(s + RING - 1) % RING].template fetch<NT>(
+            V + static_cast<size_t>(rdlane(my_e, ii + RING - 1)) * d, l);
+      const float c = rdlane(my_c, ii);
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
+    }
+  }
 }
 
 // GLU: the SwiGLU-gated variant, coefficient g silu(x . W[e]) (x . U[e]).
@@ -229,27 +253,12 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
       my_g = lg[o];
     }
     // pass A: h_k = x_t . W[e_k]; h_k ends in lane k
-    const float my_h = token_dots<T, EPL, NT>(xf, W, my_e, n, d, l, f);
+    const float my_h = token_dots<T, EPL, NT, kTokRing>(xf, W, my_e, n, d, l, f);
     float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
     // gated variant, pass A': the up factor x_t . U[e_k]
-    if constexpr (GLU) my_c *= token_dots<T, EPL, NT>(xf, U, my_e, n, d, l, f);
+    if constexpr (GLU) my_c *= token_dots<T, EPL, NT, kTokRing>(xf, U, my_e, n, d, l, f);
     // pass B: y_t += coef_k * V[e_k]
-#pragma unroll
-    for (int s = 0; s < kTokRing - 1; ++s)
-      if (s < n) f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
-    for (int i = 0; i < n; i += kTokRing) {
-#pragma unroll
-      for (int s = 0; s < kTokRing; ++s) {
-        const int ii = i + s;
-        if (ii >= n) break;
-        if (ii + kTokRing - 1 < n)
-          f[(s + kTokRing - 1) % kTokRing].template fetch<NT>(
-              V + static_cast<size_t>(rdlane(my_e, ii + kTokRing - 1)) * d, l);
-        const float c = rdlane(my_c, ii);
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
-      }
-    }
+    token_gather<T, EPL, NT, kTokRing>(V, my_e, my_c, n, d, l, f, acc);
   }
   store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d,
                                                   accumulate);
@@ -320,6 +329,62 @@ size_t atomic_forward_ws_bytes(int L, int K) {
   return 2 * ((m + 255) & ~static_cast<size_t>(255));
 }
 
+constexpr int kMultiTokens = 4;  // tokens per wave in token_multi_kernel
+constexpr int kMultiRing = 3;    // its row slots: two rows in flight per wave, 8 waves per CU
+
+// Token-centric form with kMultiTokens tokens per wave: each wave runs
+// token_kernel's passes for its tokens one after another and keeps their y
+// rows in registers until the last one is done.  With every wave resident
+// from the start (2 per SIMD) the y writes of the call come together at its
+// end instead of being spread through the random-row read stream, where each
+// write costs the HBM a read / write turnaround.  Every coefficient and y
+// element goes through token_kernel's operations in the same order, so y is
+// bit-identical to it.
+template <typename T, int EPL, bool GLU, bool NT>
+__global__ __launch_bounds__(256, 2) void token_multi_kernel(
+    const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
+    const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
+    int K, int d, int N, float* __restrict__ y, int accumulate) {
+  using Frag = RowFrag<T, EPL>;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = lane();
+  const int t0 = wv * kMultiTokens;
+  if (t0 >= L) return;
+  float acc[kMultiTokens][EPL];
+#pragma unroll
+  for (int tt = 0; tt < kMultiTokens; ++tt)
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) acc[tt][q] = 0.f;
+  Frag f[kMultiRing];
+#pragma unroll
+  for (int tt = 0; tt < kMultiTokens; ++tt) {
+    const int t = t0 + tt;
+    if (t >= L) continue;  // uniform over the wave
+    Frag xf;
+    xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int n = min(64, K - k0);
+      int my_e = 0;
+      float my_g = 0.f;
+      if (l < n) {
+        const size_t o = static_cast<size_t>(t) * K + k0 + l;
+        const int e = le[o];
+        my_e = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
+        my_g = lg[o];
+      }
+      const float my_h = token_dots<T, EPL, NT, kMultiRing>(xf, W, my_e, n, d, l, f);
+      float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
+      if constexpr (GLU) my_c *= token_dots<T, EPL, NT, kMultiRing>(xf, U, my_e, n, d, l, f);
+      token_gather<T, EPL, NT, kMultiRing>(V, my_e, my_c, n, d, l, f, acc[tt]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kMultiTokens; ++tt)
+    if (t0 + tt < L)
+      store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(
+          acc[tt], y + static_cast<size_t>(t0 + tt) * d, accumulate);
+}
+
 constexpr int kSplitRing = 8;  // pass-B row-slice slots per wave in token_split_kernel
 
 // Token-centric form for few tokens: one workgroup of WS waves per token.
@@ -365,9 +430,9 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
         my_g = lg[o];
       }
       Frag f[kTokRing];
-      const float my_h = token_dots<T, EPL, NT>(xf, W, my_e, na, d, l, f);
+      const float my_h = token_dots<T, EPL, NT, kTokRing>(xf, W, my_e, na, d, l, f);
       float my_c = my_g * (my_h / (1.f + __expf(-my_h)));
-      if constexpr (GLU) my_c *= token_dots<T, EPL, NT>(xf, U, my_e, na, d, l, f);
+      if constexpr (GLU) my_c *= token_dots<T, EPL, NT, kTokRing>(xf, U, my_e, na, d, l, f);
       if (l < na) {
         sc[a0 + l] = my_c;
         se[a0 + l] = my_e;
@@ -399,6 +464,12 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
   store_row<T, EPLB, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
                                                    accumulate);
 }
+
+// From 8192 tokens up the token-centric form runs kMultiTokens tokens per
+// wave (token_multi_kernel).  Measured at L = 8192, d = 2048, N = 2^20:
+// 702 us with one token per wave, 690 / 677 us with two (ring of 4 / 6 rows),
+// 658 us with four (ring of 3 or 4).
+static bool token_multi_tokens(int L) { return L >= 8192; }
 
 // Waves per token for the token-centric form: 1 (token_kernel) from 4096
 // tokens up; below, enough for about 8192 waves, at most 8, and at most one
@@ -456,21 +527,32 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
 #undef OMNI_SPLIT
     return true;
   }
+  const bool multi = token_multi_tokens(L);
   const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
+  const unsigned mblk = static_cast<unsigned>((L + 4 * kMultiTokens - 1) / (4 * kMultiTokens));
   // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
+#define OMNI_TOK(EPL_)                                                                         \
+  if (multi)                                                                                   \
+    token_multi_kernel<T, EPL_, GLU, NT><<<mblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N,  \
+                                                              y, accumulate);                  \
+  else                                                                                         \
+    token_kernel<T, EPL_, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y,     \
+                                                        accumulate);
   switch (d) {
-#define OMNI_TOK(D_, EPL_) case D_: token_kernel<T, EPL_, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y, accumulate); break;
-    OMNI_TOK(64, 1) OMNI_TOK(128, 2) OMNI_TOK(256, 4) OMNI_TOK(512, 8) OMNI_TOK(1024, 16)
-#undef OMNI_TOK
+    case 64: OMNI_TOK(1) break;
+    case 128: OMNI_TOK(2) break;
+    case 256: OMNI_TOK(4) break;
+    case 512: OMNI_TOK(8) break;
+    case 1024: OMNI_TOK(16) break;
     case 2048:
       if constexpr (sizeof(T) == 2) {
-        token_kernel<T, 32, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y,
-                                                          accumulate);
+        OMNI_TOK(32)
         break;
       }
       return false;
     default: return false;
   }
+#undef OMNI_TOK
   return true;
 }
 

@@ -115,6 +115,10 @@ CASES = {
     # the largest grid line count per axis (2048: 32 slots per lane in the top-K)
     "grid2048x64": custom(L=100, d=128, Nr=2048, Nc=64, kprime=64, K=64, B=100, dtype="bf16",
                           index=209),
+    # from 8192 tokens the token-centric form runs four tokens per wave: a
+    # ragged last wave and workgroup (8205 = 512 * 16 + 13)
+    "multi_ragged": custom(L=8205, d=256, Nr=64, Nc=64, kprime=8, K=8, B=16, dtype="bf16",
+                           index=210),
 }
 
 
