@@ -34,8 +34,9 @@ EXEC_SRCS = [os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
 EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
-    "token": "omni_atomic_forward, token-centric: token_kernel (token lists read from the "
-             "flattened selection the schedule carries)",
+    "token": "omni_atomic_forward, token-centric: one kernel (token_multi_kernel from 8192 "
+             "tokens, four tokens per wave; token lists read from the flattened selection the "
+             "schedule carries)",
 }
 
 
