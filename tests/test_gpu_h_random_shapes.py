@@ -78,6 +78,9 @@ EXEC_SHAPES = [
     (8200, 1024, 12000, 4, "f32"),
     # 327,680 tasks over 600,000 experts: the expert rows are streamed
     (8192, 256, 600000, 40, "bf16"),
+    # more than 64 tasks per token (the kernels walk them 64 at a time)
+    (8193, 128, 40000, 70, "bf16"),
+    (100, 256, 5000, 100, "bf16"),
 ]
 
 
