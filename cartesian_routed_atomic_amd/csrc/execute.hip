@@ -31,9 +31,17 @@
 //   but x once per token and no coefficient round trip.  When the tasks reuse
 //   experts little (uniform routing over N = 2^20 experts: 1.28 tasks per
 //   active expert) both forms are bound by the DRAM rate for random 4 KiB
-//   rows, and this one does less other work; with few tokens it cannot fill
-//   the chip.  Both forms sum y in the same order with the same fragment
-//   layout, so they give bit-identical y.
+//   rows, and this one does less other work.  Three kernels share its
+//   passes: token_kernel (one token per wave), token_multi_kernel (from 8192
+//   tokens: four tokens per wave, their y rows written together at the end)
+//   and token_split_kernel (below 4096 tokens: each token's tasks and
+//   columns split over several waves, so that few tokens still fill the
+//   chip).  Every form sums y in the same order with the same per-element
+//   operations, so they give bit-identical y.
+//
+// Cache hints: where the expert rows are rarely read twice (stream_rows)
+// they are loaded with the nontemporal hint and y is stored with the sc1
+// scope bit; elsewhere y carries the nontemporal hint (store_row policies).
 #include "device.hpp"
 #include "launch.hpp"
 #include "rowfrag.hpp"
