@@ -113,3 +113,15 @@ def test_random_executor_forms_agree(L, d, N, K, dt):
     e = rel_err(ref[toks], want)
     log(f"  forms {sorted(ys)} bit-identical; y max|d|/max|y| {e:.2e} (tol {TOL_Y[dt]})")
     assert e <= TOL_Y[dt]
+    # accumulate onto a seeded y0: every form the same bits, y0 + routed output
+    y0 = np.random.default_rng(seed + 6).standard_normal((L, d)).astype(np.float32)
+    modes = ["expert"] + (["token"] if "token" in ys else [])
+    acc = {m: B.atomic_forward(tx, tw, tv, sched, y=dev(y0), accumulate=True, mode=m)
+           for m in modes}
+    torch.cuda.synchronize()
+    ra = host(acc["expert"])
+    for m, y in acc.items():
+        np.testing.assert_array_equal(host(y).view(np.uint32), ra.view(np.uint32), err_msg=m)
+    ea = rel_err(ra[toks], want + y0[toks])
+    log(f"  accumulate: forms bit-identical, max|d|/max|y| {ea:.2e}")
+    assert ea <= TOL_Y[dt]
