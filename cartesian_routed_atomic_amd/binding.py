@@ -269,6 +269,15 @@ def schedule_tasks(expert_idx, gate, N, B, sched=None, stream=None, grouping="ac
     return sched
 
 
+def _same_shape_schedule(sched, L, N):
+    # the kernels index x, W, V with the schedule's token and expert ids
+    if sched.L != L or sched.N != N:
+        raise ValueError(f"the schedule was built for L={sched.L}, N={sched.N}; "
+                         f"x and the expert matrices give L={L}, N={N}")
+    if sched.task_index is None:
+        raise ValueError("the schedule must carry task_index")
+
+
 def _exec_mode(mode):
     if mode not in EXEC_MODES:
         raise ValueError(f"mode must be one of {sorted(EXEC_MODES)}, got {mode!r}")
@@ -294,8 +303,7 @@ def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, str
     _req(x, "x")
     _req(w, "w", x.dtype, (N, d))
     _req(v, "v", x.dtype, (N, d))
-    if sched.task_index is None:
-        raise ValueError("the schedule must carry task_index")
+    _same_shape_schedule(sched, L, N)
     code = _exec_mode(mode)
     if y is None:
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
@@ -321,8 +329,7 @@ def atomic_forward_glu(x, w, u, v, sched, y=None, accumulate=False, workspace=No
     _req(x, "x")
     for name, t in (("w", w), ("u", u), ("v", v)):
         _req(t, name, x.dtype, (N, d))
-    if sched.task_index is None:
-        raise ValueError("the schedule must carry task_index")
+    _same_shape_schedule(sched, L, N)
     if y is None:
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
     _req(y, "y", torch.float32, (L, d))

@@ -281,3 +281,16 @@ def test_flat_router_argument_checks(lib):
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(L=0, x=None, idx=None, n=lib.omni_flat_router_workspace(1, 0, 1000)) == B.OMNI_OK
     assert call(L=0, x=None, idx=None, ws=None, n=0) == B.OMNI_OK
+
+
+def test_binding_refuses_a_schedule_of_another_shape():
+    # the executor indexes x, W and V with the schedule's token and expert ids
+    import types
+    sched = types.SimpleNamespace(L=4, N=100, task_index=object())
+    B._same_shape_schedule(sched, 4, 100)
+    with pytest.raises(ValueError):
+        B._same_shape_schedule(sched, 5, 100)
+    with pytest.raises(ValueError):
+        B._same_shape_schedule(sched, 4, 99)
+    with pytest.raises(ValueError):
+        B._same_shape_schedule(types.SimpleNamespace(L=4, N=100, task_index=None), 4, 100)
