@@ -120,7 +120,8 @@ __device__ __forceinline__ float rdlane(float v, int i) {
 // How store_row writes an output row (measured on MI355X, with the random
 // 4 KiB expert-row reads of the executor running beside the writes):
 //   kStorePlain   ordinary stores (the backward: its rows are re-read soon,
-//                 and its 6.7 GB dW / dV stream lost 9 % with either hint);
+//                 and its 6.7 GB dW / dV stream lost 9 % with the
+//                 nontemporal hint and 68 % with the sc1 bit);
 //   kStoreNT      the nontemporal hint (executor y rows in most shapes);
 //   kStoreDevice  buffer stores with the sc1 scope bit (executor y rows where
 //                 the expert rows are streamed: 2 % faster than kStoreNT
