@@ -37,6 +37,8 @@ EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "token": "omni_atomic_forward, token-centric: one kernel (token_multi_kernel from 8192 "
              "tokens, four tokens per wave; token lists read from the flattened selection the "
              "schedule carries)",
+    "hybrid": "omni_atomic_forward, hybrid: hot experts as two MFMA products (hot_gemm_kernel), "
+              "the other tasks through the token-centric kernels",
 }
 
 
@@ -218,7 +220,7 @@ def main():
               "schedule": ev_time(stage_schedule), "execute": ev_time(stage_execute)}
     # the executor call alone, in each form (the step runs `form`)
     forms_ms = {}
-    for f in ("expert", "token"):
+    for f in ("expert", "token", "hybrid"):
         try:
             forms_ms[f] = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y,
                                                            workspace=exec_ws, mode=f), reps=20)

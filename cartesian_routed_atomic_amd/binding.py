@@ -17,9 +17,9 @@ LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
-EXEC_MODES = {"auto": 0, "expert": 1, "token": 2}  # omni_exec_mode
+EXEC_MODES = {"auto": 0, "expert": 1, "token": 2, "hybrid": 3}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -285,19 +285,20 @@ def _exec_mode(mode):
 
 
 def atomic_forward_mode(dtype, L, d, N, K, B):
-    """omni_atomic_forward_mode: the form mode="auto" runs ("expert" / "token")."""
+    """omni_atomic_forward_mode: the form mode="auto" runs ("expert" / "token" / "hybrid")."""
     code = torch.bfloat16 if dtype == torch.bfloat16 else torch.float32
     m = lib().omni_atomic_forward_mode(OMNI_BF16 if code == torch.bfloat16 else OMNI_F32,
                                        L, d, N, K, B)
     if m == 0:
         raise ValueError("invalid shape for omni_atomic_forward_mode")
-    return {1: "expert", 2: "token"}[m]
+    return {1: "expert", 2: "token", 3: "hybrid"}[m]
 
 
 def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, stream=None,
                    mode="auto"):
     """omni_atomic_forward: returns y [L, d] float32 (y += routed if accumulate).
-    mode: "auto", "expert" (expert-centric) or "token" (token-centric)."""
+    mode: "auto", "expert" (expert-centric), "token" (token-centric) or "hybrid"
+    (hot experts as dense MFMA products, bf16 only)."""
     L, d = x.shape
     N = w.shape[0]
     _req(x, "x")

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 11;
+constexpr int kAbiVersion = 12;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -160,13 +160,17 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
 int omni_atomic_forward_mode(omni_dtype dt, int L, int d, int N, int K, int B) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
   if (!schedule_args_ok(L, K, N, B) || d < 1) return 0;
-  return omni::auto_exec_mode(dt == OMNI_BF16, L, d, K);
+  return omni::auto_exec_mode(dt == OMNI_BF16, L, d, N, K);
 }
 
 size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B) {
-  (void)dt; (void)d; (void)N; (void)B;
+  (void)B;
   if (L <= 0 || K < 1 || !fits_i32(static_cast<long long>(L) * K)) return 0;
-  return omni::atomic_forward_ws_bytes(L, K);
+  size_t n = omni::atomic_forward_ws_bytes(L, K);
+  // the hybrid form's hot-expert buffers (bf16 shapes it supports)
+  if (dt == OMNI_BF16 && N >= 1 && omni::token_centric_supported(1, d))
+    n += omni::hot_ws_bytes(L, K, d, N);
+  return n;
 }
 
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B, const void* x,
@@ -175,7 +179,7 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                                 size_t ws_bytes, hipStream_t stream) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
   if (mode != OMNI_EXEC_AUTO && mode != OMNI_EXEC_EXPERT_CENTRIC &&
-      mode != OMNI_EXEC_TOKEN_CENTRIC)
+      mode != OMNI_EXEC_TOKEN_CENTRIC && mode != OMNI_EXEC_HYBRID)
     return OMNI_ERR_INVALID_ARG;
   if (!schedule_args_ok(L, K, N, B) || d < 1) return OMNI_ERR_INVALID_ARG;
   if (!w || !v || !sched) return OMNI_ERR_INVALID_ARG;
@@ -188,9 +192,11 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
     return OMNI_ERR_INVALID_ARG;
   if (d < 64 || d > 4096 || (d & (d - 1)) != 0) return OMNI_ERR_UNSUPPORTED;
   const int bf16 = dt == OMNI_BF16;
-  const int form = mode == OMNI_EXEC_AUTO ? omni::auto_exec_mode(bf16, L, d, K) : mode;
-  if (form == OMNI_EXEC_TOKEN_CENTRIC && !omni::token_centric_supported(bf16, d))
+  const int form = mode == OMNI_EXEC_AUTO ? omni::auto_exec_mode(bf16, L, d, N, K) : mode;
+  if ((form == OMNI_EXEC_TOKEN_CENTRIC || form == OMNI_EXEC_HYBRID) &&
+      !omni::token_centric_supported(bf16, d))
     return OMNI_ERR_UNSUPPORTED;
+  if (form == OMNI_EXEC_HYBRID && !bf16) return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(v)) return OMNI_ERR_INVALID_ARG;
   if (L > 0 && !aligned16(y)) return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;

@@ -239,19 +239,23 @@ template <typename T, int EPL, bool GLU, bool NT>
 __global__ __launch_bounds__(256, 3) void token_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
     const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
-    int K, int d, int N, float* __restrict__ y, int accumulate) {
+    int K, int d, int N, float* __restrict__ y, int accumulate,
+    const int32_t* __restrict__ kcnt, const int32_t* __restrict__ acc_dev) {
   using Frag = RowFrag<T, EPL>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
   if (t >= L) return;
+  const int Kt = kcnt ? kcnt[t] : K;
+  const int accum = acc_dev ? *acc_dev : accumulate;
+  if (Kt == 0 && accum) return;  // nothing to add to this row
   Frag xf;
   xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
   float acc[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
   Frag f[kTokRing];  // one ring for both passes keeps the register count down
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    const int n = min(64, K - k0);
+  for (int k0 = 0; k0 < Kt; k0 += 64) {
+    const int n = min(64, Kt - k0);
     int my_e = 0;
     float my_g = 0.f;
     if (l < n) {
@@ -268,8 +272,7 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
     // pass B: y_t += coef_k * V[e_k]
     token_gather<T, EPL, NT, kTokRing>(V, my_e, my_c, n, d, l, f, acc);
   }
-  store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d,
-                                                  accumulate);
+  store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d, accum);
 }
 
 static inline int clampi(long long v, int lo, int hi) {
@@ -352,7 +355,8 @@ template <typename T, int EPL, bool GLU, bool NT>
 __global__ __launch_bounds__(256, 2) void token_multi_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
     const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
-    int K, int d, int N, float* __restrict__ y, int accumulate) {
+    int K, int d, int N, float* __restrict__ y, int accumulate,
+    const int32_t* __restrict__ kcnt, const int32_t* __restrict__ acc_dev) {
   using Frag = RowFrag<T, EPL>;
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
@@ -370,8 +374,9 @@ __global__ __launch_bounds__(256, 2) void token_multi_kernel(
     if (t >= L) continue;  // uniform over the wave
     Frag xf;
     xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
-    for (int k0 = 0; k0 < K; k0 += 64) {
-      const int n = min(64, K - k0);
+    const int Kt = kcnt ? kcnt[t] : K;
+    for (int k0 = 0; k0 < Kt; k0 += 64) {
+      const int n = min(64, Kt - k0);
       int my_e = 0;
       float my_g = 0.f;
       if (l < n) {
@@ -386,11 +391,12 @@ __global__ __launch_bounds__(256, 2) void token_multi_kernel(
       token_gather<T, EPL, NT, kMultiRing>(V, my_e, my_c, n, d, l, f, acc[tt]);
     }
   }
+  const int accum = acc_dev ? *acc_dev : accumulate;
 #pragma unroll
   for (int tt = 0; tt < kMultiTokens; ++tt)
     if (t0 + tt < L)
       store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(
-          acc[tt], y + static_cast<size_t>(t0 + tt) * d, accumulate);
+          acc[tt], y + static_cast<size_t>(t0 + tt) * d, accum);
 }
 
 constexpr int kSplitRing = 8;  // pass-B row-slice slots per wave in token_split_kernel
@@ -407,7 +413,8 @@ template <typename T, int EPL, int WS, bool GLU, bool NT>
 __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
     const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
-    int K, int d, int N, float* __restrict__ y, int accumulate) {
+    int K, int d, int N, float* __restrict__ y, int accumulate,
+    const int32_t* __restrict__ kcnt, const int32_t* __restrict__ acc_dev) {
   static_assert(EPL % WS == 0, "every wave needs at least one element per lane");
   constexpr int EPLB = EPL / WS;  // pass-B elements per lane
   using Frag = RowFrag<T, EPL>;
@@ -417,14 +424,17 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
   const int t = blockIdx.x;
   const int w = threadIdx.x >> 6, l = lane();
   if (t >= L) return;  // the whole workgroup leaves together
+  const int Kt = kcnt ? kcnt[t] : K;
+  const int accum = acc_dev ? *acc_dev : accumulate;
+  if (Kt == 0 && accum) return;  // nothing to add to this row (whole workgroup)
   Frag xf;
   xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
   const int col0 = w * 64 * EPLB;
   float acc[EPLB];
 #pragma unroll
   for (int q = 0; q < EPLB; ++q) acc[q] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    const int n = min(64, K - k0);
+  for (int k0 = 0; k0 < Kt; k0 += 64) {
+    const int n = min(64, Kt - k0);
     const int per = (n + WS - 1) / WS;
     const int a0 = w * per;
     const int na = max(0, min(per, n - a0));  // this wave's tasks: [a0, a0 + na)
@@ -470,7 +480,7 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     __syncthreads();  // the next chunk's coefficients overwrite sc / se
   }
   store_row<T, EPLB, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
-                                                   accumulate);
+                                                   accum);
 }
 
 // From 8192 tokens up the token-centric form runs kMultiTokens tokens per
@@ -498,7 +508,8 @@ template <typename T, bool GLU, bool NT>
 static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const int32_t* te,
                            const float* tg, const int32_t* ti, const int32_t* fe,
                            const float* fg, int M, int d, int L, int K, int N, void* ws, float* y,
-                           int accumulate, hipStream_t s) {
+                           int accumulate, hipStream_t s, const int32_t* kcnt = nullptr,
+                           const int32_t* acc_dev = nullptr, bool allow_multi = true) {
   if (!fe) {
     int32_t* le = static_cast<int32_t*>(ws);
     float* lg = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -513,7 +524,8 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
     const unsigned grid = static_cast<unsigned>(L);
 #define OMNI_SPLIT(EPL_, WS_)                                                                   \
   token_split_kernel<T, EPL_, WS_, GLU, NT><<<grid, 64 * WS_, 0, s>>>(x, w, u, v, fe, fg, L, K, \
-                                                                       d, N, y, accumulate)
+                                                                       d, N, y, accumulate, \
+                                                                       kcnt, acc_dev)
 #define OMNI_SPLIT_WS(EPL_)                                                                     \
   if (nw == 2) { if constexpr (EPL_ >= 2) OMNI_SPLIT(EPL_, 2); }                                \
   else if (nw == 4) { if constexpr (EPL_ >= 4) OMNI_SPLIT(EPL_, 4); }                           \
@@ -535,17 +547,17 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
 #undef OMNI_SPLIT
     return true;
   }
-  const bool multi = token_multi_tokens(L);
+  const bool multi = allow_multi && token_multi_tokens(L);
   const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
   const unsigned mblk = static_cast<unsigned>((L + 4 * kMultiTokens - 1) / (4 * kMultiTokens));
   // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
 #define OMNI_TOK(EPL_)                                                                         \
   if (multi)                                                                                   \
     token_multi_kernel<T, EPL_, GLU, NT><<<mblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N,  \
-                                                              y, accumulate);                  \
+                                                              y, accumulate, kcnt, acc_dev);   \
   else                                                                                         \
     token_kernel<T, EPL_, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y,     \
-                                                        accumulate);
+                                                        accumulate, kcnt, acc_dev);
   switch (d) {
     case 64: OMNI_TOK(1) break;
     case 128: OMNI_TOK(2) break;
@@ -579,7 +591,8 @@ bool stream_rows(long long M, long long N) {
   return M >= (1ll << 18) && M <= N;
 }
 
-int auto_exec_mode(int bf16, int L, int d, int K) {
+int auto_exec_mode(int bf16, int L, int d, int N, int K) {
+  (void)N;
   (void)K;
   // One wave per token keeps 3072 waves resident (3 per SIMD); it beat the
   // two-kernel form from L = 8192 tokens of d = 2048 up (2.7 resident rounds)
@@ -587,6 +600,9 @@ int auto_exec_mode(int bf16, int L, int d, int K) {
   // over several waves (token_split_kernel), which beat the two-kernel form
   // at L = 256, d = 2048 (22 against 27 us) and L = 64, d = 128 (12.5
   // against 15 us).
+  // The hybrid form (hot experts as MFMA products) is never picked: it lost
+  // to the token-centric form at every workload measured, the Zipf-routed
+  // one included (L = 16384, N = 2^18: 0.43 against 0.37 ms per call).
   if (!token_centric_supported(bf16, d)) return 1;
   if ((L >= 8192 && d >= 1024) || L < 4096) return 2;
   return 1;
@@ -611,7 +627,35 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
   const int acc = accumulate ? 1 : 0;
   const bool nt = stream_rows(M, N);
   bool ok;
-  if (mode == 2) {
+  if (mode == 3) {  // hybrid, bf16 only (checked by the caller)
+    const auto* xb = static_cast<const uint16_t*>(x);
+    const auto* wb = static_cast<const uint16_t*>(w);
+    const auto* vb = static_cast<const uint16_t*>(v);
+    const int32_t* fe = flat_expert;
+    const float* fg = flat_gate;
+    if (!fe) {
+      int32_t* le = static_cast<int32_t*>(ws);
+      float* lg = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           atomic_forward_ws_bytes(L, K) / 2);
+      unpermute_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(
+          task_expert, task_gate, task_index, M, N, le, lg);
+      fe = le;
+      fg = lg;
+    }
+    HotCold cold;
+    const hipError_t e = launch_hot_part(xb, wb, vb, fe, fg, L, K, d, N, y, acc,
+                                         static_cast<char*>(ws) + atomic_forward_ws_bytes(L, K),
+                                         &cold, s);
+    if (e != hipSuccess) return e;
+    ok = nt ? dispatch_token<uint16_t, false, true>(xb, wb, nullptr, vb, task_expert, task_gate,
+                                                    task_index, cold.expert, cold.gate, M, d, L,
+                                                    K, N, ws, y, acc, s, cold.count,
+                                                    cold.accumulate, false)
+            : dispatch_token<uint16_t, false, false>(xb, wb, nullptr, vb, task_expert, task_gate,
+                                                     task_index, cold.expert, cold.gate, M, d, L,
+                                                     K, N, ws, y, acc, s, cold.count,
+                                                     cold.accumulate, false);
+  } else if (mode == 2) {
     if (bf16) {
       const auto* xb = static_cast<const uint16_t*>(x);
       const auto* wb = static_cast<const uint16_t*>(w);

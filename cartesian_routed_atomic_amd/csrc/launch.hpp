@@ -54,7 +54,8 @@ size_t atomic_forward_ws_bytes(int L, int K);
 // true: read expert rows with the nontemporal hint (M tasks over N experts)
 bool stream_rows(long long M, long long N);
 bool token_centric_supported(int bf16, int d);
-int auto_exec_mode(int bf16, int L, int d, int K);  // 1 expert-centric, 2 token-centric
+// 1 expert-centric, 2 token-centric, 3 hybrid
+int auto_exec_mode(int bf16, int L, int d, int N, int K);
 // flat_expert / flat_gate: the selection in flatten order, or NULL (the
 // token-centric form then inverts the sorted order through task_index)
 hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,
@@ -70,6 +71,35 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
                                      const int32_t* task_index, const int32_t* flat_expert,
                                      const float* flat_gate, float* y, bool accumulate,
                                      void* ws, hipStream_t s);
+
+// hot.hip: the hybrid executor's hot-expert part (bf16).  An expert is hot
+// with at least hot_threshold(L, K) tasks; at most kHotCap are.
+constexpr int kHotCap = 2048;
+constexpr int kHotDensity = 128;  // hot from L / kHotDensity tasks up
+size_t hot_threshold(int L, int K);
+size_t hot_ws_bytes(int L, int K, int d, int N);
+// What the token-centric kernels run afterwards: the cold tasks of token t at
+// expert / gate[t K, t K + count[t]), added onto y if *accumulate.
+struct HotCold {
+  const int32_t* expert;
+  const float* gate;
+  const int32_t* count;
+  const int32_t* accumulate;
+};
+// Selects the hot experts (task counts over fe), writes y (or adds
+// to it) with their share of every token's output, and the cold lists from
+// the flattened selection fe / fg.  hws: hot_ws_bytes(L, K, d, N) bytes.
+hipError_t launch_hot_part(const uint16_t* x, const uint16_t* w, const uint16_t* v,
+                           const int32_t* fe, const float* fg, int L,
+                           int K, int d, int N, float* y, int accumulate, void* hws,
+                           HotCold* out, hipStream_t s);
+
+// router.hip: the hybrid executor's two products on the large-tile MFMA
+// kernel.  cb[t, n] = bf16(g[t, n] silu(x_t . wh[n])) for n < dext[1] (row
+// stride hcap), then y (+)= cb vt^T over K = dext[1] (vt: [d, hcap]).
+hipError_t launch_hot_products(const uint16_t* x, const uint16_t* wh, const uint16_t* vt,
+                               const float* g, uint16_t* cb, float* y, int L, int d, int hcap,
+                               const int32_t* dext, int accumulate, hipStream_t s);
 
 // flat_router.hip: the d x N router baseline
 size_t flat_router_ws_bytes(int L, int N);

@@ -33,6 +33,9 @@ constexpr int kEpiLogits = 0, kEpiSwiglu = 1;
 // Split-K partial: the raw accumulators of K range blockIdx.y, no bias, into
 // zr + blockIdx.y * L * (Nr + Nc) (summed in order by splitk_reduce_kernel).
 constexpr int kEpiPartial = 2;
+// The executor's hot-expert coefficients: hout[t, n] = bf16(rb[t, n] *
+// silu(C[t, n])) (row stride Nr) for the first dext[1] columns.
+constexpr int kEpiHotCoef = 3;
 
 __device__ __forceinline__ int swiglu_hidden(int n) { return ((n >> 5) << 4) | (n & 15); }
 
@@ -291,7 +294,8 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint16_t* __restrict__ wc, const float* __restrict__ rb,
     const float* __restrict__ cb, float* __restrict__ zr, float* __restrict__ zc,
-    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out, uint16_t* __restrict__ hout) {
+    int L, int d, int Nr, int Nc, int n_mt, int n_nt, int acc_out, uint16_t* __restrict__ hout,
+    const int32_t* __restrict__ dext = nullptr) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[GSTAGES * GSTAGE_BYTES];
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int nblk = n_mt * n_nt;
@@ -301,6 +305,13 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
   const int mt = logical / n_nt, nt = logical - mt * n_nt;
   const int m0 = mt * GBM, n0 = nt * GBN;
   const int NT = Nr + Nc;
+  // The executor's hot-expert products read one extent from the device:
+  // kEpiHotCoef its column count, kEpiLogits with dext its K extent (d is
+  // then only the row stride of both operands).
+  const int ncol = EPI == kEpiHotCoef ? dext[1] : NT;
+  if (EPI == kEpiHotCoef && n0 >= ncol) return;  // (SwiGLU tiles run to 2 NT)
+  const int nk = (EPI == kEpiLogits && dext) ? dext[1] / GBK : d / GBK;
+  if (nk == 0) return;
 
   // Direct loads: each wave fills 2 KiB of A (32 rows) and 2 KiB of B per
   // stage with two 1-KiB instructions each; lane i of an instruction lands
@@ -334,7 +345,6 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
 
   const int wm = wv >> 2, wn = wv & 3;  // 2 x 4 waves
   const int fr = l & 15, fc = l >> 4;
-  const int nk = d / GBK;
   // Software pipeline.  Iteration kt: wait until stage kt+1 has landed,
   // barrier, refill the slot of stage kt (its fragments are already in
   // registers) with stage kt+4, read stage kt+1's fragments into the other
@@ -360,6 +370,34 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
 
   // Accumulator lane layout (16x16 output tile): column = lane % 16,
   // rows 4 * (lane / 16) + q, q = 0..3.
+  if constexpr (EPI == kEpiHotCoef) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + j * 16 + fr;
+      if (n >= ncol) continue;
+      // the column's gates first, all loads in flight
+      float gv[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
+          gv[i][q] = t < L ? rb[static_cast<size_t>(t) * Nr + n] : 0.f;
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
+          if (t >= L) continue;
+          const float h = acc[i][j][q];
+          const uint32_t b = __float_as_uint(gv[i][q] * (h / (1.f + __expf(-h))));
+          hout[static_cast<size_t>(t) * Nr + n] =
+              static_cast<uint16_t>((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+        }
+    }
+    return;
+  }
   if constexpr (EPI == kEpiSwiglu) {
     // tiles j = 0, 2 hold gate columns and j = 1, 3 the up columns of the
     // same hidden units (the B rows were interleaved in blocks of 16)
@@ -478,6 +516,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   float* out = n < Nr ? zr + static_cast<size_t>(t) * Nr + n
                       : zc + static_cast<size_t>(t) * Nc + (n - Nr);
   *out = v + (n < Nr ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f)) + (acc_out ? *out : 0.f);
+}
+
+hipError_t launch_hot_products(const uint16_t* x, const uint16_t* wh, const uint16_t* vt,
+                               const float* g, uint16_t* cb, float* y, int L, int d, int hcap,
+                               const int32_t* dext, int accumulate, hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  const int n_mt = (L + GBM - 1) / GBM, n_ht = hcap / GBN, n_dt = (d + GBN - 1) / GBN;
+  // cb = bf16(g * silu(x WH^T)) over the first dext[1] of hcap columns
+  router_gemm_bf16_big_kernel<kEpiHotCoef><<<n_mt * n_ht, 512, 0, s>>>(
+      x, wh, wh, g, nullptr, nullptr, nullptr, L, d, hcap, 0, n_mt, n_ht, 0, cb, dext);
+  // y (+)= cb VT^T over K = dext[1] (row stride hcap for both operands)
+  router_gemm_bf16_big_kernel<kEpiLogits><<<n_mt * n_dt, 512, 0, s>>>(
+      cb, vt, vt, nullptr, nullptr, y, y, L, hcap, d, 0, n_mt, n_dt, accumulate, nullptr, dext);
+  return hipGetLastError();
 }
 
 hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wr, const uint16_t* wc,

@@ -64,7 +64,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 11 */
+int omni_abi_version(void);  /* 12 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -242,10 +242,24 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *     4096 tokens each token gets several waves: its tasks are split over
  *     them for the coefficients, the columns of y_t for the sum.  Needs
  *     d * element size <= 4096 bytes (else UNSUPPORTED).
+ *   OMNI_EXEC_HYBRID (bf16 only, else UNSUPPORTED; same row-size limit as
+ *     the token-centric form): the experts with at least
+ *     max(2, ceil(L / 32), ceil(L K / 2048)) tasks (at most 2048 of them, in
+ *     id order) are "hot"; for them the coefficients of every (token, hot
+ *     expert) pair come from one dense bf16 MFMA product x WH^T (c = g *
+ *     silu(h) on task pairs, 0 elsewhere) and their share of y from a second
+ *     product C VH, with c rounded to bf16 for it and fp32 accumulation (the
+ *     pages' grouped execution on matrix units; gist.science explainer §2.2).
+ *     The other tasks run through the token-centric kernels and are added
+ *     onto that y.  Pays where a few experts take many tasks (skewed
+ *     routing); with none hot it runs the token-centric form (same bits).
+ *     Expects distinct experts per token (as the top-K gives).
  *   OMNI_EXEC_AUTO: the form omni_atomic_forward_mode() names for the shape
  *     (the one that measured faster on MI355X).
- * Both forms evaluate every coefficient and every y element with the same
- * operations in the same order (k = 0..K-1), so they give bit-identical y.
+ * The expert- and token-centric forms evaluate every coefficient and every y
+ * element with the same operations in the same order (k = 0..K-1), so they
+ * give bit-identical y; the hybrid form agrees with them within the bf16
+ * rounding of its hot coefficients.
  *
  * x [L, d], w [N, d], v [N, d] of dt; sched: a schedule produced by
  * omni_schedule_tasks for the same L, K, N, B, with task_index present;
@@ -254,16 +268,19 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  * it stands (e.g. onto the output of a shared dense branch).
  * ws / ws_bytes: at least omni_atomic_forward_workspace(...) bytes, 256-byte
  * aligned (8 bytes per task: a coefficient and an expert id, or the per-token
- * lists).  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
+ * lists; for bf16 shapes the token-centric form supports, also the hybrid
+ * form's buffers: 8 more bytes per task, about 12 KiB per token, 8 KiB per
+ * column of d and 4 bytes per expert).  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
  * 16-byte aligned x, w, v.  Deterministic.
  */
 typedef enum omni_exec_mode {
   OMNI_EXEC_AUTO = 0,
   OMNI_EXEC_EXPERT_CENTRIC = 1,
-  OMNI_EXEC_TOKEN_CENTRIC = 2
+  OMNI_EXEC_TOKEN_CENTRIC = 2,
+  OMNI_EXEC_HYBRID = 3
 } omni_exec_mode;
 
-/* The form OMNI_EXEC_AUTO runs for this shape (1 or 2); 0 for invalid args. */
+/* The form OMNI_EXEC_AUTO runs for this shape (1, 2 or 3); 0 for invalid args. */
 int omni_atomic_forward_mode(omni_dtype dt, int L, int d, int N, int K, int B);
 size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B);
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B,

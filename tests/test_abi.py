@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 11
+    assert lib.omni_abi_version() == 12
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -145,8 +145,12 @@ def test_atomic_forward_argument_checks(lib):
     assert call(s=None) == B.OMNI_ERR_INVALID_ARG
     assert call(y=None) == B.OMNI_ERR_INVALID_ARG
     assert call(w=MIS) == B.OMNI_ERR_INVALID_ARG
-    assert call(mode=3) == B.OMNI_ERR_INVALID_ARG
+    assert call(mode=4) == B.OMNI_ERR_INVALID_ARG
     assert call(mode=-1) == B.OMNI_ERR_INVALID_ARG
+    # the hybrid form: bf16 only, rows as the token-centric form
+    assert call(dt=0, mode=3) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=4096, mode=3) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=2048, mode=3) == B.OMNI_ERR_WORKSPACE
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=8192) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=32) == B.OMNI_ERR_UNSUPPORTED
@@ -166,6 +170,11 @@ def test_atomic_forward_argument_checks(lib):
     both = B.ScheduleStruct(*([1 << 20] * 9))
     assert call(s=both) == B.OMNI_ERR_WORKSPACE
     assert lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256) >= 8 * 8192 * 64
+    # bf16 shapes the token-centric form supports also hold the hybrid buffers
+    # (8 more bytes per task, 12 KiB per token, 8 KiB per column, 4 per expert)
+    hyb = lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256)
+    assert hyb >= 16 * 8192 * 64 + 12288 * 8192 + 8192 * 2048 + 4 * (1 << 20)
+    assert lib.omni_atomic_forward_workspace(0, 8192, 1024, 1 << 20, 64, 256) < hyb // 4
 
 
 def test_atomic_forward_auto_mode(lib):
