@@ -256,6 +256,10 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *     Expects distinct experts per token (as the top-K gives).
  *   OMNI_EXEC_AUTO: the form omni_atomic_forward_mode() names for the shape
  *     (the one that measured faster on MI355X).
+ * The token-centric and hybrid forms with flat_expert / flat_gate set read no
+ * other member of sched (those must still be non-null): such a call may run
+ * while the omni_schedule_tasks call that fills the rest is still running on
+ * another stream.  The expert-centric form reads the sorted tasks.
  * The expert- and token-centric forms evaluate every coefficient and every y
  * element with the same operations in the same order (k = 0..K-1), so they
  * give bit-identical y; the hybrid form agrees with them within the bf16
