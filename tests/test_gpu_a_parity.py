@@ -221,7 +221,15 @@ def _zipf_ids(L, K, N, s, seed):
                                           (256, 64, 1 << 20, 1, "uniform"),
                                           (256, 64, 1 << 20, 64, "zipf"),
                                           (257, 64, 1 << 20, 64, "uniform"),
-                                          (100, 10, (1 << 20) + 1, 4, "uniform")])
+                                          (100, 10, (1 << 20) + 1, 4, "uniform"),
+                                          # group ids of 9 to 11 bits (two passes),
+                                          # tile counts scanned in the scatter
+                                          # (<= 32 tiles) or apart
+                                          (3000, 10, 25000, 16, "uniform"),
+                                          (2000, 8, 5000, 16, "zipf"),
+                                          (10000, 20, 200000, 128, "uniform"),
+                                          (4096, 64, 1 << 20, 128, "zipf"),
+                                          (2000, 16, 1 << 20, 16, "uniform")])
 def test_schedule_direct_is_bit_exact(L, K, N, Bg, kind):
     # Ragged task tiles, one to three radix passes, hot experts; the decode
     # shape (16384 tasks over 2^20 experts) with B = 1, as the backward runs
@@ -245,7 +253,9 @@ def test_schedule_direct_is_bit_exact(L, K, N, Bg, kind):
                                           (70000, 3, 210000, 1, "uniform"),
                                           (40, 4, 100, 1000, "uniform"),
                                           (256, 64, 1 << 20, 16, "uniform"),
-                                          (256, 64, 1 << 20, 15, "uniform")])
+                                          (256, 64, 1 << 20, 15, "uniform"),
+                                          (3000, 16, 100000, 64, "zipf"),
+                                          (20000, 8, 1 << 20, 600, "uniform")])
 def test_window_schedule_is_bit_exact(L, K, N, Bg, kind):
     # fixed id windows: every window a group, empty ones included (up to
     # 210,000 groups: three radix passes), one window holding every expert;
