@@ -643,7 +643,7 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
       fg = lg;
     }
     HotCold cold;
-    const hipError_t e = launch_hot_part(xb, wb, vb, fe, fg, L, K, d, N, y, acc,
+    const hipError_t e = launch_hot_part(xb, wb, vb, task_expert, fe, fg, L, K, d, N, y, acc,
                                          static_cast<char*>(ws) + atomic_forward_ws_bytes(L, K),
                                          &cold, s);
     if (e != hipSuccess) return e;

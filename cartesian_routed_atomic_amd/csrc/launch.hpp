@@ -86,11 +86,11 @@ struct HotCold {
   const int32_t* count;
   const int32_t* accumulate;
 };
-// Selects the hot experts (task counts over fe), writes y (or adds
+// Selects the hot experts (task counts over task_expert), writes y (or adds
 // to it) with their share of every token's output, and the cold lists from
 // the flattened selection fe / fg.  hws: hot_ws_bytes(L, K, d, N) bytes.
 hipError_t launch_hot_part(const uint16_t* x, const uint16_t* w, const uint16_t* v,
-                           const int32_t* fe, const float* fg, int L,
+                           const int32_t* task_expert, const int32_t* fe, const float* fg, int L,
                            int K, int d, int N, float* y, int accumulate, void* hws,
                            HotCold* out, hipStream_t s);
 
