@@ -243,17 +243,19 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *     them for the coefficients, the columns of y_t for the sum.  Needs
  *     d * element size <= 4096 bytes (else UNSUPPORTED).
  *   OMNI_EXEC_HYBRID (bf16 only, else UNSUPPORTED; same row-size limit as
- *     the token-centric form): the experts with at least
- *     max(2, ceil(L / 32), ceil(L K / 2048)) tasks (at most 2048 of them, in
- *     id order) are "hot"; for them the coefficients of every (token, hot
+ *     the token-centric form): the experts with at least t tasks, t =
+ *     max(2, ceil(L / 128)) doubled until no more than 2048 experts reach
+ *     it, are "hot" (in id order); for them the coefficients of every (token, hot
  *     expert) pair come from one dense bf16 MFMA product x WH^T (c = g *
  *     silu(h) on task pairs, 0 elsewhere) and their share of y from a second
  *     product C VH, with c rounded to bf16 for it and fp32 accumulation (the
  *     pages' grouped execution on matrix units; gist.science explainer §2.2).
  *     The other tasks run through the token-centric kernels and are added
- *     onto that y.  Pays where a few experts take many tasks (skewed
- *     routing); with none hot it runs the token-centric form (same bits).
- *     Expects distinct experts per token (as the top-K gives).
+ *     onto that y.  Meant for skewed routing, where a few experts take many
+ *     tasks; on MI355X it measured slower than the token-centric form at
+ *     every workload tried (Zipf routing included), so AUTO never picks it.
+ *     With none hot it gives the token-centric form's bits.  Expects
+ *     distinct experts per token (as the top-K gives).
  *   OMNI_EXEC_AUTO: the form omni_atomic_forward_mode() names for the shape
  *     (the one that measured faster on MI355X).
  * The token-centric and hybrid forms with flat_expert / flat_gate set read no
