@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (binding.forward on one stream).  The oracle checks the whole
 router output and the whole schedule, and samples tokens for the top-K and
-for y (each sampled token is computed independently by the oracle)."""
+for y (each sampled token is computed independently by the oracle), for the
+form auto picks and for the hybrid form."""
 import time
 
 import numpy as np
@@ -46,7 +47,13 @@ def test_full_size_parity(name):
     torch.cuda.synchronize()
     assert torch.equal(y3.view(torch.int32), out["y"].view(torch.int32))
     log("  token lists from the selection and from the schedule give bit-identical y")
-    del t, y2, y3
+    # the hybrid form (hot experts as MFMA products) on the same schedule
+    yh = B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], mode="hybrid")
+    yh2 = B.atomic_forward(t["x"], t["w"], t["v"], out["schedule"], mode="hybrid")
+    torch.cuda.synchronize()
+    assert torch.equal(yh.view(torch.int32), yh2.view(torch.int32))
+    log("  hybrid form: two calls bit-identical")
+    del t, y2, y3, yh2
     log(f"  gpu done {time.time() - t0:.1f}s")
     check_router(inp, out)
     rng = np.random.default_rng(0)
@@ -57,4 +64,6 @@ def test_full_size_parity(name):
         f"{O.traffic_elements(wl.d, wl.L, wl.K, want['n_active'])}")
     ytoks = np.sort(rng.choice(wl.L, size=min(wl.L, 96), replace=False))
     check_y(inp, out, out["y"], wl.dtype, tokens=ytoks)
+    log("  hybrid form:")
+    check_y(inp, out, yh, wl.dtype, tokens=ytoks)
     log(f"  done in {time.time() - t0:.1f}s")
