@@ -71,6 +71,8 @@ SHAPES = [
     (2048, 256, 2048, 64, "cap"),        # all 2048 experts hot: the cap
     (3000, 256, 3000, 64, "cap"),        # 3000 reach the threshold: it doubles
     (513, 128, 1 << 20, 64, "uniform"),  # nothing hot
+    (500, 128, 1000, 1, "zipf"),         # one task per token
+    (5, 128, 50, 8, "zipf"),             # 5 tokens: a 256-row tile of clamped rows
 ]
 
 
