@@ -40,7 +40,11 @@ constexpr int kInfoInts = 64, kLevels = 16;
 // Task counting: each workgroup aggregates a chunk of the tasks in an
 // LDS hash table, then adds one count per distinct expert to memory, so a
 // hot expert sees one atomic per chunk instead of one per task.
-constexpr int kCountChunk = 2048, kCountSlots = 4096;
+// Chunk c adds its counts to replica c % kCountReps, so the busiest
+// experts' atomics spread over kCountReps addresses; readers sum the
+// replicas.  After the sort, replica 0 marks hot expert e in slot s as
+// -(s + 1) (a slot map for the split).
+constexpr int kCountChunk = 2048, kCountSlots = 4096, kCountReps = 4;
 
 size_t hot_threshold(int L, int K) {
   (void)K;
@@ -60,8 +64,8 @@ struct HotLayout {
     ce = o; o += al256(M * 4);
     cg = o; o += al256(M * 4);
     kc = o; o += al256(static_cast<size_t>(L) * 4);
-    info = o; o += al256((kInfoInts + static_cast<size_t>(N) + 3) / 4 * 16);  // info, then counts
-    hot = o; o += al256(kHotCap * 4);
+    info = o; o += al256((kInfoInts + kCountReps * static_cast<size_t>(N) + 3) / 4 * 16);  // info, counts
+    hot = o; o += al256(2 * kHotCap * 4);  // picked (any order), then sorted
     g = o; o += al256(static_cast<size_t>(L) * kHotCap * 4);
     cb = o; o += al256(static_cast<size_t>(L) * kHotCap * 2);
     wh = o; o += al256(static_cast<size_t>(kHotCap) * d * 2);
@@ -78,9 +82,9 @@ __global__ __launch_bounds__(256) void hot_zero_kernel(int4* __restrict__ p, siz
 // Tasks per expert (ids outside [0, N) count as expert 0, as the token
 // kernels read them), over chunks of kCountChunk tasks of the sorted task
 // list.  Sorted by group, a chunk spans few groups, so a hot expert is
-// flushed by few chunks (Zipf routing, 2^20 tasks: 41 us; over the
-// token-major flattened selection every chunk holds the hot experts and
-// their global atomics serialise: 149 us).
+// flushed by few chunks (Zipf routing, 2^20 tasks: 15 us with four count
+// replicas, 41 us with one; over the token-major flattened selection every
+// chunk holds the hot experts and their global atomics serialise: 149 us).
 __global__ __launch_bounds__(256) void hot_count_kernel(const int32_t* __restrict__ te, int M,
                                                         int N, int32_t* __restrict__ cnt) {
   __shared__ int key[kCountSlots];
@@ -108,8 +112,16 @@ __global__ __launch_bounds__(256) void hot_count_kernel(const int32_t* __restric
     }
   }
   __syncthreads();
+  int32_t* rep = cnt + static_cast<size_t>(blockIdx.x % kCountReps) * N;
   for (int i = tid; i < kCountSlots; i += 256)
-    if (key[i] >= 0) atomicAdd(&cnt[key[i]], num[i]);
+    if (key[i] >= 0) atomicAdd(&rep[key[i]], num[i]);
+}
+
+__device__ __forceinline__ int task_count(const int32_t* __restrict__ cnt, int N, int e) {
+  int c = 0;
+#pragma unroll
+  for (int r = 0; r < kCountReps; ++r) c += cnt[static_cast<size_t>(r) * N + e];
+  return c;
 }
 
 // info[8 + i] = experts with at least thr << i tasks (one atomic per wave
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(256) void hot_count_kernel(const int32_t* __restric
 __global__ __launch_bounds__(256) void hot_level_kernel(const int32_t* __restrict__ cnt, int N,
                                                         int thr, int32_t* __restrict__ info) {
   const int e = blockIdx.x * 256 + threadIdx.x;
-  const int c = e < N ? cnt[e] : 0;
+  const int c = e < N ? task_count(cnt, N, e) : 0;
   if (__ballot(c >= thr) == 0) return;  // uniform over the wave
   for (int i = 0; i < kLevels; ++i) {
     const int n = __popcll(__ballot(c >= (static_cast<long long>(thr) << i)));
@@ -135,33 +147,43 @@ __global__ __launch_bounds__(256) void hot_pick_kernel(const int32_t* __restrict
   if (e >= N) return;
   int lv = 0;
   while (lv < kLevels - 1 && info[8 + lv] > kHotCap) ++lv;
-  if (cnt[e] < (static_cast<long long>(thr) << lv)) return;
+  if (task_count(cnt, N, e) < (static_cast<long long>(thr) << lv)) return;
   const int j = atomicAdd(&info[0], 1);
   if (j < kHotCap) hot[j] = e;
 }
 
-// One workgroup: the hot list in ascending id order (ids are distinct, so
-// an id's place is the number of smaller ids), then the sizes and the cold
-// pass's accumulate flag.
-__global__ __launch_bounds__(1024) void hot_sort_kernel(int32_t* __restrict__ hot,
-                                                        int32_t* __restrict__ info,
-                                                        int accumulate) {
+// The hot list in ascending id order (ids are distinct, so an id's place is
+// the number of smaller ids): each of kSortBlocks workgroups loads every id
+// and places kHotCap / kSortBlocks of them (the count is VALU work, spread
+// over that many CUs); workgroup 0 also writes the sizes and the cold
+// pass's accumulate flag (the capped count it stores gives every workgroup
+// the same n).  The places go to a second list: hot itself is still being
+// read by the other workgroups.
+constexpr int kSortBlocks = 8, kSortThreads = kHotCap / kSortBlocks;
+__global__ __launch_bounds__(kSortThreads) void hot_sort_kernel(
+    const int32_t* __restrict__ hot_in, int32_t* __restrict__ hot, int32_t* __restrict__ info,
+    int32_t* __restrict__ cnt, int accumulate) {
   __shared__ __attribute__((aligned(16))) int key[kHotCap];
   const int tid = threadIdx.x;
   const int n = min(info[0], kHotCap);
   const int n4 = (n + 3) / 4;
-  for (int i = tid; i < 4 * n4; i += 1024) key[i] = i < n ? hot[i] : INT_MAX;
+  for (int i = tid; i < 4 * n4; i += kSortThreads) key[i] = i < n ? hot_in[i] : INT_MAX;
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) {
-    const int k = key[i];
-    int r = 0;
-    for (int j = 0; j < n4; ++j) {  // pads are INT_MAX, never smaller
-      const int4 v = reinterpret_cast<const int4*>(key)[j];
-      r += (v.x < k) + (v.y < k) + (v.z < k) + (v.w < k);
+  {
+    const int i = blockIdx.x * kSortThreads + tid;
+    if (i < n) {
+      const int k = key[i];
+      int r = 0;
+#pragma unroll 8
+      for (int j = 0; j < n4; ++j) {  // pads are INT_MAX, never smaller
+        const int4 v = reinterpret_cast<const int4*>(key)[j];
+        r += (v.x < k) + (v.y < k) + (v.z < k) + (v.w < k);
+      }
+      hot[r] = k;
+      cnt[k] = -(r + 1);  // replica 0 as the slot map
     }
-    hot[r] = k;
   }
-  if (tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     info[0] = n;
     info[1] = (n + kHotPad - 1) / kHotPad * kHotPad;
     info[2] = (n > 0 || accumulate) ? 1 : 0;
@@ -209,14 +231,12 @@ __global__ __launch_bounds__(256) void hot_gather_kernel(
 // in LDS, written whole), its cold tasks are compacted, in task order, into
 // ce / cg[t K, t K + kc[t]).
 __global__ __launch_bounds__(256) void hot_split_kernel(
-    const int32_t* __restrict__ fe, const float* __restrict__ fg, const int32_t* __restrict__ hot,
+    const int32_t* __restrict__ fe, const float* __restrict__ fg, const int32_t* __restrict__ slot_map,
     const int32_t* __restrict__ info, int L, int K, int N, float* __restrict__ G,
     int32_t* __restrict__ ce, float* __restrict__ cg, int32_t* __restrict__ kc) {
-  __shared__ int sh[kHotCap];
   __shared__ __attribute__((aligned(16))) float sg[4][kHotCap];
   const int w = threadIdx.x >> 6, l = lane();
-  const int nh = info[0], hp = info[1];
-  for (int i = threadIdx.x; i < nh; i += 256) sh[i] = hot[i];
+  const int hp = info[1];
   for (int i = l; i < hp; i += 64) sg[w][i] = 0.f;
   __syncthreads();
   const int t = blockIdx.x * 4 + w;
@@ -231,13 +251,8 @@ __global__ __launch_bounds__(256) void hot_split_kernel(
         const int e0 = fe[o];
         e = static_cast<unsigned>(e0) < static_cast<unsigned>(N) ? e0 : 0;
         g = fg[o];
-        int lo = 0, hi = nh;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (sh[mid] < e) lo = mid + 1;
-          else hi = mid;
-        }
-        if (lo < nh && sh[lo] == e) slot = lo;
+        const int m = slot_map[e];  // -(s + 1) for the hot expert in slot s
+        slot = m < 0 ? -m - 1 : -1;
       }
       if (slot >= 0) atomicAdd(&sg[w][slot], g);
       const bool cold = l < n && slot < 0;
@@ -276,13 +291,14 @@ hipError_t launch_hot_part(const uint16_t* x, const uint16_t* w, const uint16_t*
   int32_t* kc = reinterpret_cast<int32_t*>(base + lay.kc);
   int32_t* info = reinterpret_cast<int32_t*>(base + lay.info);
   int32_t* cnt = info + kInfoInts;
-  int32_t* hot = reinterpret_cast<int32_t*>(base + lay.hot);
+  int32_t* picked = reinterpret_cast<int32_t*>(base + lay.hot);
+  int32_t* hot = picked + kHotCap;
   float* G = reinterpret_cast<float*>(base + lay.g);
   uint16_t* Cb = reinterpret_cast<uint16_t*>(base + lay.cb);
   uint16_t* WH = reinterpret_cast<uint16_t*>(base + lay.wh);
   uint16_t* VT = reinterpret_cast<uint16_t*>(base + lay.vt);
   const int M = L * K;
-  const size_t n4 = (kInfoInts + static_cast<size_t>(N) + 3) / 4;
+  const size_t n4 = (kInfoInts + kCountReps * static_cast<size_t>(N) + 3) / 4;
   hot_zero_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<int4*>(info), n4);
   const int thr = static_cast<int>(hot_threshold(L, K));
@@ -290,11 +306,11 @@ hipError_t launch_hot_part(const uint16_t* x, const uint16_t* w, const uint16_t*
       task_expert, M, N, cnt);
   const unsigned nb = static_cast<unsigned>((N + 255) / 256);
   hot_level_kernel<<<nb, 256, 0, s>>>(cnt, N, thr, info);
-  hot_pick_kernel<<<nb, 256, 0, s>>>(cnt, N, thr, hot, info);
-  hot_sort_kernel<<<1, 1024, 0, s>>>(hot, info, accumulate);
+  hot_pick_kernel<<<nb, 256, 0, s>>>(cnt, N, thr, picked, info);
+  hot_sort_kernel<<<kSortBlocks, kSortThreads, 0, s>>>(picked, hot, info, cnt, accumulate);
   hot_gather_kernel<<<dim3(kHotCap / 64, static_cast<unsigned>(d / 64)), 256, 0, s>>>(
       w, v, hot, info, d, WH, VT);
-  hot_split_kernel<<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(fe, fg, hot, info, L, K, N,
+  hot_split_kernel<<<static_cast<unsigned>((L + 3) / 4), 256, 0, s>>>(fe, fg, cnt, info, L, K, N,
                                                                       G, ce, cg, kc);
   const hipError_t e = launch_hot_products(x, WH, VT, G, Cb, y, L, d, kHotCap, info + 0,
                                            accumulate, s);

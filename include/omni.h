@@ -276,7 +276,7 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  * aligned (8 bytes per task: a coefficient and an expert id, or the per-token
  * lists; for bf16 shapes the token-centric form supports, also the hybrid
  * form's buffers: 8 more bytes per task, about 12 KiB per token, 8 KiB per
- * column of d and 4 bytes per expert).  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
+ * column of d and 16 bytes per expert).  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
  * 16-byte aligned x, w, v.  Deterministic.
  */
 typedef enum omni_exec_mode {

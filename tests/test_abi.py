@@ -171,9 +171,9 @@ def test_atomic_forward_argument_checks(lib):
     assert call(s=both) == B.OMNI_ERR_WORKSPACE
     assert lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256) >= 8 * 8192 * 64
     # bf16 shapes the token-centric form supports also hold the hybrid buffers
-    # (8 more bytes per task, 12 KiB per token, 8 KiB per column, 4 per expert)
+    # (8 more bytes per task, 12 KiB per token, 8 KiB per column, 16 per expert)
     hyb = lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256)
-    assert hyb >= 16 * 8192 * 64 + 12288 * 8192 + 8192 * 2048 + 4 * (1 << 20)
+    assert hyb >= 16 * 8192 * 64 + 12288 * 8192 + 8192 * 2048 + 16 * (1 << 20)
     assert lib.omni_atomic_forward_workspace(0, 8192, 1024, 1 << 20, 64, 256) < hyb // 4
 
 
