@@ -88,7 +88,8 @@ __device__ __forceinline__ void kth_step(KthSearch& s, const uint32_t (&vk)[NI],
 // 0.  Each lane counts the keys above its own with broadcast LDS reads (no
 // cross-lane shuffles on the critical path), then stores its key at that
 // rank in `out`.  Returns rank r in lane r (0 past k).
-__device__ __forceinline__ uint64_t rank_sort64(const uint64_t* buf, uint64_t* out, int k) {
+__device__ __forceinline__ uint64_t rank_sort64(const uint64_t (&buf)[64], uint64_t (&out)[64],
+                                                int k) {
   const int l = lane();
   const uint64_t mine = buf[l];
   int rank = 0;
@@ -110,7 +111,7 @@ __device__ __forceinline__ uint64_t rank_sort64(const uint64_t* buf, uint64_t* o
 // taken in index order.
 template <int NI>
 __device__ __forceinline__ void axis_collect(const uint32_t (&vk)[NI], const KthSearch& s, int k,
-                                             uint64_t* buf) {
+                                             uint64_t (&buf)[64]) {
   const int l = lane();
   buf[l] = 0ull;
   wave_lds_fence();
@@ -174,7 +175,7 @@ __device__ __forceinline__ bool top64_take(const Top64& s, uint32_t hi, uint32_t
 // Write the taken keys to buf[0..k) (slot order), buf zero-padded to 64.
 template <int NI>
 __device__ __forceinline__ void top64_collect(const uint32_t (&hi)[NI], const uint32_t (&lo)[NI],
-                                              const Top64& s, uint64_t* buf) {
+                                              const Top64& s, uint64_t (&buf)[64]) {
   const int l = lane();
   buf[l] = 0ull;
   wave_lds_fence();
@@ -193,7 +194,8 @@ __device__ __forceinline__ void top64_collect(const uint32_t (&hi)[NI], const ui
 // cand[0..128) as (key << 32 | ~index), zero-padded; returns them two per
 // lane (cand[l], cand[64 + l]).  Requires at most 128 such items.
 template <int NI>
-__device__ __forceinline__ void axis_compact(const uint32_t (&vk)[NI], uint32_t v, uint64_t* cand,
+__device__ __forceinline__ void axis_compact(const uint32_t (&vk)[NI], uint32_t v,
+                                             uint64_t (&cand)[128],
                                              uint32_t (&hi)[2], uint32_t (&lo)[2]) {
   const int l = lane();
   cand[l] = 0ull;
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(256) void product_topk_kernel(
   // tied at it are split by a second search on ~expert among them.
   KthSearch qm = kth_begin<kStairItems>(phi, K);
   while (qm.bit >= 0) kth_step<kStairItems>(qm, phi, K);
-  uint64_t* mb = S.buf[0];
+  uint64_t (&mb)[64] = S.buf[0];
   top64_collect<kStairItems>(phi, plo, top64_finish<kStairItems>(phi, plo, K, qm), mb);
   const uint64_t best = rank_sort64(mb, S.srt[0], K);
   const uint32_t tau = static_cast<uint32_t>(__shfl(best, K - 1) >> 32);
@@ -459,10 +461,10 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
   if (L == 0) return hipSuccess;
   const int n = Nr > Nc ? Nr : Nc;
   const int grid = (L + 3) / 4;
-#define OMNI_TOPK(NI_)                                                                     \
-  product_topk_kernel<NI_><<<grid, 256, 0, s>>>(zr, zc, L, Nr, Nc, kp, K, expert_idx, score, \
-                                                gate, row_logp, col_logp, row_sel, col_sel,  \
-                                                tie_flag, lse)
+#define OMNI_TOPK(NI_)                                                                       \
+  hipLaunchKernelGGL(product_topk_kernel<NI_>, dim3(grid), dim3(256), 0, s, zr, zc, L, Nr, Nc, \
+                     kp, K, expert_idx, score, gate, row_logp, col_logp, row_sel, col_sel,     \
+                     tie_flag, lse)
   if (n <= 64) OMNI_TOPK(1);
   else if (n <= 128) OMNI_TOPK(2);
   else if (n <= 256) OMNI_TOPK(4);
@@ -472,8 +474,8 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
 #undef OMNI_TOPK
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  product_topk_fixup_kernel<<<grid, 256, 0, s>>>(zr, zc, L, Nr, Nc, kp, K, row_sel, col_sel,
-                                                 tie_flag, lse, expert_idx, score, gate);
+  hipLaunchKernelGGL(product_topk_fixup_kernel, dim3(grid), dim3(256), 0, s, zr, zc, L, Nr, Nc,
+                     kp, K, row_sel, col_sel, tie_flag, lse, expert_idx, score, gate);
   return hipGetLastError();
 }
 

@@ -182,3 +182,23 @@ def custom(L, d, Nr, Nc, kprime, K, B, dtype="f32", zipf_s=0.0, index=100, name=
     """A workload of arbitrary shape (tests use it for ragged and edge cases)."""
     return Workload(name, index, L=L, d=d, Nr=Nr, Nc=Nc, kprime=kprime, K=K, B=B,
                     dtype=dtype, zipf_s=zipf_s, dff=dff)
+
+
+def tied_logits(L: int, n: int, step: float, seed: int) -> np.ndarray:
+    """[L, n] float32 logits drawn N(0, 1) and rounded to multiples of `step`,
+    so that many values in a row are equal (inputs where ties decide the
+    selection order)."""
+    rng = np.random.default_rng(seed)
+    z = np.round(rng.standard_normal((L, n)) / step) * step
+    return z.astype(np.float32)
+
+
+def tie_case(L: int, Nr: int, Nc: int, step: float):
+    """The tie-heavy row / column logits of the top-K tests: tied_logits with
+    seeds Nr and Nc + 1, and signed zeros planted in the first token's rows
+    (-0 and +0 compare equal)."""
+    za = tied_logits(L, Nr, step, Nr)
+    zb = tied_logits(L, Nc, step, Nc + 1)
+    za[0, :3] = [0.0, -0.0, 0.0]
+    zb[0, :2] = [-0.0, 0.0]
+    return za, zb
