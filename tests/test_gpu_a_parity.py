@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import omni_oracle as O
-from synth import WORKLOADS, custom, make_inputs
+from synth import WORKLOADS, custom, make_inputs, tie_case
 from tests.gpu_helpers import dev, host, log, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -168,16 +168,12 @@ def test_end_to_end_selection_agreement_is_reported():
     assert same >= 0.9
 
 
-def _tied_logp(L, n, step, seed):
-    rng = np.random.default_rng(seed)
-    z = np.round(rng.standard_normal((L, n)) / step) * step
-    return z.astype(np.float32)
-
-
-FAULTED_ONCE = ("faulted the GPU (memory aperture violation) in its first run, inside the "
-                "former in-kernel tie fallback that the compiler outlined into a call "
-                "taking generic pointers; that code is removed, the cause was not "
-                "established, so this exact case stays off the GPU until it is")
+FAULTED_ONCE = ("faulted the GPU (memory aperture violation) in its first run, inside a "
+                "former in-kernel tie fallback (never committed) that the compiler outlined "
+                "into a call taking generic pointers; that code is gone and the fault's cause "
+                "was never shown, so this exact case stays off the GPU.  The current kernels "
+                "run these exact inputs on the CPU in tests/test_host_sim_topk.py: every LDS "
+                "and global index in range, results bit-exact against the oracle")
 
 
 @pytest.mark.parametrize("Nr,Nc,kp,K,step", [
@@ -189,11 +185,7 @@ FAULTED_ONCE = ("faulted the GPU (memory aperture violation) in its first run, i
 def test_topk_with_ties_is_bit_exact(Nr, Nc, kp, K, step):
     # Quantised inputs produce many equal values, so ties decide the order and
     # the merge's exact fallback (a tie at the staircase threshold) runs.
-    L = 97
-    za = _tied_logp(L, Nr, step, Nr)
-    zb = _tied_logp(L, Nc, step, Nc + 1)
-    za[0, :3] = [0.0, -0.0, 0.0]
-    zb[0, :2] = [-0.0, 0.0]
+    za, zb = tie_case(97, Nr, Nc, step)
     sel = B.product_topk(dev(za), dev(zb), kp, K)
     torch.cuda.synchronize()
     # equal logits stay equal after the float32 normalisation: ties persist
