@@ -29,16 +29,21 @@ METRIC = "routed tokens/sec per atomic-expert layer at 1 GPU; % of HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 FP32_TFLOPS = 157.3            # MI355X float32 vector peak
-EXEC_SRCS = [os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc", f)
-             for f in ("execute.hip", "rowfrag.hpp", "device.hpp")]
+CSRC = os.path.join(ROOT, "cartesian_routed_atomic_amd", "csrc")
+EXEC_SRCS = {  # the sources each executor form's kernels are built from
+    "expert": ("execute.hip", "rowfrag.hpp", "device.hpp"),
+    "token": ("execute.hip", "rowfrag.hpp", "device.hpp"),
+    "grouped": ("grouped.hip", "rowfrag.hpp", "device.hpp"),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
 EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
     "token": "omni_atomic_forward, token-centric: one kernel (token_multi_kernel from 8192 "
              "tokens, four tokens per wave; token lists read from the flattened selection the "
              "schedule carries)",
-    "hybrid": "omni_atomic_forward, hybrid: hot experts as two MFMA products (hot_gemm_kernel), "
-              "the other tasks through the token-centric kernels",
+    "grouped": "omni_atomic_forward, grouped: gf_count_kernel (hot set from the schedule), "
+               "gf_vt_kernel, gf_tile_kernel (per 64-token tile the hot experts as two MFMA "
+               "products, the cold tasks per task, y written once)",
 }
 
 
@@ -46,54 +51,99 @@ def say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def exec_src_hash():
-    """Fingerprint of the executor's kernel sources (a counter record taken on
-    other sources no longer describes the kernel)."""
+def exec_src_hash(form):
+    """Fingerprint of one executor form's kernel sources (a counter record
+    taken on other sources no longer describes the kernel)."""
     h = hashlib.sha256()
-    for p in EXEC_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for f in EXEC_SRCS[form]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, form):
     """Counter-derived HBM bytes per executor call, if taken on this kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if form not in EXEC_SRCS or not os.path.exists(TRAFFIC_FILE):
         return None
     for m in re.finditer(r"traffic_record:\s*(\{.*\})", open(TRAFFIC_FILE).read()):
         rec = json.loads(m.group(1))
         if (rec.get("workload") == workload and rec.get("form") == form
-                and rec.get("executor_src_sha256_16") == exec_src_hash()):
+                and rec.get("executor_src_sha256_16") == exec_src_hash(form)):
             return rec.get("bytes_per_launch")
     return None
 
 
-def cpu_baseline(inp, wl, target_s):
-    """The oracle, untuned, on the first S tokens of the workload."""
-    from oracle import omni_oracle as O
+_ORACLE_INPUTS = {}  # the workload, for the forked oracle workers (inherited at fork)
+
+
+def _one_blas_thread():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([1] + [p.get("num_threads", 1) for p in threadpool_info()])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
 
-    def run(S):
-        xs = inp["x"][:S]
-        t0 = time.perf_counter()
-        a, b = O.router_logp(xs, inp["wr"], inp["wc"], inp["row_bias"], inp["col_bias"])
-        idx, score, gate, _, _ = O.product_topk(a, b, wl.kprime, wl.K)
-        O.build_schedule(idx, gate, wl.N, wl.B)
-        O.atomic_forward(xs, inp["w"], inp["v"], idx, gate)
-        return time.perf_counter() - t0
 
-    s0 = min(wl.L, 16)
-    t0 = run(s0)
-    S = int(max(s0, min(wl.L, s0 * target_s / max(t0, 1e-3))))
-    t = run(S)
-    return {"value": S / t, "unit": "routed tokens/s", "cores": int(cores), "kind": "oracle",
+def _oracle_tokens(span):
+    """The oracle's per-token part of the path on tokens [lo, hi): router
+    log-probabilities, product top-K + gates, token-centric y."""
+    from oracle import omni_oracle as O
+    lo, hi = span
+    inp, wl = _ORACLE_INPUTS["inp"], _ORACLE_INPUTS["wl"]
+    xs = inp["x"][lo:hi]
+    a, b = O.router_logp(xs, inp["wr"], inp["wc"], inp["row_bias"], inp["col_bias"])
+    idx, _, gate, _, _ = O.product_topk(a, b, wl.kprime, wl.K)
+    O.atomic_forward(xs, inp["w"], inp["v"], idx, gate)
+    return idx, gate
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, wl, target_s):
+    """The oracle, untuned, over the host's cores: tokens split into chunks
+    over one worker process per core (one BLAS thread each), then the
+    schedule over the whole selection in the parent (one global sort).  The
+    workers are forked before this process touches the GPU."""
+    import multiprocessing as mp
+
+    import numpy as np
+    from oracle import omni_oracle as O
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(int(avail or 1), 16))  # a one-GPU box's share is 16 cores
+    _ORACLE_INPUTS.update(inp=inp, wl=wl)
+    with mp.get_context("fork").Pool(cores, initializer=_one_blas_thread) as pool:
+        def run(S):
+            bounds = np.linspace(0, S, min(S, 4 * cores) + 1).astype(int)
+            spans = [(int(bounds[i]), int(bounds[i + 1])) for i in range(len(bounds) - 1)]
+            t0 = time.perf_counter()
+            parts = pool.map(_oracle_tokens, spans)
+            idx = np.concatenate([p[0] for p in parts])
+            gate = np.concatenate([p[1] for p in parts])
+            O.build_schedule(idx, gate, wl.N, wl.B)
+            return time.perf_counter() - t0
+
+        # grow the sample until it takes about target_s or covers the batch
+        S = min(wl.L, 8 * cores)
+        t = run(S)
+        while S < wl.L and t < 0.5 * target_s:
+            S = min(wl.L, int(S * min(8.0, target_s / max(t, 1e-3))))
+            t = run(S)
+    _ORACLE_INPUTS.clear()
+    return {"value": S / t, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": int(avail or 1),
+            "threads": f"{cores} worker processes x 1 BLAS thread; schedule in the parent",
             "sample": f"first {S} of {wl.L} tokens of the {wl.name} workload, whole path "
-                      f"(router, top-K + gates, schedule, token-centric y) in {t:.1f}s; "
-                      f"numpy float64, BLAS threads={cores}, the rest single-threaded"}
+                      f"(router log-probabilities, product top-K + gates, schedule, "
+                      f"token-centric y) in {t:.1f}s; numpy float64 oracle, tokens split "
+                      f"over {cores} processes on {cpu_model()}"}
 
 
 def main():
@@ -122,8 +172,6 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
-    from cartesian_routed_atomic_amd import binding as B
     from synth import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
@@ -132,6 +180,17 @@ def main():
     t0 = time.time()
     inp = make_inputs(wl)
     say(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    # the CPU oracle first: its worker processes are forked before anything
+    # here touches the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        say("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+        say(f"[bench] oracle {cpu['value']:.1f} tokens/s ({cpu['sample']})")
+
+    import torch
+    from cartesian_routed_atomic_amd import binding as B
 
     def to_dev(a):
         if a is None:
@@ -154,8 +213,10 @@ def main():
         max(1, B.lib().omni_product_topk_workspace(L, wl.Nr, wl.Nc, wl.kprime, K)),
         dtype=torch.uint8, device=dev)
     sched = B.alloc_schedule(L, K, wl.N, wl.B, dev)
-    exec_ws = torch.empty(
-        max(1, B.lib().omni_atomic_forward_workspace(1, L, wl.d, wl.N, K, wl.B)),
+    code = 1 if wl.dtype == "bf16" else 0
+    exec_ws = torch.empty(  # large enough for every form (the forms are timed below)
+        max(1, *(B.lib().omni_atomic_forward_workspace(code, L, wl.d, wl.N, K, wl.B, m)
+                 for m in (1, 2, 3))),
         dtype=torch.uint8, device=dev)
     y = torch.empty((L, wl.d), dtype=torch.float32, device=dev)
     form = B.atomic_forward_mode(x.dtype, L, wl.d, wl.N, K, wl.B)
@@ -220,7 +281,7 @@ def main():
               "schedule": ev_time(stage_schedule), "execute": ev_time(stage_execute)}
     # the executor call alone, in each form (the step runs `form`)
     forms_ms = {}
-    for f in ("expert", "token", "hybrid"):
+    for f in ("expert", "token", "grouped"):
         try:
             forms_ms[f] = ev_time(lambda: B.atomic_forward(x, w, v, sched, y=y,
                                                            workspace=exec_ws, mode=f), reps=20)
@@ -230,6 +291,15 @@ def main():
                       reps=20)
     counts = sched.counts.cpu().tolist()
     n_active, n_groups = int(counts[0]), int(counts[1])
+    # the grouped form's hot set for this batch, by the rule the header states
+    # (experts with >= tau tasks, tau = max(2, ceil(L / 64)) doubled until at
+    # most 512 reach it), recomputed here from the selection for the record
+    cnt = np.bincount(sel["expert_idx"].cpu().numpy().ravel(), minlength=wl.N)
+    tau = max(2, -(-L // 64))
+    while (cnt >= tau).sum() > 512:
+        tau *= 2
+    grouped_hot = {"n_hot": int((cnt >= tau).sum()), "tau": int(tau),
+                   "task_share": float(cnt[cnt >= tau].sum() / (L * K))}
     s = wl.elem_bytes
     M = L * K
     bytes_alg = 2 * wl.d * s * n_active + L * wl.d * s + 4 * L * wl.d + 12 * M
@@ -355,12 +425,6 @@ def main():
         del wf, fr
         say(f"[bench] variants: {json.dumps(variants)}")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        say("[bench] timing the CPU oracle ...")
-        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
-        say(f"[bench] oracle {cpu['value']:.1f} tokens/s ({cpu['sample']})")
-
     rec = {
         "metric": METRIC,
         "value": L / (ms * 1e-3),
@@ -385,6 +449,7 @@ def main():
                      "kernel_ms": exec_ms},
         "executor_form": form,
         "executor_forms_ms": forms_ms,
+        "grouped_hot_set": grouped_hot,
         "router_mfma": {"achieved": router_tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": router_tflops / MFMA_BF16_TFLOPS,
                         "note": "router call = one MFMA GEMM kernel (bias fused)"},

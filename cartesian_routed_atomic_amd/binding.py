@@ -17,9 +17,9 @@ LIB_PATH = os.environ.get("OMNI_LIB", os.path.join(_HERE, "libomni.so"))
 
 OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ERR_HIP = range(5)
 OMNI_F32, OMNI_BF16 = 0, 1
-EXEC_MODES = {"auto": 0, "expert": 1, "token": 2, "hybrid": 3}  # omni_exec_mode
+EXEC_MODES = {"auto": 0, "expert": 1, "token": 2, "grouped": 3}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -60,7 +60,7 @@ _SIGS = {
     "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),
                                  _vp, _sz, _vp]),
     "omni_atomic_forward_mode": (_i, [_i, _i, _i, _i, _i, _i]),
-    "omni_atomic_forward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "omni_atomic_forward_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "omni_atomic_forward": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
                                  ctypes.POINTER(ScheduleStruct), _vp, _i, _i, _vp, _sz, _vp]),
     "omni_routed_backward_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -285,20 +285,21 @@ def _exec_mode(mode):
 
 
 def atomic_forward_mode(dtype, L, d, N, K, B):
-    """omni_atomic_forward_mode: the form mode="auto" runs ("expert" / "token" / "hybrid")."""
+    """omni_atomic_forward_mode: the form mode="auto" runs ("expert" / "token" / "grouped")."""
     code = torch.bfloat16 if dtype == torch.bfloat16 else torch.float32
     m = lib().omni_atomic_forward_mode(OMNI_BF16 if code == torch.bfloat16 else OMNI_F32,
                                        L, d, N, K, B)
     if m == 0:
         raise ValueError("invalid shape for omni_atomic_forward_mode")
-    return {1: "expert", 2: "token", 3: "hybrid"}[m]
+    return {1: "expert", 2: "token", 3: "grouped"}[m]
 
 
 def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, stream=None,
                    mode="auto"):
     """omni_atomic_forward: returns y [L, d] float32 (y += routed if accumulate).
-    mode: "auto", "expert" (expert-centric), "token" (token-centric) or "hybrid"
-    (hot experts as dense MFMA products, bf16 only)."""
+    mode: "auto", "expert" (expert-centric), "token" (token-centric) or "grouped"
+    (per token tile, the most shared experts as two MFMA products and the rest
+    per task; bf16 only)."""
     L, d = x.shape
     N = w.shape[0]
     _req(x, "x")
@@ -310,7 +311,7 @@ def atomic_forward(x, w, v, sched, y=None, accumulate=False, workspace=None, str
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
     _req(y, "y", torch.float32, (L, d))
     st = sched.struct()
-    nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B)
+    nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B, code)
     ws = workspace
     if nws and (ws is None or ws.numel() < nws):
         ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
@@ -335,7 +336,8 @@ def atomic_forward_glu(x, w, u, v, sched, y=None, accumulate=False, workspace=No
         y = torch.empty((L, d), dtype=torch.float32, device=x.device)
     _req(y, "y", torch.float32, (L, d))
     st = sched.struct()
-    nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B)
+    nws = lib().omni_atomic_forward_workspace(_dtype_code(x), L, d, N, sched.K, sched.B,
+                                              EXEC_MODES["token"])
     ws = workspace
     if nws and (ws is None or ws.numel() < nws):
         ws = torch.empty(nws, dtype=torch.uint8, device=x.device)

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 12;
+constexpr int kAbiVersion = 13;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -75,23 +75,30 @@ omni_status omni_router_logits(omni_dtype dt, int L, int d, int Nr, int Nc, cons
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace of omni_product_topk: a tie flag and the two float32 normalisers
-// per token, then room for the per-axis lists when the caller does not ask
-// for them.
-static size_t topk_ws_lists_offset(int L) {
-  return align256(static_cast<size_t>(L) * 4) + align256(static_cast<size_t>(L) * 8);
+// per token, then room for the per-axis lists the caller does not ask for.
+struct TopkWs {
+  size_t lse, rsel, csel, bytes;  // byte offsets (the flags start at 0)
+};
+static TopkWs topk_ws_layout(int L, int kprime, bool lists_r, bool lists_c) {
+  const size_t list = align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
+  TopkWs w;
+  w.lse = align256(static_cast<size_t>(L) * 4);
+  w.rsel = w.lse + align256(static_cast<size_t>(L) * 8);
+  w.csel = w.rsel + (lists_r ? list : 0);
+  w.bytes = w.csel + (lists_c ? list : 0);
+  return w;
 }
 
 size_t omni_product_topk_workspace(int L, int Nr, int Nc, int kprime, int K) {
   (void)Nr; (void)Nc; (void)K;
   if (L <= 0 || kprime < 1) return 0;
-  return topk_ws_lists_offset(L) +
-         2 * align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
+  return topk_ws_layout(L, kprime, true, true).bytes;
 }
 
-omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const float* row_logits,
-                              const float* col_logits, int32_t* expert_idx, float* score,
-                              float* gate, float* row_logp, float* col_logp, int32_t* row_sel,
-                              int32_t* col_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Argument checks shared by both top-K entry points.
+static omni_status topk_args(int L, int Nr, int Nc, int kprime, int K, const float* row_logits,
+                             const float* col_logits, const int32_t* expert_idx,
+                             const float* score, const float* gate) {
   if (L < 0 || Nr < 1 || Nc < 1) return OMNI_ERR_INVALID_ARG;
   if (kprime < 1 || kprime > Nr || kprime > Nc) return OMNI_ERR_INVALID_ARG;
   if (K < 1 || static_cast<long long>(K) > static_cast<long long>(kprime) * kprime)
@@ -103,19 +110,34 @@ omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const fl
   if (!fits_i32(static_cast<long long>(L) * Nr) || !fits_i32(static_cast<long long>(L) * Nc) ||
       !fits_i32(static_cast<long long>(L) * K) || !fits_i32(static_cast<long long>(L) * kprime))
     return OMNI_ERR_UNSUPPORTED;
-  if (L == 0) return OMNI_OK;
-  const size_t need = omni_product_topk_workspace(L, Nr, Nc, kprime, K);
-  if (!ws || ws_bytes < need || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
+  return OMNI_OK;
+}
+
+static omni_status topk_run(int L, int Nr, int Nc, int kprime, int K, const float* row_logits,
+                            const float* col_logits, int32_t* expert_idx, float* score,
+                            float* gate, float* row_logp, float* col_logp, int32_t* row_sel,
+                            int32_t* col_sel, char* base, const TopkWs& w, hipStream_t stream) {
   int32_t* flags = reinterpret_cast<int32_t*>(base);
-  float* lse = reinterpret_cast<float*>(base + align256(static_cast<size_t>(L) * 4));
-  const size_t o1 = topk_ws_lists_offset(L);
-  const size_t o2 = o1 + align256(static_cast<size_t>(L) * static_cast<size_t>(kprime) * 4);
-  int32_t* rsel = row_sel ? row_sel : reinterpret_cast<int32_t*>(base + o1);
-  int32_t* csel = col_sel ? col_sel : reinterpret_cast<int32_t*>(base + o2);
+  float* lse = reinterpret_cast<float*>(base + w.lse);
+  int32_t* rsel = row_sel ? row_sel : reinterpret_cast<int32_t*>(base + w.rsel);
+  int32_t* csel = col_sel ? col_sel : reinterpret_cast<int32_t*>(base + w.csel);
   return hip_status(omni::launch_product_topk(row_logits, col_logits, L, Nr, Nc, kprime, K,
                                               expert_idx, score, gate, row_logp, col_logp, rsel,
                                               csel, flags, lse, stream));
+}
+
+omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const float* row_logits,
+                              const float* col_logits, int32_t* expert_idx, float* score,
+                              float* gate, float* row_logp, float* col_logp, int32_t* row_sel,
+                              int32_t* col_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const omni_status a = topk_args(L, Nr, Nc, kprime, K, row_logits, col_logits, expert_idx,
+                                  score, gate);
+  if (a != OMNI_OK) return a;
+  if (L == 0) return OMNI_OK;
+  const TopkWs w = topk_ws_layout(L, kprime, true, true);
+  if (!ws || ws_bytes < w.bytes || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
+  return topk_run(L, Nr, Nc, kprime, K, row_logits, col_logits, expert_idx, score, gate,
+                  row_logp, col_logp, row_sel, col_sel, static_cast<char*>(ws), w, stream);
 }
 
 static bool grouping_ok(omni_grouping g) {
@@ -163,14 +185,24 @@ int omni_atomic_forward_mode(omni_dtype dt, int L, int d, int N, int K, int B) {
   return omni::auto_exec_mode(dt == OMNI_BF16, L, d, N, K);
 }
 
-size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B) {
+static bool exec_mode_ok(omni_exec_mode m) {
+  return m == OMNI_EXEC_AUTO || m == OMNI_EXEC_EXPERT_CENTRIC || m == OMNI_EXEC_TOKEN_CENTRIC ||
+         m == OMNI_EXEC_GROUPED;
+}
+
+// The form a call runs: AUTO resolved the way omni_atomic_forward resolves it.
+static int resolve_form(omni_dtype dt, int L, int d, int N, int K, omni_exec_mode mode) {
+  return mode == OMNI_EXEC_AUTO ? omni::auto_exec_mode(dt == OMNI_BF16, L, d, N, K)
+                                : static_cast<int>(mode);
+}
+
+size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B,
+                                     omni_exec_mode mode) {
   (void)B;
+  if (dt != OMNI_F32 && dt != OMNI_BF16) return 0;
+  if (!exec_mode_ok(mode) || N < 1 || d < 1) return 0;
   if (L <= 0 || K < 1 || !fits_i32(static_cast<long long>(L) * K)) return 0;
-  size_t n = omni::atomic_forward_ws_bytes(L, K);
-  // the hybrid form's hot-expert buffers (bf16 shapes it supports)
-  if (dt == OMNI_BF16 && N >= 1 && omni::token_centric_supported(1, d))
-    n += omni::hot_ws_bytes(L, K, d, N);
-  return n;
+  return omni::exec_ws_bytes(resolve_form(dt, L, d, N, K, mode), L, d, N, K);
 }
 
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B, const void* x,
@@ -178,9 +210,7 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
                                 float* y, int accumulate, omni_exec_mode mode, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
   if (dt != OMNI_F32 && dt != OMNI_BF16) return OMNI_ERR_INVALID_ARG;
-  if (mode != OMNI_EXEC_AUTO && mode != OMNI_EXEC_EXPERT_CENTRIC &&
-      mode != OMNI_EXEC_TOKEN_CENTRIC && mode != OMNI_EXEC_HYBRID)
-    return OMNI_ERR_INVALID_ARG;
+  if (!exec_mode_ok(mode)) return OMNI_ERR_INVALID_ARG;
   if (!schedule_args_ok(L, K, N, B) || d < 1) return OMNI_ERR_INVALID_ARG;
   if (!w || !v || !sched) return OMNI_ERR_INVALID_ARG;
   const long long M = static_cast<long long>(L) * K;
@@ -190,18 +220,17 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
     return OMNI_ERR_INVALID_ARG;
   if ((sched->flat_expert == nullptr) != (sched->flat_gate == nullptr))
     return OMNI_ERR_INVALID_ARG;
-  if (d < 64 || d > 4096 || (d & (d - 1)) != 0) return OMNI_ERR_UNSUPPORTED;
+  if (!omni::chunked_supported(d)) return OMNI_ERR_UNSUPPORTED;
   const int bf16 = dt == OMNI_BF16;
-  const int form = mode == OMNI_EXEC_AUTO ? omni::auto_exec_mode(bf16, L, d, N, K) : mode;
-  if ((form == OMNI_EXEC_TOKEN_CENTRIC || form == OMNI_EXEC_HYBRID) &&
-      !omni::token_centric_supported(bf16, d))
+  const int form = resolve_form(dt, L, d, N, K, mode);
+  if (form == OMNI_EXEC_GROUPED && !omni::grouped_supported(bf16, d, K))
     return OMNI_ERR_UNSUPPORTED;
-  if (form == OMNI_EXEC_HYBRID && !bf16) return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(v)) return OMNI_ERR_INVALID_ARG;
   if (L > 0 && !aligned16(y)) return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;
   if (L == 0) return OMNI_OK;
-  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
+  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B,
+                                                    static_cast<omni_exec_mode>(form));
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
   return hip_status(omni::launch_atomic_forward(bf16, form, L, d, N, K, x, w, v,
                                                 sched->task_token, sched->task_expert,
@@ -224,13 +253,13 @@ omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, i
   if ((sched->flat_expert == nullptr) != (sched->flat_gate == nullptr))
     return OMNI_ERR_INVALID_ARG;
   const int bf16 = dt == OMNI_BF16;
-  if (!omni::token_centric_supported(bf16, d)) return OMNI_ERR_UNSUPPORTED;
+  if (!omni::chunked_supported(d)) return OMNI_ERR_UNSUPPORTED;
   if ((L > 0 && !aligned16(x)) || !aligned16(w) || !aligned16(u) || !aligned16(v))
     return OMNI_ERR_INVALID_ARG;
   if (L > 0 && !aligned16(y)) return OMNI_ERR_INVALID_ARG;
   if (!fits_i32(static_cast<long long>(L) * d)) return OMNI_ERR_UNSUPPORTED;
   if (L == 0) return OMNI_OK;
-  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B);
+  const size_t need = omni_atomic_forward_workspace(dt, L, d, N, K, B, OMNI_EXEC_TOKEN_CENTRIC);
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return OMNI_ERR_WORKSPACE;
   return hip_status(omni::launch_atomic_forward_glu(bf16, L, d, N, K, x, w, u, v,
                                                     sched->task_expert, sched->task_gate,

@@ -141,19 +141,18 @@ __global__ __launch_bounds__(256) void gather_kernel(
     my_e = static_cast<unsigned>(my_e) < static_cast<unsigned>(N) ? my_e : 0;
     const float my_c = (l < n) ? coef[base + l] : 0.f;
     Frag f[kRing];
+    // loads unconditional (see token_gather): positions past n re-read row n - 1
+    const int last = n - 1;
 #pragma unroll
     for (int s = 0; s < kRing - 1; ++s)
-      if (s < n)
-        f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d + col0, l);
+      f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, min(s, last))) * d + col0, l);
     for (int i = 0; i < n; i += kRing) {
 #pragma unroll
       for (int s = 0; s < kRing; ++s) {
         const int ii = i + s;
-        if (ii >= n) break;
-        if (ii + kRing - 1 < n)
-          f[(s + kRing - 1) % kRing].template fetch<NT>(
-              V + static_cast<size_t>(rdlane(my_e, ii + kRing - 1)) * d + col0, l);
-        const float c = rdlane(my_c, ii);
+        f[(s + kRing - 1) % kRing].template fetch<NT>(
+            V + static_cast<size_t>(rdlane(my_e, min(ii + kRing - 1, last))) * d + col0, l);
+        const float c = ii < n ? rdlane(my_c, min(ii, 63)) : 0.f;
 #pragma unroll
         for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
       }
@@ -183,79 +182,25 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const int32_t* __restric
 
 constexpr int kTokRing = 6;  // row slots per wave in the token-centric kernel: five in flight
 
-// h_k = x_t . M[e_k] for the n tasks of a chunk (expert e_k in lane k),
-// streamed through the row ring with kTokRing - 1 rows in flight; h_k ends
-// in lane k.
-template <typename T, int EPL, bool NT, int RING>
-__device__ __forceinline__ float token_dots(const RowFrag<T, EPL>& xf, const T* __restrict__ M,
-                                            int my_e, int n, int d, int l,
-                                            RowFrag<T, EPL> (&f)[RING]) {
-  float my_h = 0.f;
-#pragma unroll
-  for (int s = 0; s < RING - 1; ++s)
-    if (s < n) f[s].template fetch<NT>(M + static_cast<size_t>(rdlane(my_e, s)) * d, l);
-  for (int i = 0; i < n; i += RING) {
-#pragma unroll
-    for (int s = 0; s < RING; ++s) {
-      const int ii = i + s;
-      if (ii >= n) break;
-      if (ii + RING - 1 < n)
-        f[(s + RING - 1) % RING].template fetch<NT>(
-            M + static_cast<size_t>(rdlane(my_e, ii + RING - 1)) * d, l);
-      const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
-      if (l == ii) my_h = h;
-    }
-  }
-  return my_h;
-}
-
-// y_t (+)= sum_k c_k V[e_k] over the n tasks of a chunk (c_k, e_k in lane k),
-// the V rows streamed through the ring, fp32 accumulation in k order.
-template <typename T, int EPL, bool NT, int RING>
-__device__ __forceinline__ void token_gather(const T* __restrict__ V, int my_e, float my_c, int n,
-                                             int d, int l, RowFrag<T, EPL> (&f)[RING],
-                                             float (&acc)[EPL]) {
-#pragma unroll
-  for (int s = 0; s < RING - 1; ++s)
-    if (s < n) f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
-  for (int i = 0; i < n; i += RING) {
-#pragma unroll
-    for (int s = 0; s < RING; ++s) {
-      const int ii = i + s;
-      if (ii >= n) break;
-      if (ii + RING - 1 < n)
-        f[(s + RING - 1) % RING].template fetch<NT>(
-            V + static_cast<size_t>(rdlane(my_e, ii + RING - 1)) * d, l);
-      const float c = rdlane(my_c, ii);
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
-    }
-  }
-}
-
 // GLU: the SwiGLU-gated variant, coefficient g silu(x . W[e]) (x . U[e]).
 // NT: the expert rows and x_t (each read once here) carry the nontemporal hint.
 template <typename T, int EPL, bool GLU, bool NT>
 __global__ __launch_bounds__(256, 3) void token_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
     const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
-    int K, int d, int N, float* __restrict__ y, int accumulate,
-    const int32_t* __restrict__ kcnt, const int32_t* __restrict__ acc_dev) {
+    int K, int d, int N, float* __restrict__ y, int accumulate) {
   using Frag = RowFrag<T, EPL>;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
   if (t >= L) return;
-  const int Kt = kcnt ? kcnt[t] : K;
-  const int accum = acc_dev ? *acc_dev : accumulate;
-  if (Kt == 0 && accum) return;  // nothing to add to this row
   Frag xf;
   xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
   float acc[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
   Frag f[kTokRing];  // one ring for both passes keeps the register count down
-  for (int k0 = 0; k0 < Kt; k0 += 64) {
-    const int n = min(64, Kt - k0);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int n = min(64, K - k0);
     int my_e = 0;
     float my_g = 0.f;
     if (l < n) {
@@ -272,7 +217,8 @@ __global__ __launch_bounds__(256, 3) void token_kernel(
     // pass B: y_t += coef_k * V[e_k]
     token_gather<T, EPL, NT, kTokRing>(V, my_e, my_c, n, d, l, f, acc);
   }
-  store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d, accum);
+  store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d,
+                                                  accumulate);
 }
 
 static inline int clampi(long long v, int lo, int hi) {
@@ -355,8 +301,7 @@ template <typename T, int EPL, bool GLU, bool NT>
 __global__ __launch_bounds__(256, 2) void token_multi_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
     const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
-    int K, int d, int N, float* __restrict__ y, int accumulate,
-    const int32_t* __restrict__ kcnt, const int32_t* __restrict__ acc_dev) {
+    int K, int d, int N, float* __restrict__ y, int accumulate) {
   using Frag = RowFrag<T, EPL>;
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = lane();
@@ -374,9 +319,8 @@ __global__ __launch_bounds__(256, 2) void token_multi_kernel(
     if (t >= L) continue;  // uniform over the wave
     Frag xf;
     xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
-    const int Kt = kcnt ? kcnt[t] : K;
-    for (int k0 = 0; k0 < Kt; k0 += 64) {
-      const int n = min(64, Kt - k0);
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int n = min(64, K - k0);
       int my_e = 0;
       float my_g = 0.f;
       if (l < n) {
@@ -391,12 +335,11 @@ __global__ __launch_bounds__(256, 2) void token_multi_kernel(
       token_gather<T, EPL, NT, kMultiRing>(V, my_e, my_c, n, d, l, f, acc[tt]);
     }
   }
-  const int accum = acc_dev ? *acc_dev : accumulate;
 #pragma unroll
   for (int tt = 0; tt < kMultiTokens; ++tt)
     if (t0 + tt < L)
       store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(
-          acc[tt], y + static_cast<size_t>(t0 + tt) * d, accum);
+          acc[tt], y + static_cast<size_t>(t0 + tt) * d, accumulate);
 }
 
 constexpr int kSplitRing = 8;  // pass-B row-slice slots per wave in token_split_kernel
@@ -413,8 +356,7 @@ template <typename T, int EPL, int WS, bool GLU, bool NT>
 __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     const T* __restrict__ x, const T* __restrict__ W, const T* __restrict__ U,
     const T* __restrict__ V, const int32_t* __restrict__ le, const float* __restrict__ lg, int L,
-    int K, int d, int N, float* __restrict__ y, int accumulate,
-    const int32_t* __restrict__ kcnt, const int32_t* __restrict__ acc_dev) {
+    int K, int d, int N, float* __restrict__ y, int accumulate) {
   static_assert(EPL % WS == 0, "every wave needs at least one element per lane");
   constexpr int EPLB = EPL / WS;  // pass-B elements per lane
   using Frag = RowFrag<T, EPL>;
@@ -424,17 +366,14 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
   const int t = blockIdx.x;
   const int w = threadIdx.x >> 6, l = lane();
   if (t >= L) return;  // the whole workgroup leaves together
-  const int Kt = kcnt ? kcnt[t] : K;
-  const int accum = acc_dev ? *acc_dev : accumulate;
-  if (Kt == 0 && accum) return;  // nothing to add to this row (whole workgroup)
   Frag xf;
   xf.template fetch<NT>(x + static_cast<size_t>(t) * d, l);
   const int col0 = w * 64 * EPLB;
   float acc[EPLB];
 #pragma unroll
   for (int q = 0; q < EPLB; ++q) acc[q] = 0.f;
-  for (int k0 = 0; k0 < Kt; k0 += 64) {
-    const int n = min(64, Kt - k0);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int n = min(64, K - k0);
     const int per = (n + WS - 1) / WS;
     const int a0 = w * per;
     const int na = max(0, min(per, n - a0));  // this wave's tasks: [a0, a0 + na)
@@ -460,19 +399,18 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     const int my_e = l < n ? se[l] : 0;
     const float my_c = l < n ? sc[l] : 0.f;
     FragB g[kSplitRing];
+    // loads unconditional (see token_gather): positions past n re-read row n - 1
+    const int last = n - 1;
 #pragma unroll
     for (int s = 0; s < kSplitRing - 1; ++s)
-      if (s < n)
-        g[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d + col0, l);
+      g[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, min(s, last))) * d + col0, l);
     for (int i = 0; i < n; i += kSplitRing) {
 #pragma unroll
       for (int s = 0; s < kSplitRing; ++s) {
         const int ii = i + s;
-        if (ii >= n) break;
-        if (ii + kSplitRing - 1 < n)
-          g[(s + kSplitRing - 1) % kSplitRing].template fetch<NT>(
-              V + static_cast<size_t>(rdlane(my_e, ii + kSplitRing - 1)) * d + col0, l);
-        const float c = rdlane(my_c, ii);
+        g[(s + kSplitRing - 1) % kSplitRing].template fetch<NT>(
+            V + static_cast<size_t>(rdlane(my_e, min(ii + kSplitRing - 1, last))) * d + col0, l);
+        const float c = ii < n ? rdlane(my_c, min(ii, 63)) : 0.f;
 #pragma unroll
         for (int q = 0; q < EPLB; ++q) acc[q] = fmaf(c, g[s].get(q), acc[q]);
       }
@@ -480,7 +418,7 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     __syncthreads();  // the next chunk's coefficients overwrite sc / se
   }
   store_row<T, EPLB, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
-                                                   accum);
+                                                   accumulate);
 }
 
 // From 8192 tokens up the token-centric form runs kMultiTokens tokens per
@@ -508,8 +446,7 @@ template <typename T, bool GLU, bool NT>
 static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const int32_t* te,
                            const float* tg, const int32_t* ti, const int32_t* fe,
                            const float* fg, int M, int d, int L, int K, int N, void* ws, float* y,
-                           int accumulate, hipStream_t s, const int32_t* kcnt = nullptr,
-                           const int32_t* acc_dev = nullptr, bool allow_multi = true) {
+                           int accumulate, hipStream_t s) {
   if (!fe) {
     int32_t* le = static_cast<int32_t*>(ws);
     float* lg = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -524,8 +461,7 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
     const unsigned grid = static_cast<unsigned>(L);
 #define OMNI_SPLIT(EPL_, WS_)                                                                   \
   token_split_kernel<T, EPL_, WS_, GLU, NT><<<grid, 64 * WS_, 0, s>>>(x, w, u, v, fe, fg, L, K, \
-                                                                       d, N, y, accumulate, \
-                                                                       kcnt, acc_dev)
+                                                                       d, N, y, accumulate)
 #define OMNI_SPLIT_WS(EPL_)                                                                     \
   if (nw == 2) { if constexpr (EPL_ >= 2) OMNI_SPLIT(EPL_, 2); }                                \
   else if (nw == 4) { if constexpr (EPL_ >= 4) OMNI_SPLIT(EPL_, 4); }                           \
@@ -547,17 +483,17 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
 #undef OMNI_SPLIT
     return true;
   }
-  const bool multi = allow_multi && token_multi_tokens(L);
+  const bool multi = token_multi_tokens(L);
   const unsigned nblk = static_cast<unsigned>((L + 3) / 4);
   const unsigned mblk = static_cast<unsigned>((L + 4 * kMultiTokens - 1) / (4 * kMultiTokens));
   // rows of at most 4 KiB: d <= 2048 for bf16, d <= 1024 for float32
 #define OMNI_TOK(EPL_)                                                                         \
   if (multi)                                                                                   \
     token_multi_kernel<T, EPL_, GLU, NT><<<mblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N,  \
-                                                              y, accumulate, kcnt, acc_dev);   \
+                                                              y, accumulate);                  \
   else                                                                                         \
     token_kernel<T, EPL_, GLU, NT><<<nblk, 256, 0, s>>>(x, w, u, v, fe, fg, L, K, d, N, y,     \
-                                                        accumulate, kcnt, acc_dev);
+                                                        accumulate);
   switch (d) {
     case 64: OMNI_TOK(1) break;
     case 128: OMNI_TOK(2) break;
@@ -576,9 +512,20 @@ static bool dispatch_token(const T* x, const T* w, const T* u, const T* v, const
   return true;
 }
 
-bool token_centric_supported(int bf16, int d) {
+bool token_rows_in_registers(int bf16, int d) {
   const long long row_bytes = static_cast<long long>(d) * (bf16 ? 2 : 4);
   return row_bytes <= 4096 && d >= 64 && (d & (d - 1)) == 0;
+}
+
+// The expert-centric kernels above hold a row per wave for d = 64 .. 4096, a
+// power of two; other widths run the chunked kernels (chunked.hip).
+static bool expert_rows_in_registers(int d) { return d >= 64 && d <= 4096 && (d & (d - 1)) == 0; }
+
+hipError_t launch_unpermute(const int32_t* texp, const float* tgate, const int32_t* tidx, int M,
+                            int N, int32_t* le, float* lg, hipStream_t s) {
+  unpermute_kernel<<<static_cast<unsigned>((M + 255) / 256), 256, 0, s>>>(texp, tgate, tidx, M,
+                                                                          N, le, lg);
+  return hipGetLastError();
 }
 
 bool stream_rows(long long M, long long N) {
@@ -591,6 +538,14 @@ bool stream_rows(long long M, long long N) {
   return M >= (1ll << 18) && M <= N;
 }
 
+size_t exec_ws_bytes(int mode, int L, int d, int N, int K) {
+  // the per-task lists (8 bytes per task) of every form; the grouped form's
+  // counts, hot set and gathered V_H^T follow
+  size_t n = atomic_forward_ws_bytes(L, K);
+  if (mode == 3) n += grouped_ws_bytes(L, K, d, N);
+  return n;
+}
+
 int auto_exec_mode(int bf16, int L, int d, int N, int K) {
   (void)N;
   (void)K;
@@ -600,10 +555,7 @@ int auto_exec_mode(int bf16, int L, int d, int N, int K) {
   // over several waves (token_split_kernel), which beat the two-kernel form
   // at L = 256, d = 2048 (22 against 27 us) and L = 64, d = 128 (12.5
   // against 15 us).
-  // The hybrid form (hot experts as MFMA products) is never picked: it lost
-  // to the token-centric form at every workload measured, the Zipf-routed
-  // one included (L = 16384, N = 2^18: 0.43 against 0.37 ms per call).
-  if (!token_centric_supported(bf16, d)) return 1;
+  if (!token_rows_in_registers(bf16, d)) return 1;
   if ((L >= 8192 && d >= 1024) || L < 4096) return 2;
   return 1;
 }
@@ -624,13 +576,15 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
     }
     return hipGetLastError();
   }
+  if ((mode == 2 && !token_rows_in_registers(bf16, d)) ||
+      (mode == 1 && !expert_rows_in_registers(d)))
+    return launch_chunked(bf16, mode, false, L, d, N, K, x, w, nullptr, v, task_token,
+                          task_expert, task_gate, task_index, flat_expert, flat_gate, y,
+                          accumulate, ws, s);
   const int acc = accumulate ? 1 : 0;
   const bool nt = stream_rows(M, N);
   bool ok;
-  if (mode == 3) {  // hybrid, bf16 only (checked by the caller)
-    const auto* xb = static_cast<const uint16_t*>(x);
-    const auto* wb = static_cast<const uint16_t*>(w);
-    const auto* vb = static_cast<const uint16_t*>(v);
+  if (mode == 3) {  // grouped, bf16 only (checked by the caller)
     const int32_t* fe = flat_expert;
     const float* fg = flat_gate;
     if (!fe) {
@@ -642,19 +596,10 @@ hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K,
       fe = le;
       fg = lg;
     }
-    HotCold cold;
-    const hipError_t e = launch_hot_part(xb, wb, vb, task_expert, fe, fg, L, K, d, N, y, acc,
-                                         static_cast<char*>(ws) + atomic_forward_ws_bytes(L, K),
-                                         &cold, s);
-    if (e != hipSuccess) return e;
-    ok = nt ? dispatch_token<uint16_t, false, true>(xb, wb, nullptr, vb, task_expert, task_gate,
-                                                    task_index, cold.expert, cold.gate, M, d, L,
-                                                    K, N, ws, y, acc, s, cold.count,
-                                                    cold.accumulate, false)
-            : dispatch_token<uint16_t, false, false>(xb, wb, nullptr, vb, task_expert, task_gate,
-                                                     task_index, cold.expert, cold.gate, M, d, L,
-                                                     K, N, ws, y, acc, s, cold.count,
-                                                     cold.accumulate, false);
+    return launch_grouped(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                          static_cast<const uint16_t*>(v), task_expert, fe,
+                          fg, L, K, d, N, y, acc, static_cast<char*>(ws) + atomic_forward_ws_bytes(L, K),
+                          s);
   } else if (mode == 2) {
     if (bf16) {
       const auto* xb = static_cast<const uint16_t*>(x);
@@ -712,7 +657,6 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
                                      const float* flat_gate, float* y, bool accumulate,
                                      void* ws, hipStream_t s) {
   if (L == 0) return hipSuccess;
-  if (!token_centric_supported(bf16, d)) return hipErrorInvalidValue;
   const int M = L * K;
   if (M == 0) {
     if (!accumulate) {
@@ -722,6 +666,9 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
     }
     return hipGetLastError();
   }
+  if (!token_rows_in_registers(bf16, d))
+    return launch_chunked(bf16, 2, true, L, d, N, K, x, w, u, v, nullptr, task_expert, task_gate,
+                          task_index, flat_expert, flat_gate, y, accumulate, ws, s);
   const int acc = accumulate ? 1 : 0;
   const bool nt = stream_rows(M, N);
   bool ok;

@@ -49,15 +49,33 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
                            int32_t* group_offsets, int32_t* task_token, int32_t* task_expert,
                            float* task_gate, int32_t* task_index, void* ws, hipStream_t s);
 
+// schedule_small.hip: the whole schedule in one workgroup, for at most 16,384
+// tasks and groups (G = max_groups); no workspace
+bool schedule_small_fits(long long M, long long G);
+hipError_t launch_schedule_small(int L, int K, int N, int B, int window, int G,
+                                 const int32_t* expert_idx, const float* gate, int32_t* counts,
+                                 int32_t* active, int32_t* group_offsets, int32_t* task_token,
+                                 int32_t* task_expert, float* task_gate, int32_t* task_index,
+                                 hipStream_t s);
+
 // execute.hip
 size_t atomic_forward_ws_bytes(int L, int K);
 // true: read expert rows with the nontemporal hint (M tasks over N experts)
 bool stream_rows(long long M, long long N);
-bool token_centric_supported(int bf16, int d);
-// 1 expert-centric, 2 token-centric, 3 hybrid
+// the token-centric kernels that hold a row per wave: d a power of two, rows
+// of at most 4 KiB (other widths run the chunked kernels)
+bool token_rows_in_registers(int bf16, int d);
+// schedule order -> flatten order: le[task_index[m]] = task_expert[m] (ids
+// outside [0, N) mapped to 0), lg[task_index[m]] = task_gate[m]
+hipError_t launch_unpermute(const int32_t* texp, const float* tgate, const int32_t* tidx, int M,
+                            int N, int32_t* le, float* lg, hipStream_t s);
+// 1 expert-centric, 2 token-centric, 3 grouped
 int auto_exec_mode(int bf16, int L, int d, int N, int K);
+// workspace of one form (mode 1, 2 or 3)
+size_t exec_ws_bytes(int mode, int L, int d, int N, int K);
 // flat_expert / flat_gate: the selection in flatten order, or NULL (the
-// token-centric form then inverts the sorted order through task_index)
+// token-centric and grouped forms then invert the sorted order through
+// task_index); sched_counts / active: the schedule's (grouped form only)
 hipError_t launch_atomic_forward(int bf16, int mode, int L, int d, int N, int K, const void* x,
                                  const void* w, const void* v, const int32_t* task_token,
                                  const int32_t* task_expert, const float* task_gate,
@@ -72,34 +90,26 @@ hipError_t launch_atomic_forward_glu(int bf16, int L, int d, int N, int K, const
                                      const float* flat_gate, float* y, bool accumulate,
                                      void* ws, hipStream_t s);
 
-// hot.hip: the hybrid executor's hot-expert part (bf16).  An expert is hot
-// with at least hot_threshold(L, K) tasks; at most kHotCap are.
-constexpr int kHotCap = 2048;
-constexpr int kHotDensity = 128;  // hot from L / kHotDensity tasks up
-size_t hot_threshold(int L, int K);
-size_t hot_ws_bytes(int L, int K, int d, int N);
-// What the token-centric kernels run afterwards: the cold tasks of token t at
-// expert / gate[t K, t K + count[t]), added onto y if *accumulate.
-struct HotCold {
-  const int32_t* expert;
-  const float* gate;
-  const int32_t* count;
-  const int32_t* accumulate;
-};
-// Selects the hot experts (task counts over task_expert), writes y (or adds
-// to it) with their share of every token's output, and the cold lists from
-// the flattened selection fe / fg.  hws: hot_ws_bytes(L, K, d, N) bytes.
-hipError_t launch_hot_part(const uint16_t* x, const uint16_t* w, const uint16_t* v,
-                           const int32_t* task_expert, const int32_t* fe, const float* fg, int L,
-                           int K, int d, int N, float* y, int accumulate, void* hws,
-                           HotCold* out, hipStream_t s);
+// chunked.hip: the expert-centric (form 1) and token-centric (form 2) forms
+// for any d = 64 m up to 16384, the row taken in chunks; glu: the gated
+// variant (form 2 only).  ws: atomic_forward_ws_bytes(L, K).
+bool chunked_supported(int d);
+hipError_t launch_chunked(int bf16, int form, bool glu, int L, int d, int N, int K,
+                          const void* x, const void* w, const void* u, const void* v,
+                          const int32_t* task_token, const int32_t* task_expert,
+                          const float* task_gate, const int32_t* task_index,
+                          const int32_t* flat_expert, const float* flat_gate, float* y,
+                          bool accumulate, void* ws, hipStream_t s);
 
-// router.hip: the hybrid executor's two products on the large-tile MFMA
-// kernel.  cb[t, n] = bf16(g[t, n] silu(x_t . wh[n])) for n < dext[1] (row
-// stride hcap), then y (+)= cb vt^T over K = dext[1] (vt: [d, hcap]).
-hipError_t launch_hot_products(const uint16_t* x, const uint16_t* wh, const uint16_t* vt,
-                               const float* g, uint16_t* cb, float* y, int L, int d, int hcap,
-                               const int32_t* dext, int accumulate, hipStream_t s);
+// grouped.hip: the grouped form (bf16, K <= 64, rows of at most 4 KiB).  The
+// hot set comes from the sorted schedule (counts, active, task_expert); the
+// token tiles read the flattened selection fe / fg.  gws: grouped_ws_bytes.
+size_t grouped_ws_bytes(int L, int K, int d, int N);
+bool grouped_supported(int bf16, int d, int K);
+hipError_t launch_grouped(const uint16_t* x, const uint16_t* w, const uint16_t* v,
+                          const int32_t* task_expert, const int32_t* fe, const float* fg, int L,
+                          int K, int d, int N, float* y, int accumulate, void* gws,
+                          hipStream_t s);
 
 // flat_router.hip: the d x N router baseline
 size_t flat_router_ws_bytes(int L, int N);

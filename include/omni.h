@@ -64,7 +64,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 12 */
+int omni_abi_version(void);  /* 13 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -229,7 +229,7 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *
  *   y[t, :] = sum over scheduled tasks (t, e, g): g * silu(x[t,:] . W[e,:]) * V[e,:]
  *
- * Two execution forms, selected by `mode`:
+ * Three execution forms, selected by `mode`:
  *   OMNI_EXEC_EXPERT_CENTRIC: two kernels; the first walks the tasks in the
  *     schedule's (group, token) order and computes c = g * silu(x_t . W[e])
  *     per task, the second gathers y_t = sum_k c_tk V[e_tk] per token, so y
@@ -240,31 +240,40 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  *     token assembles its experts: x_t stays in registers, the token's W
  *     rows give the K coefficients, its V rows are summed into y_t.  Below
  *     4096 tokens each token gets several waves: its tasks are split over
- *     them for the coefficients, the columns of y_t for the sum.  Needs
- *     d * element size <= 4096 bytes (else UNSUPPORTED).
- *   OMNI_EXEC_HYBRID (bf16 only, else UNSUPPORTED; same row-size limit as
- *     the token-centric form): the experts with at least t tasks, t =
- *     max(2, ceil(L / 128)) doubled until no more than 2048 experts reach
- *     it, are "hot" (in id order); for them the coefficients of every (token, hot
- *     expert) pair come from one dense bf16 MFMA product x WH^T (c = g *
- *     silu(h) on task pairs, 0 elsewhere) and their share of y from a second
- *     product C VH, with c rounded to bf16 for it and fp32 accumulation (the
- *     pages' grouped execution on matrix units; gist.science explainer §2.2).
- *     The other tasks run through the token-centric kernels and are added
- *     onto that y.  Meant for skewed routing, where a few experts take many
- *     tasks; on MI355X it measured slower than the token-centric form at
- *     every workload tried (Zipf routing included), so AUTO never picks it.
- *     With none hot it gives the token-centric form's bits.  Expects
- *     distinct experts per token (as the top-K gives).
+ *     them for the coefficients, the columns of y_t for the sum.
+ *   Both forms hold a whole row per wave in registers where they can (d a
+ *   power of two; token-centric: rows of at most 4 KiB; expert-centric:
+ *   d <= 4096).  Every other width d = 64 m (m >= 1, d <= 16384) runs a pair
+ *   of chunked kernels: the coefficients with the rows taken in chunks of
+ *   64 * 2^j elements (2^j the largest power of two dividing m, at most 16
+ *   bytes per lane), then one wave per (token, chunk of columns) summing the
+ *   token's tasks in k order.
+ *   OMNI_EXEC_GROUPED (bf16 only, K <= 64, d = 64 * 2^p <= 2048, else
+ *     UNSUPPORTED): the pages' grouped execution on the matrix cores.  From
+ *     the sorted schedule's task_expert the tasks of every expert are
+ *     counted; the experts with at least tau tasks form
+ *     the hot set H (tau = max(2, ceil(L / 64)), doubled until at most 512
+ *     experts reach it; H in id order).  Each tile of 64 consecutive tokens
+ *     then computes S = x_tile W_H^T and y_tile = C V_H with two bf16 MFMA
+ *     products, C[t, h] = g * silu(S[t, h]) rounded to bf16 on the tile's
+ *     hot tasks and 0 elsewhere, so every hot expert's W and V rows are read
+ *     once per tile and reused by all its tokens; the tile's other (cold)
+ *     tasks run token by token in float32 as in the token-centric form, and
+ *     the hot product is added to the rows they wrote.  Meant for skewed
+ *     routing, where a few hundred experts take most tasks.  With no hot
+ *     expert it computes every task that way.  Agrees with the other forms within the bf16 rounding of the
+ *     hot coefficients; deterministic.
  *   OMNI_EXEC_AUTO: the form omni_atomic_forward_mode() names for the shape
  *     (the one that measured faster on MI355X).
- * The token-centric and hybrid forms with flat_expert / flat_gate set read no
- * other member of sched (those must still be non-null): such a call may run
- * while the omni_schedule_tasks call that fills the rest is still running on
- * another stream.  The expert-centric form reads the sorted tasks.
+ * The token-centric form with flat_expert / flat_gate set reads no other
+ * member of sched (those must still be non-null): such a call may run while
+ * the omni_schedule_tasks call that fills the rest is still running on
+ * another stream.  The expert-centric and grouped forms read the sorted
+ * schedule (the grouped form its task_expert), so they must follow it on the
+ * stream.
  * The expert- and token-centric forms evaluate every coefficient and every y
  * element with the same operations in the same order (k = 0..K-1), so they
- * give bit-identical y; the hybrid form agrees with them within the bf16
+ * give bit-identical y; the grouped form agrees with them within the bf16
  * rounding of its hot coefficients.
  *
  * x [L, d], w [N, d], v [N, d] of dt; sched: a schedule produced by
@@ -272,23 +281,26 @@ omni_status omni_schedule_tasks(int L, int K, int N, int B, omni_grouping groupi
  * y [L, d] float32 out, 16-byte aligned.  accumulate = 0: y is overwritten
  * with the routed output; accumulate != 0: the routed output is added to y as
  * it stands (e.g. onto the output of a shared dense branch).
- * ws / ws_bytes: at least omni_atomic_forward_workspace(...) bytes, 256-byte
- * aligned (8 bytes per task: a coefficient and an expert id, or the per-token
- * lists; for bf16 shapes the token-centric form supports, also the hybrid
- * form's buffers: 8 more bytes per task, about 12 KiB per token, 8 KiB per
- * column of d and 16 bytes per expert).  Requires d = 64 * 2^p with 64 <= d <= 4096 (else UNSUPPORTED);
+ * ws / ws_bytes: at least omni_atomic_forward_workspace(..., mode) bytes for
+ * the mode of the call, 256-byte aligned (8 bytes per task: a coefficient and
+ * an expert id, or the per-token lists; the grouped form adds a task count
+ * per expert id, 4 N bytes, 32 KiB of level lists and 2 KiB per column of d
+ * for the gathered W_H and V_H^T).  Requires d = 64 m with 64 <= d <= 16384 (else UNSUPPORTED);
  * 16-byte aligned x, w, v.  Deterministic.
  */
 typedef enum omni_exec_mode {
   OMNI_EXEC_AUTO = 0,
   OMNI_EXEC_EXPERT_CENTRIC = 1,
   OMNI_EXEC_TOKEN_CENTRIC = 2,
-  OMNI_EXEC_HYBRID = 3
+  OMNI_EXEC_GROUPED = 3
 } omni_exec_mode;
 
 /* The form OMNI_EXEC_AUTO runs for this shape (1, 2 or 3); 0 for invalid args. */
 int omni_atomic_forward_mode(omni_dtype dt, int L, int d, int N, int K, int B);
-size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B);
+/* Workspace of the call with this mode (AUTO: the form AUTO runs); 0 for
+   invalid arguments. */
+size_t omni_atomic_forward_workspace(omni_dtype dt, int L, int d, int N, int K, int B,
+                                     omni_exec_mode mode);
 omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B,
                                 const void* x, const void* w, const void* v,
                                 const omni_schedule* sched, float* y, int accumulate,
@@ -304,9 +316,11 @@ omni_status omni_atomic_forward(omni_dtype dt, int L, int d, int N, int K, int B
  *   y_t = sum_k g_tk * silu(x_t . W[e_tk]) * (x_t . U[e_tk]) * V[e_tk]
  *
  * (3d parameters per expert instead of 2d).  Arguments as omni_atomic_forward
- * plus u [N, d] of dt; the workspace is omni_atomic_forward_workspace(...).
- * Token-centric form only: requires d = 64 * 2^p with rows of at most 4 KiB
- * (bf16 d <= 2048, float32 d <= 1024), else UNSUPPORTED.  Deterministic.
+ * plus u [N, d] of dt; the workspace is omni_atomic_forward_workspace(...,
+ * OMNI_EXEC_TOKEN_CENTRIC).
+ * Token-centric form only (the chunked kernels for the widths whose rows do
+ * not fit in registers): requires d = 64 m with 64 <= d <= 16384, else
+ * UNSUPPORTED.  Deterministic.
  */
 omni_status omni_atomic_forward_glu(omni_dtype dt, int L, int d, int N, int K, int B,
                                     const void* x, const void* w, const void* u, const void* v,

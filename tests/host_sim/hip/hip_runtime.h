@@ -322,6 +322,7 @@ inline unsigned sim_mbcnt_hi(unsigned m, unsigned acc) {
 
 inline void __syncthreads() { sim::block_barrier(); }
 inline void __threadfence() { std::atomic_thread_fence(std::memory_order_seq_cst); }
+#define __builtin_amdgcn_sched_barrier(m) ((void)0)
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x0, x1, x2) sim::mfma_16x16x32_bf16((a), (b), (c))
 #define __builtin_amdgcn_fdot2_f32_bf16(a, b, c, clamp)                                  \
   ((c) + static_cast<float>((a)[0]) * static_cast<float>((b)[0]) +                      \

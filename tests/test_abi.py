@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.omni_abi_version() == 12
+    assert lib.omni_abi_version() == 13
     for code in range(5):
         assert lib.omni_status_string(code)
     assert lib.omni_status_string(99) == b"unknown status"
@@ -147,19 +147,20 @@ def test_atomic_forward_argument_checks(lib):
     assert call(w=MIS) == B.OMNI_ERR_INVALID_ARG
     assert call(mode=4) == B.OMNI_ERR_INVALID_ARG
     assert call(mode=-1) == B.OMNI_ERR_INVALID_ARG
-    # the hybrid form: bf16 only, rows as the token-centric form
+    # the grouped form: bf16 only, K <= 64, d a power of two up to 2048
     assert call(dt=0, mode=3) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=4096, mode=3) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=768, mode=3) == B.OMNI_ERR_UNSUPPORTED
+    assert call(K=65, mode=3) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=2048, mode=3) == B.OMNI_ERR_WORKSPACE
+    # the expert- and token-centric forms: any d = 64 m up to 16384
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
-    assert call(d=8192) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=16448) == B.OMNI_ERR_UNSUPPORTED
     assert call(d=32) == B.OMNI_ERR_UNSUPPORTED
-    # token-centric rows must fit 4 KiB: bf16 up to d = 2048, float32 up to 1024
-    assert call(d=4096, mode=2) == B.OMNI_ERR_UNSUPPORTED
-    assert call(dt=0, d=2048, mode=2) == B.OMNI_ERR_UNSUPPORTED
-    assert call(d=2048, mode=2) == B.OMNI_ERR_WORKSPACE
-    assert call(dt=0, d=1024, mode=2) == B.OMNI_ERR_WORKSPACE
-    assert call(d=4096, mode=1) == B.OMNI_ERR_WORKSPACE
+    for d in (192, 320, 768, 3072, 4096, 16384):
+        for mode in (0, 1, 2):
+            assert call(d=d, mode=mode) == B.OMNI_ERR_WORKSPACE, (d, mode)
+    assert call(dt=0, d=2048, mode=2) == B.OMNI_ERR_WORKSPACE
     assert call(L=0) == B.OMNI_OK
     assert call() == B.OMNI_ERR_WORKSPACE                  # L*K tasks need a workspace
     noidx = B.ScheduleStruct(*([1 << 20] * 6 + [0]))
@@ -169,12 +170,21 @@ def test_atomic_forward_argument_checks(lib):
     assert call(s=half) == B.OMNI_ERR_INVALID_ARG
     both = B.ScheduleStruct(*([1 << 20] * 9))
     assert call(s=both) == B.OMNI_ERR_WORKSPACE
-    assert lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256) >= 8 * 8192 * 64
-    # bf16 shapes the token-centric form supports also hold the hybrid buffers
-    # (8 more bytes per task, 12 KiB per token, 8 KiB per column, 16 per expert)
-    hyb = lib.omni_atomic_forward_workspace(1, 8192, 2048, 1 << 20, 64, 256)
-    assert hyb >= 16 * 8192 * 64 + 12288 * 8192 + 8192 * 2048 + 16 * (1 << 20)
-    assert lib.omni_atomic_forward_workspace(0, 8192, 1024, 1 << 20, 64, 256) < hyb // 4
+    ws = lib.omni_atomic_forward_workspace
+    # per form: 8 bytes per task; the grouped form adds a task count per
+    # expert id (4 bytes each), 16 level lists of 512 ids (32 KiB) and the
+    # gathered W_H and V_H^T (1 KiB each per column of d)
+    for mode in (1, 2):
+        assert 8 * 8192 * 64 <= ws(1, 8192, 2048, 1 << 20, 64, 256, mode) < 8 * 8192 * 64 + 4096
+    g = ws(1, 8192, 2048, 1 << 20, 64, 256, 3)
+    assert g >= 8 * 8192 * 64 + 4 * (1 << 20) + 32768 + 2 * 1024 * 2048
+    assert g < 8 * 8192 * 64 + 4 * (1 << 20) + 32768 + 2 * 1024 * 2048 + 8192
+    # auto sizes for the form it runs; an invalid mode or dtype asks for nothing
+    auto_form = lib.omni_atomic_forward_mode(1, 8192, 2048, 1 << 20, 64, 256)
+    assert ws(1, 8192, 2048, 1 << 20, 64, 256, 0) == ws(1, 8192, 2048, 1 << 20, 64, 256,
+                                                         auto_form)
+    assert ws(1, 8192, 2048, 1 << 20, 64, 256, 4) == 0
+    assert ws(2, 8192, 2048, 1 << 20, 64, 256, 1) == 0
 
 
 def test_atomic_forward_auto_mode(lib):
@@ -189,6 +199,7 @@ def test_atomic_forward_auto_mode(lib):
     assert mode(0, 64, 2048, 1024, 8, 16) == 1             # float32 row over 4 KiB
     assert mode(1, 8192, 4096, 1 << 20, 64, 256) == 1      # row over 4 KiB
     assert mode(0, 8192, 2048, 1 << 20, 64, 256) == 1      # float32 row over 4 KiB
+    assert mode(1, 8192, 768, 1 << 20, 64, 256) == 1       # d not a power of two (chunked)
     assert mode(3, 8192, 2048, 1 << 20, 64, 256) == 0      # bad dtype
     assert mode(1, 8192, 2048, 1 << 20, 0, 256) == 0       # bad K
 
@@ -253,7 +264,7 @@ def test_shared_mlp_argument_checks(lib):
 def test_atomic_forward_glu_argument_checks(lib):
     st = B.ScheduleStruct(*([1 << 20] * 7))
     f = lib.omni_atomic_forward_glu
-    nws = lib.omni_atomic_forward_workspace(1, 4, 128, 64, 2, 4)
+    nws = lib.omni_atomic_forward_workspace(1, 4, 128, 64, 2, 4, 2)
 
     def call(dt=1, L=4, d=128, N=64, K=2, Bg=4, x=FAKE, u=FAKE, y=FAKE, s=st, ws=FAKE, n=nws):
         return f(dt, L, d, N, K, Bg, x, FAKE, u, FAKE, ctypes.byref(s) if s is not None else None,
@@ -265,8 +276,12 @@ def test_atomic_forward_glu_argument_checks(lib):
     assert call(x=None) == B.OMNI_ERR_INVALID_ARG
     assert call(u=MIS) == B.OMNI_ERR_INVALID_ARG
     assert call(d=96) == B.OMNI_ERR_UNSUPPORTED
-    assert call(d=4096) == B.OMNI_ERR_UNSUPPORTED            # rows over 4 KiB
-    assert call(dt=0, d=2048) == B.OMNI_ERR_UNSUPPORTED
+    assert call(d=16448) == B.OMNI_ERR_UNSUPPORTED
+    # any d = 64 m up to 16384 (rows over 4 KiB or m not a power of two:
+    # chunked); no workspace, so the call stops before any launch
+    assert call(d=4096, ws=None, n=0) == B.OMNI_ERR_WORKSPACE
+    assert call(d=768, ws=None, n=0) == B.OMNI_ERR_WORKSPACE
+    assert call(dt=0, d=2048, ws=None, n=0) == B.OMNI_ERR_WORKSPACE
     assert call(n=nws - 1) == B.OMNI_ERR_WORKSPACE
     assert call(L=0, x=None, y=None) == B.OMNI_OK
 

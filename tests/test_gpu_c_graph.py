@@ -29,7 +29,7 @@ def test_graph_replay_matches_eager(name):
                dtype=torch.uint8, device="cuda")}
     sched = B.alloc_schedule(L, K, wl.N, wl.B, "cuda")
     code = 1 if wl.dtype == "bf16" else 0
-    ws = torch.empty(max(1, B.lib().omni_atomic_forward_workspace(code, L, wl.d, wl.N, K, wl.B)),
+    ws = torch.empty(max(1, B.lib().omni_atomic_forward_workspace(code, L, wl.d, wl.N, K, wl.B, 0)),
                      dtype=torch.uint8, device="cuda")
     y = torch.empty((L, wl.d), dtype=torch.float32, device="cuda")
 

@@ -24,6 +24,11 @@ GLU_CASES = {
     "k1": custom(L=40, d=128, Nr=16, Nc=16, kprime=1, K=1, B=1, dtype="bf16", index=503),
     "small": WORKLOADS["small"],
     "large": WORKLOADS["large"],
+    # d = 64 m not a power of two, and rows over 4 KiB (the chunked kernels)
+    "d768": custom(L=300, d=768, Nr=40, Nc=50, kprime=10, K=16, B=8, dtype="bf16", index=504),
+    "d4096": custom(L=70, d=4096, Nr=32, Nc=32, kprime=8, K=12, B=8, dtype="bf16", index=505),
+    "f32_d1536": custom(L=40, d=1536, Nr=16, Nc=24, kprime=6, K=9, B=4, dtype="f32",
+                        index=506),
 }
 
 
@@ -59,7 +64,7 @@ def test_glu_expert_parity(name):
     assert e1 <= TOL[wl.dtype] and e2 <= TOL[wl.dtype]
 
 
-def test_glu_expert_is_deterministic_and_rejects_unsupported_rows():
+def test_glu_expert_is_deterministic_and_rejects_unsupported_widths():
     wl = GLU_CASES["ragged_bf16"]
     inp = make_inputs(wl, parts=PARTS)
     t = {k: dev(v) for k, v in inp.items()}
@@ -68,9 +73,9 @@ def test_glu_expert_is_deterministic_and_rejects_unsupported_rows():
     b = B.atomic_forward_glu(t["x"], t["w"], t["u"], t["v"], out["schedule"])
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
-    # rows over 4 KiB are refused before anything is launched
-    x4 = torch.zeros((2, 4096), dtype=torch.bfloat16, device="cuda")
-    w4 = torch.zeros((8, 4096), dtype=torch.bfloat16, device="cuda")
+    # a width that is not a multiple of 64 is refused before anything is launched
+    x4 = torch.zeros((2, 72), dtype=torch.bfloat16, device="cuda")
+    w4 = torch.zeros((8, 72), dtype=torch.bfloat16, device="cuda")
     s4 = B.schedule_tasks(torch.zeros((2, 1), dtype=torch.int32, device="cuda"),
                           torch.ones((2, 1), dtype=torch.float32, device="cuda"), 8, 1)
     with pytest.raises(B.OmniError):
@@ -126,4 +131,4 @@ def test_flat_router_parity(name):
     want = OV.flat_router_logp(x[toks], wf, bias)
     dl = float(np.abs(logp[toks] - want).max())
     log(f"  selection bit-exact; gates max|d| {dg:.1e}; log p max|d| {dl:.1e}")
-    assert dl <= 2e-4
+    assert dl <= 1e-4  # the router bar; measured <= 3.8e-6 (N = 2^20)

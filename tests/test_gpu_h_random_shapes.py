@@ -1,13 +1,16 @@
 """Seeded random shapes through the C ABI.
 
 * The schedule, both groupings, bit-exact against the oracle, over shapes that
-  fall on both sides of every launch-path choice (one or several radix passes,
-  at most 32 sort tiles or more, at most 8 expert tiles or more).
+  fall on both sides of every launch-path choice (the one-workgroup schedule
+  up to 16,384 tasks and groups; one or several radix passes, at most 32 sort
+  tiles or more, at most 8 expert tiles or more).
 * The executor: the expert-centric and token-centric forms bit-identical to
   each other, and within the float tolerance of the oracle on sampled tokens,
   over row widths 64..2048 and token counts that take each token-centric
   kernel (several waves per token below 4096 tokens, one from 4096, four
-  tokens per wave from 8192, with a ragged last wave).
+  tokens per wave from 8192, with a ragged last wave); and over widths
+  d = 64 m that are not powers of two or whose rows are too long for the
+  register-resident kernels (the chunked kernels: d = 192 .. 4096).
 """
 import numpy as np
 import pytest
@@ -47,9 +50,13 @@ def _schedule_shapes(seed, n):
     return out
 
 
-# plus shapes with at most 8 expert tiles (N <= 32768) and a minimal one
+# plus shapes with at most 8 expert tiles (N <= 32768) and a minimal one, and
+# shapes the one-workgroup schedule takes (at most 16,384 tasks and groups):
+# decode-sized, the task limit with K = 1, ids up to 2^24, one group per expert
 SCHEDULE_SHAPES = _schedule_shapes(7, 12) + [(1500, 20, 20000, 8), (700, 64, 32768, 64),
-                                              (5, 3, 7, 1)]
+                                              (5, 3, 7, 1), (256, 64, 1 << 20, 64),
+                                              (16384, 1, 50, 7), (129, 64, 1 << 24, 16),
+                                              (500, 20, 3000, 1)]
 
 
 @pytest.mark.parametrize("grouping", ["active", "window"])
@@ -81,6 +88,17 @@ EXEC_SHAPES = [
     # more than 64 tasks per token (the kernels walk them 64 at a time)
     (8193, 128, 40000, 70, "bf16"),
     (100, 256, 5000, 100, "bf16"),
+    # d = 64 m, m not a power of two (chunks of 64 .. 512 elements), and rows
+    # longer than 4 KiB (token form chunked; the expert form holds d = 4096
+    # and float32 d = 2048 in registers, with the same sums in the same order)
+    (33, 192, 5000, 7, "bf16"),
+    (700, 768, 20000, 64, "bf16"),
+    (257, 1536, 9000, 70, "f32"),
+    (4100, 3072, 30000, 16, "bf16"),
+    (8192, 768, 600000, 40, "bf16"),
+    (64, 4096, 3000, 8, "bf16"),
+    (300, 2048, 5000, 9, "f32"),
+    (5, 320, 100, 3, "f32"),
 ]
 
 
@@ -96,13 +114,14 @@ def test_random_executor_forms_agree(L, d, N, K, dt):
     v = normal((N, d), seed + 4, float(d) ** -0.5, dt)
     tx, tw, tv = dev(x), dev(w), dev(v)
     sched = B.schedule_tasks(dev(idx), dev(gate), N, 16)
-    ys = {"expert": B.atomic_forward(tx, tw, tv, sched, mode="expert")}
-    if (2 if dt == "bf16" else 4) * d <= 4096:
-        ys["token"] = B.atomic_forward(tx, tw, tv, sched, mode="token")
-        # the token lists inverted from the sorted schedule instead of read
-        # from the flattened selection
-        sched.flat_expert = sched.flat_gate = None
-        ys["token_inverted"] = B.atomic_forward(tx, tw, tv, sched, mode="token")
+    ys = {"expert": B.atomic_forward(tx, tw, tv, sched, mode="expert"),
+          "token": B.atomic_forward(tx, tw, tv, sched, mode="token")}
+    # the token lists inverted from the sorted schedule instead of read from
+    # the flattened selection
+    flat = (sched.flat_expert, sched.flat_gate)
+    sched.flat_expert = sched.flat_gate = None
+    ys["token_inverted"] = B.atomic_forward(tx, tw, tv, sched, mode="token")
+    sched.flat_expert, sched.flat_gate = flat
     torch.cuda.synchronize()
     ref = host(ys["expert"])
     for name, y in ys.items():
@@ -115,7 +134,7 @@ def test_random_executor_forms_agree(L, d, N, K, dt):
     assert e <= TOL_Y[dt]
     # accumulate onto a seeded y0: every form the same bits, y0 + routed output
     y0 = np.random.default_rng(seed + 6).standard_normal((L, d)).astype(np.float32)
-    modes = ["expert"] + (["token"] if "token" in ys else [])
+    modes = ["expert", "token"]
     acc = {m: B.atomic_forward(tx, tw, tv, sched, y=dev(y0), accumulate=True, mode=m)
            for m in modes}
     torch.cuda.synchronize()

@@ -18,7 +18,7 @@ FIELDS = ("counts", "active", "group_offsets", "task_token", "task_expert", "tas
           "task_index")
 
 
-@pytest.mark.parametrize("mode", ["token", "hybrid"])
+@pytest.mark.parametrize("mode", ["token"])
 def test_schedule_overlaps_the_executor(mode):
     wl = custom(L=8200, d=512, Nr=64, Nc=64, kprime=16, K=16, B=32, dtype="bf16",
                 zipf_s=1.1, index=230)
