@@ -19,7 +19,7 @@ OMNI_OK, OMNI_ERR_INVALID_ARG, OMNI_ERR_WORKSPACE, OMNI_ERR_UNSUPPORTED, OMNI_ER
 OMNI_F32, OMNI_BF16 = 0, 1
 EXEC_MODES = {"auto": 0, "expert": 1, "token": 2, "grouped": 3}  # omni_exec_mode
 GROUPINGS = {"active": 0, "window": 1}             # omni_grouping
-ABI_VERSION = 13
+ABI_VERSION = 14
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -30,6 +30,7 @@ EXPORTS = (
     "omni_atomic_forward_workspace", "omni_atomic_forward", "omni_routed_backward_workspace",
     "omni_routed_backward", "omni_shared_mlp_workspace", "omni_shared_mlp",
     "omni_atomic_forward_glu", "omni_flat_router_workspace", "omni_flat_router_topk",
+    "omni_product_topk_static",
 )
 
 
@@ -55,6 +56,8 @@ _SIGS = {
     "omni_product_topk_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "omni_product_topk": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _sz, _vp]),
+    "omni_product_topk_static": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp]),
     "omni_schedule_max_groups": (_i, [_i, _i, _i, _i, _i]),
     "omni_schedule_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "omni_schedule_tasks": (_i, [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(ScheduleStruct),

@@ -3,12 +3,14 @@
 // before anything is enqueued; nothing here allocates or synchronises.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/omni.h"
 #include "launch.hpp"
 
 namespace {
 
-constexpr int kAbiVersion = 13;
+constexpr int kAbiVersion = 14;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -138,6 +140,46 @@ omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K, const fl
   if (!ws || ws_bytes < w.bytes || !aligned256(ws)) return OMNI_ERR_WORKSPACE;
   return topk_run(L, Nr, Nc, kprime, K, row_logits, col_logits, expert_idx, score, gate,
                   row_logp, col_logp, row_sel, col_sel, static_cast<char*>(ws), w, stream);
+}
+
+// omni_product_topk_static: the same call with its workspace in a fixed
+// device array (one per GPU, held until the process ends).  Host code never
+// passes the array's name to a kernel: the device address comes from
+// hipGetSymbolAddress, once per device, on the first call there.
+static __device__ __align__(256) uint8_t scratch[OMNI_TOPK_STATIC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[256];
+
+static omni_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return OMNI_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return OMNI_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OMNI_OK;
+}
+
+omni_status omni_product_topk_static(int L, int Nr, int Nc, int kprime, int K,
+                                     const float* row_logits, const float* col_logits,
+                                     int32_t* expert_idx, float* score, float* gate,
+                                     float* row_logp, float* col_logp, int32_t* row_sel,
+                                     int32_t* col_sel, hipStream_t stream) {
+  const omni_status a = topk_args(L, Nr, Nc, kprime, K, row_logits, col_logits, expert_idx,
+                                  score, gate);
+  if (a != OMNI_OK) return a;
+  if (L == 0) return OMNI_OK;
+  const TopkWs w = topk_ws_layout(L, kprime, row_sel == nullptr, col_sel == nullptr);
+  if (w.bytes > OMNI_TOPK_STATIC_SCRATCH_BYTES) return OMNI_ERR_WORKSPACE;
+  void* p = nullptr;
+  const omni_status e = scratch_ptr(&p);
+  if (e != OMNI_OK) return e;
+  return topk_run(L, Nr, Nc, kprime, K, row_logits, col_logits, expert_idx, score, gate,
+                  row_logp, col_logp, row_sel, col_sel, static_cast<char*>(p), w, stream);
 }
 
 static bool grouping_ok(omni_grouping g) {

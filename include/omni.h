@@ -64,7 +64,7 @@ typedef enum omni_dtype {
 } omni_dtype;
 
 /* ABI revision of this header. */
-int omni_abi_version(void);  /* 13 */
+int omni_abi_version(void);  /* 14 */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* omni_status_string(omni_status s);
@@ -136,6 +136,35 @@ omni_status omni_product_topk(int L, int Nr, int Nc, int kprime, int K,
                               float* row_logp, float* col_logp,
                               int32_t* row_sel, int32_t* col_sel,
                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * omni_product_topk_static — omni_product_topk for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation.  Arguments, results and
+ * errors as omni_product_topk, without the workspace: the call uses a fixed
+ * array of OMNI_TOPK_STATIC_SCRATCH_BYTES bytes in device memory that the
+ * library holds on every GPU it runs on until the process ends.  It calls
+ * no allocator.
+ *
+ * Limit: the call needs, in bytes,
+ *   A(4 L) + A(8 L) + (row_sel ? 0 : A(4 L k')) + (col_sel ? 0 : A(4 L k'))
+ * with A(n) = n rounded up to a multiple of 256 (a tie flag and two
+ * normalisers per token, then the per-axis lists the caller does not ask
+ * for); more than OMNI_TOPK_STATIC_SCRATCH_BYTES returns OMNI_ERR_WORKSPACE
+ * before anything is enqueued.  8 MiB holds 16,008 tokens with both lists
+ * at k' = 64, and 699,040 tokens when the caller passes row_sel and col_sel.
+ * The array is per GPU and shared by every call on that GPU: calls that
+ * overlap on one GPU (two streams, two threads) race and give unspecified
+ * results.  Nothing in it needs to start at zero (the kernels write every
+ * entry they read).  The GPU is the caller's current device.
+ */
+#define OMNI_TOPK_STATIC_SCRATCH_BYTES (8u << 20)
+omni_status omni_product_topk_static(int L, int Nr, int Nc, int kprime, int K,
+                                     const float* row_logits, const float* col_logits,
+                                     int32_t* expert_idx, float* score, float* gate,
+                                     float* row_logp, float* col_logp,
+                                     int32_t* row_sel, int32_t* col_sel,
+                                     hipStream_t stream);
 
 /*
  * How omni_schedule_tasks forms its groups.
