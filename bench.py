@@ -15,6 +15,7 @@ same four calls captured once into a HIP graph are timed beside it
 Prints one JSON line on stdout (progress goes to stderr).
 """
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -35,7 +36,7 @@ EXEC_SRCS = {  # the sources each executor form's kernels are built from
     "token": ("execute.hip", "rowfrag.hpp", "device.hpp"),
     "grouped": ("grouped.hip", "rowfrag.hpp", "device.hpp"),
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "atomic_forward_large_traffic.md")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "atomic_forward_*_traffic.md")
 EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "expert": "omni_atomic_forward, expert-centric: coef_kernel + gather_kernel",
     "token": "omni_atomic_forward, token-centric: one kernel (token_multi_kernel from 8192 "
@@ -62,14 +63,16 @@ def exec_src_hash(form):
 
 
 def measured_traffic(workload, form):
-    """Counter-derived HBM bytes per executor call, if taken on this kernel."""
-    if form not in EXEC_SRCS or not os.path.exists(TRAFFIC_FILE):
+    """Counter-derived HBM bytes per executor call, if taken on this kernel
+    (records in the profiles/atomic_forward_*_traffic.md summaries)."""
+    if form not in EXEC_SRCS:
         return None
-    for m in re.finditer(r"traffic_record:\s*(\{.*\})", open(TRAFFIC_FILE).read()):
-        rec = json.loads(m.group(1))
-        if (rec.get("workload") == workload and rec.get("form") == form
-                and rec.get("executor_src_sha256_16") == exec_src_hash(form)):
-            return rec.get("bytes_per_launch")
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        for m in re.finditer(r"traffic_record:\s*(\{.*\})", open(path).read()):
+            rec = json.loads(m.group(1))
+            if (rec.get("workload") == workload and rec.get("form") == form
+                    and rec.get("executor_src_sha256_16") == exec_src_hash(form)):
+                return rec.get("bytes_per_launch")
     return None
 
 
@@ -146,6 +149,77 @@ def cpu_baseline(inp, wl, target_s):
                       f"over {cores} processes on {cpu_model()}"}
 
 
+def decode_step(args, B, to_dev):
+    """The whole step (router, top-K, schedule, executor in auto's form) at the
+    decode workload (256 tokens, N = 2^20), launched one by one and as a HIP
+    graph replay, with the per-stage times: the latency-bound end of the
+    workloads, where launch overhead is the cost."""
+    import torch
+    from synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["decode"]
+    t = {k: to_dev(v) for k, v in make_inputs(wl).items()}
+    out = B.forward(t["x"], t["wr"], t["wc"], t["w"], t["v"], wl.kprime, wl.K, wl.B,
+                    t["row_bias"], t["col_bias"])
+    sel = {k: out[k] for k in ("expert_idx", "score", "gate")}
+    sel["workspace"] = torch.empty(
+        max(1, B.lib().omni_product_topk_workspace(wl.L, wl.Nr, wl.Nc, wl.kprime, wl.K)),
+        dtype=torch.uint8, device="cuda")
+    a, b, sched, y = out["row_logits"], out["col_logits"], out["schedule"], out["y"]
+    code = 1 if wl.dtype == "bf16" else 0
+    rws = torch.empty(max(1, B.lib().omni_router_logits_workspace(code, wl.L, wl.d, wl.Nr, wl.Nc)),
+                      dtype=torch.uint8, device="cuda")
+    form = B.atomic_forward_mode(t["x"].dtype, wl.L, wl.d, wl.N, wl.K, wl.B)
+    ews = torch.empty(max(1, B.lib().omni_atomic_forward_workspace(
+        code, wl.L, wl.d, wl.N, wl.K, wl.B, B.EXEC_MODES[form])), dtype=torch.uint8, device="cuda")
+    stages = {
+        "router": lambda: B.router_logits(t["x"], t["wr"], t["wc"], t["row_bias"], t["col_bias"],
+                                          row_logits=a, col_logits=b, workspace=rws),
+        "topk": lambda: B.product_topk(a, b, wl.kprime, wl.K, want_sel=False, want_logp=False,
+                                       out=sel),
+        "schedule": lambda: B.schedule_tasks(sel["expert_idx"], sel["gate"], wl.N, wl.B,
+                                             sched=sched),
+        "execute": lambda: B.atomic_forward(t["x"], t["w"], t["v"], sched, y=y, workspace=ews),
+    }
+
+    def step():
+        for f in stages.values():
+            f()
+
+    def timed(fn, reps):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t1) / reps
+
+    reps = max(args.steps, 50)
+    ms = timed(step, reps)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_ms = timed(graph.replay, reps)
+    ev = {}
+    for name, f in stages.items():
+        s0 = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(20):
+            f()
+        e0.record()
+        e0.synchronize()
+        ev[name] = s0.elapsed_time(e0) / 20
+    del t, out, graph
+    torch.cuda.empty_cache()
+    return {"workload": "decode", "L": wl.L, "ms_per_step": ms, "graph_ms_per_step": graph_ms,
+            "tokens_per_s": wl.L / (ms * 1e-3), "executor_form": form, "stages_ms": ev,
+            "steps": reps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +235,8 @@ def main():
                     help="skip timing the variants (gated experts, id-window grouping)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the HIP-graph replay of the step")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip timing the decode step (256 tokens), eager and as a graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run three device-to-device copies of this many MiB (a "
@@ -425,6 +501,11 @@ def main():
         del wf, fr
         say(f"[bench] variants: {json.dumps(variants)}")
 
+    decode = None
+    if not args.no_decode and wl.name != "decode":
+        decode = decode_step(args, B, to_dev)
+        say(f"[bench] decode step: {json.dumps(decode)}")
+
     rec = {
         "metric": METRIC,
         "value": L / (ms * 1e-3),
@@ -459,6 +540,7 @@ def main():
         "backward": bwd,
         "layer": layer,
         "variants": variants,
+        "decode_step": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

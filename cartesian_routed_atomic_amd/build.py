@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libomni.so")
 SOURCES = ["api.hip", "router.hip", "topk.hip", "schedule.hip", "execute.hip", "backward.hip",
-           "flat_router.hip", "grouped.hip", "chunked.hip", "schedule_small.hip"]
+           "flat_router.hip", "grouped.hip", "chunked.hip"]
 ARCH = os.environ.get("OMNI_OFFLOAD_ARCH", "gfx950")
 
 

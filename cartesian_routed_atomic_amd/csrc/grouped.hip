@@ -38,7 +38,7 @@
 // tasks, tau = max(2, ceil(L / 64)) doubled until at most kGfHot remain.
 // gf_level_kernel finds it in one parallel pass over the counts: for every
 // level tau0 * 2^j how many experts reach it and the first kGfHot of them;
-// its last workgroup picks the level and sorts that list.  gf_pack_kernel gathers the hot rows of W into one contiguous block
+// gf_select_kernel (one workgroup) then picks the level and sorts that list.  gf_pack_kernel gathers the hot rows of W into one contiguous block
 // (W_H, [kGfHot, d]) and those of V transposed (V_H^T, [d, kGfHot]), so both
 // MFMA operands are K-contiguous and the tiles' loads touch a few pages
 // instead of one per hot expert.
@@ -62,7 +62,7 @@ constexpr int kGfCS = kGfHot + 8;  // bf16 row stride of the C tile (16-byte pad
 constexpr int kGfMaxK = 64;        // tasks per token the tile kernel holds
 constexpr int kGfCntChunk = 4096;  // sorted tasks per counting workgroup
 constexpr int kGfCntLds = 4096;    // expert ids a counting workgroup counts in LDS
-constexpr int kGfMisc = 64;        // ints: [0] ticket, [1] |H|, [2] tau, [16 + j] level j counts
+constexpr int kGfMisc = 64;        // ints: [1] |H|, [2] tau, [16 + j] level j counts
 constexpr int kGfLevels = 16;      // thresholds tau0 * 2^j, j < kGfLevels
 constexpr int kGfLvl = 16;         // misc index of the level counts
 constexpr int kGfRing = 6;         // W-row slots per wave for the cold tasks (five in flight)
@@ -119,9 +119,6 @@ __device__ __forceinline__ int lower_bound_i32(P&& a, int n, int v) {
   return lo;
 }
 
-__device__ __forceinline__ int load_agent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 struct GfCntLds {
   int32_t cnt[kGfCntLds];
@@ -189,81 +186,88 @@ __global__ __launch_bounds__(256) void gf_count_kernel(const int32_t* __restrict
   }
 }
 
+constexpr int kGfLevelBlocks = 128;  // workgroups of the level pass (each walks N / 128 ids)
+constexpr int kGfLevelCap = 4096;    // experts a workgroup may stage: at most L K / tau0 <= 64 K reach tau0
+
 struct GfLevelLds {
-  int32_t lc[kGfLevels];     // experts of this workgroup at each level
-  int32_t lbase[kGfLevels];  // their first position in the level's list
-  int32_t flag, jstar;
-  int32_t srt[kGfHot];       // the last workgroup: the chosen level's list, sorted
+  int32_t lc[kGfLevels];      // staged experts at each level
+  int32_t lbase[kGfLevels];   // their first position in the level's list
+  int32_t lpos[kGfLevels];    // positions handed out so far
+  int32_t nq;
+  int32_t q[kGfLevelCap];     // staged experts
+  int8_t qtop[kGfLevelCap];   // the highest level each reaches
 };
 
-// The hot set, in one pass over the counts: for every level tau0 * 2^j
-// (tau0 = max(2, ceil(L / 64)), j < kGfLevels) the number of experts with
-// at least that many tasks, and the first kGfHot of them in a list (a
-// workgroup reserves its range of a list with one atomic per level).  The
-// last workgroup takes the lowest level at most kGfHot experts reach and
-// sorts its list by id: the hot ids, |H| and tau.
+// For every level tau0 * 2^j (tau0 = max(2, ceil(L / 64)), j < kGfLevels):
+// how many experts have at least that many tasks, and the first kGfHot of
+// them in a list.  A workgroup stages the experts of its id stride that reach
+// tau0 (no more than L K / tau0 in all), then reserves its range of each
+// level's list with one atomic per level.
 __global__ __launch_bounds__(256) void gf_level_kernel(const int32_t* __restrict__ cnt, int N,
                                                        int L, int32_t* __restrict__ misc,
-                                                       int32_t* __restrict__ lvl,
-                                                       int32_t* __restrict__ hot_ids) {
+                                                       int32_t* __restrict__ lvl) {
   __shared__ GfLevelLds S;
   const int tid = threadIdx.x;
   const long long tau0 = max(2, (L + kGfHotDiv - 1) / kGfHotDiv);
-  if (tid < kGfLevels) S.lc[tid] = 0;
+  if (tid < kGfLevels) S.lc[tid] = S.lpos[tid] = 0;
+  if (tid == 0) S.nq = 0;
   __syncthreads();
-  const int e = blockIdx.x * 256 + tid;
-  const long long c = e < N ? cnt[e] : 0;
-  int top = -1;  // the highest level this expert reaches
-  while (top + 1 < kGfLevels && c >= (tau0 << (top + 1))) ++top;
-  int rk[kGfLevels];
-#pragma unroll
-  for (int j = 0; j < kGfLevels; ++j) rk[j] = j <= top ? atomicAdd(&S.lc[j], 1) : 0;
+  for (int e = blockIdx.x * 256 + tid; e < N; e += gridDim.x * 256) {
+    const long long c = cnt[e];
+    if (c < tau0) continue;
+    int top = 0;  // the highest level this expert reaches
+    while (top + 1 < kGfLevels && c >= (tau0 << (top + 1))) ++top;
+    for (int j = 0; j <= top; ++j) atomicAdd(&S.lc[j], 1);
+    const int i = atomicAdd(&S.nq, 1);
+    if (i < kGfLevelCap) {  // always: the total is bounded as stated above
+      S.q[i] = e;
+      S.qtop[i] = static_cast<int8_t>(top);
+    }
+  }
   __syncthreads();
   if (tid < kGfLevels) S.lbase[tid] = S.lc[tid] ? atomicAdd(&misc[kGfLvl + tid], S.lc[tid]) : 0;
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kGfLevels; ++j) {
-    const int pos = S.lbase[j] + rk[j];
-    if (j <= top && pos < kGfHot) lvl[j * kGfHot + pos] = e;
+  const int nq = min(S.nq, kGfLevelCap);
+  for (int i = tid; i < nq; i += 256) {
+    const int top = S.qtop[i];
+    for (int j = 0; j <= top; ++j) {
+      const int pos = S.lbase[j] + atomicAdd(&S.lpos[j], 1);
+      if (pos < kGfHot) lvl[j * kGfHot + pos] = S.q[i];
+    }
   }
+}
 
-  // ---- the last workgroup to finish selects the hot set
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) S.flag = atomicAdd(&misc[0], 1) == static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!S.flag) return;
-  __threadfence();
-  // the lowest level at most kGfHot experts reach (the top level, tau0 *
-  // 2^15 > L, only with a token listing an expert more than once)
-  if (tid == 0) {
-    int js = kGfLevels - 1;
-    for (int j = kGfLevels - 1; j >= 0; --j)
-      if (load_agent(misc + kGfLvl + j) <= kGfHot) js = j;
-    S.jstar = js;
-  }
-  __syncthreads();
-  const int js = S.jstar;
-  const int H = min(load_agent(misc + kGfLvl + js), kGfHot);
-  for (int i = tid; i < kGfHot; i += 256)
-    S.srt[i] = i < H ? load_agent(lvl + js * kGfHot + i) : INT_MAX;
+// One workgroup, after the level pass: the lowest level that at most kGfHot
+// experts reach (the top level, tau0 * 2^15 > L, only with a token listing an
+// expert more than once), its list sorted by id: the hot ids, |H| and tau.
+__global__ __launch_bounds__(256) void gf_select_kernel(int L, int32_t* __restrict__ misc,
+                                                        const int32_t* __restrict__ lvl,
+                                                        int32_t* __restrict__ hot_ids) {
+  __shared__ int32_t srt[kGfHot];
+  const int tid = threadIdx.x;
+  const long long tau0 = max(2, (L + kGfHotDiv - 1) / kGfHotDiv);
+  int js = kGfLevels - 1;
+  for (int j = kGfLevels - 1; j >= 0; --j)
+    if (misc[kGfLvl + j] <= kGfHot) js = j;
+  const int H = min(misc[kGfLvl + js], kGfHot);
+  for (int i = tid; i < kGfHot; i += 256) srt[i] = i < H ? lvl[js * kGfHot + i] : INT_MAX;
   __syncthreads();
   for (int k = 2; k <= kGfHot; k <<= 1) {  // bitonic sort, ascending
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < kGfHot; i += 256) {
         const int p = i ^ j;
         if (p > i) {
-          const int a = S.srt[i], b = S.srt[p];
+          const int a = srt[i], b = srt[p];
           if ((a > b) == ((i & k) == 0)) {
-            S.srt[i] = b;
-            S.srt[p] = a;
+            srt[i] = b;
+            srt[p] = a;
           }
         }
       }
       __syncthreads();
     }
   }
-  for (int i = tid; i < H; i += 256) hot_ids[i] = S.srt[i];
+  for (int i = tid; i < H; i += 256) hot_ids[i] = srt[i];
   if (tid == 0) {
     misc[1] = H;
     misc[2] = static_cast<int>(tau0 << js);
@@ -673,14 +677,15 @@ hipError_t launch_grouped(const uint16_t* x, const uint16_t* w, const uint16_t* 
   int32_t* hot = reinterpret_cast<int32_t*>(base + ly.hot);
   uint16_t* vtf = reinterpret_cast<uint16_t*>(base + ly.vtf);
   uint16_t* whf = reinterpret_cast<uint16_t*>(base + ly.whf);
-  // counters and the misc block (ticket, |H|, tau, level counts) start at zero
+  // counters and the misc block (|H|, tau, level counts) start at zero
   const size_t n4 = ly.lvl / 16;
   hipLaunchKernelGGL(gf_zero_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0,
                      s, reinterpret_cast<int4*>(base), n4);
   hipLaunchKernelGGL(gf_count_kernel, dim3(static_cast<unsigned>((M + kGfCntChunk - 1) / kGfCntChunk)),
                      dim3(256), 0, s, task_expert, M, N, cnt);
-  hipLaunchKernelGGL(gf_level_kernel, dim3(static_cast<unsigned>((N + 255) / 256)), dim3(256), 0,
-                     s, cnt, N, L, misc, lvl, hot);
+  hipLaunchKernelGGL(gf_level_kernel, dim3(static_cast<unsigned>(min((N + 255) / 256, kGfLevelBlocks))),
+                     dim3(256), 0, s, cnt, N, L, misc, lvl);
+  hipLaunchKernelGGL(gf_select_kernel, dim3(1), dim3(256), 0, s, L, misc, lvl, hot);
   hipLaunchKernelGGL(gf_pack_kernel, dim3(static_cast<unsigned>(d / 64), kGfHot / 64),
                      dim3(256), 0, s, w, v, d, misc, hot, whf, vtf);
   // tokens per tile: 64 where that still gives a tile per CU (the hot rows are

@@ -49,15 +49,6 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
                            int32_t* group_offsets, int32_t* task_token, int32_t* task_expert,
                            float* task_gate, int32_t* task_index, void* ws, hipStream_t s);
 
-// schedule_small.hip: the whole schedule in one workgroup, for at most 16,384
-// tasks and groups (G = max_groups); no workspace
-bool schedule_small_fits(long long M, long long G);
-hipError_t launch_schedule_small(int L, int K, int N, int B, int window, int G,
-                                 const int32_t* expert_idx, const float* gate, int32_t* counts,
-                                 int32_t* active, int32_t* group_offsets, int32_t* task_token,
-                                 int32_t* task_expert, float* task_gate, int32_t* task_index,
-                                 hipStream_t s);
-
 // execute.hip
 size_t atomic_forward_ws_bytes(int L, int K);
 // true: read expert rows with the nontemporal hint (M tasks over N experts)

@@ -380,11 +380,6 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
                             s>>>(counts, group_offsets, ng, lay.max_groups);
     return hipGetLastError();
   }
-  // a few thousand tasks: one workgroup, one launch (schedule_small.hip)
-  if (schedule_small_fits(M, lay.max_groups))
-    return launch_schedule_small(L, K, N, B, window, lay.max_groups, expert_idx, gate, counts,
-                                 active, group_offsets, task_token, task_expert, task_gate,
-                                 task_index, s);
   char* base = static_cast<char*>(ws);
   uint8_t* flags = reinterpret_cast<uint8_t*>(base + lay.flags);
   int* tile_cnt = reinterpret_cast<int*>(base + lay.tile_cnt);

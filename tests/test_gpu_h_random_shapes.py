@@ -1,9 +1,8 @@
 """Seeded random shapes through the C ABI.
 
 * The schedule, both groupings, bit-exact against the oracle, over shapes that
-  fall on both sides of every launch-path choice (the one-workgroup schedule
-  up to 16,384 tasks and groups; one or several radix passes, at most 32 sort
-  tiles or more, at most 8 expert tiles or more).
+  fall on both sides of every launch-path choice (one or several radix passes,
+  at most 32 sort tiles or more, at most 8 expert tiles or more).
 * The executor: the expert-centric and token-centric forms bit-identical to
   each other, and within the float tolerance of the oracle on sampled tokens,
   over row widths 64..2048 and token counts that take each token-centric
@@ -51,8 +50,7 @@ def _schedule_shapes(seed, n):
 
 
 # plus shapes with at most 8 expert tiles (N <= 32768) and a minimal one, and
-# shapes the one-workgroup schedule takes (at most 16,384 tasks and groups):
-# decode-sized, the task limit with K = 1, ids up to 2^24, one group per expert
+# decode-sized, 16,384 tasks with K = 1, ids up to 2^24, one group per expert
 SCHEDULE_SHAPES = _schedule_shapes(7, 12) + [(1500, 20, 20000, 8), (700, 64, 32768, 64),
                                               (5, 3, 7, 1), (256, 64, 1 << 20, 64),
                                               (16384, 1, 50, 7), (129, 64, 1 << 24, 16),
