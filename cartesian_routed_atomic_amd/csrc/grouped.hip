@@ -13,24 +13,24 @@
 // groups.  So the reuse is organised per token tile instead: the executor
 // takes from the schedule the number of tasks of every active expert and
 // groups the experts it reuses most, the hot set H (at most kGfHot, in id
-// order), into one block of expert rows.  Each workgroup owns 64 consecutive
-// tokens and
-//   1. scatters the gates of its tasks on hot experts into a dense
-//      64 x |H| gate tile in LDS;
+// order), into one block of expert rows.  Then
+//   gf_cold_kernel runs every token's other (cold) tasks as the token-centric
+//     form does, one token per wave, x_t in registers and the cold W then V
+//     rows streamed whole, and writes every row of y;
+//   gf_tile_kernel, one workgroup per tile of 64 consecutive tokens,
+//   1. scatters the gates of the tile's hot tasks into a dense 64 x |H|
+//      gate tile in LDS;
 //   2. S = x_tile . W_H^T on MFMA (v_mfma_f32_16x16x32_bf16, float32
 //      accumulation), the hot rows of W read once per tile;
 //   3. C = bf16(G * silu(S)) in LDS (zero where a token has no task on that
 //      expert);
-//   4. runs the tile's cold tasks (experts outside H) token by token as the
-//      token-centric form does: x_t in registers, the cold W rows and then
-//      the cold V rows streamed whole, y_t = sum of c V[e] over them written
-//      (added to y_t with accumulate);
-//   5. y_tile^T = V_H^T . C^T on MFMA, 64 output columns at a time, added to
-//      the rows step 4 wrote (written plain where a token had no cold task).
+//   4. y_tile^T += V_H^T . C^T on MFMA, 64 output columns at a time.
 // The hot rows of W and V are thus read once per tile (256 times per call at
 // L = 16384) instead of once per task.  The cold rows are read whole, a row
 // per wave at a time: read in 64-column slices by the MFMA layout, 16 rows
-// per load instruction, they cost 2-3 times as much.
+// per load instruction, they cost 2-3 times as much; and in a kernel of
+// their own they run at three waves per SIMD instead of the tile kernel's
+// two (its LDS holds one workgroup per CU).
 //
 // The hot set comes from the schedule: gf_count_kernel walks the sorted tasks
 // (contiguous id ranges of active experts) and counts the tasks of every
@@ -65,7 +65,6 @@ constexpr int kGfCntLds = 4096;    // expert ids a counting workgroup counts in 
 constexpr int kGfMisc = 64;        // ints: [1] |H|, [2] tau, [16 + j] level j counts
 constexpr int kGfLevels = 16;      // thresholds tau0 * 2^j, j < kGfLevels
 constexpr int kGfLvl = 16;         // misc index of the level counts
-constexpr int kGfRing = 6;         // W-row slots per wave for the cold tasks (five in flight)
 
 // --------------------------------------------------------------- workspace
 
@@ -342,16 +341,11 @@ constexpr int kGfXS = 64 + 8;  // bf16 row stride of the staged x chunk (16-byte
 
 template <int TT>
 struct GfTileLds {
-  int32_t hot[kGfHot];  // the hot expert ids, ascending
-  int32_t ncold[TT];    // cold tasks per token of the tile
+  int32_t hot[kGfHot];        // the hot expert ids, ascending
   uint16_t xs[2][TT][kGfXS];  // step 2: two x chunks of 64 columns
   union {
-    float g[TT][kGfHot];  // steps 1-3: gates of the hot tasks (0 = no task)
-    struct {
-      uint16_t c[TT][kGfCS];      // steps 3-5: C tile (bf16 bits)
-      int32_t ce[8][kGfMaxK];     // step 4, per wave: the cold experts of its token
-      float cc[8][kGfMaxK];       // and their gates
-    } p;
+    float g[TT][kGfHot];      // steps 1-3: gates of the hot tasks (0 = no task)
+    uint16_t c[TT][kGfCS];    // steps 3-4: C tile (bf16 bits)
   } u;
 };
 
@@ -494,19 +488,85 @@ __device__ __forceinline__ void gf_gemm2(const uint16_t* const (&vrow)[4],
     if (u < nk - k0) gf_gemm2_step<TT>(av[u], c, k0 + u, fr, fq, a2);
 }
 
-// A tile of TT = 16, 32 or 64 tokens per workgroup of 8 waves.
-template <int EPL, int TT>
-__global__ __launch_bounds__(512) void gf_tile_kernel(
+constexpr int kGfRing = 4;  // row slots per wave of the cold kernel: three in flight (153 VGPRs, 3 waves / SIMD)
+
+// The cold tasks (experts outside the hot set), one token per wave as the
+// token-centric form runs its tasks: the token's cold tasks gathered into
+// lanes 0 .. nc - 1 in k order, x_t in registers, the cold W rows then the
+// cold V rows streamed whole through the ring, y_t written (added to y_t with
+// accumulate; zero where the token has no cold task).  Every token's row is
+// written here, so the tile kernel adds the hot product to all of them.
+// NT: the rows carry the nontemporal hint (stream_rows).
+template <int EPL, bool NT>
+__global__ __launch_bounds__(256, 3) void gf_cold_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ fe,
     const float* __restrict__ fg, int L, int K, int d, int N, const int32_t* __restrict__ misc,
+    const int32_t* __restrict__ hot_ids, float* __restrict__ y, int accumulate) {
+  __shared__ int32_t hot[kGfHot];
+  __shared__ int32_t ce[4][kGfMaxK];
+  __shared__ float cg[4][kGfMaxK];
+  const int tid = threadIdx.x, wv = tid >> 6, l = lane();
+  const int H = min(max(misc[1], 0), kGfHot);
+  for (int i = tid; i < H; i += 256) hot[i] = hot_ids[i];
+  __syncthreads();
+  const int tok = blockIdx.x * 4 + wv;
+  if (tok >= L) return;
+  int my_e = 0;
+  float my_g = 0.f;
+  bool cold = false;
+  if (l < K) {
+    const size_t m = static_cast<size_t>(tok) * K + l;
+    const int e = fe[m];
+    my_e = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
+    my_g = fg[m];
+    cold = H == 0 || gf_find_hot(hot, H, e) < 0;
+  }
+  const uint64_t cm = __ballot(cold);
+  const int nc = __popcll(cm);
+  float* yrow = y + static_cast<size_t>(tok) * d;
+  if (nc == 0) {  // uniform over the wave: a zero row, or y0 as it stands
+    if (!accumulate) {
+      float z[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) z[q] = 0.f;
+      store_row<uint16_t, EPL, kStorePlain>(z, yrow, 0);
+    }
+    return;
+  }
+  if (cold) {  // the cold tasks into lanes 0 .. nc - 1, in k order
+    const int j = mbcnt(cm);
+    ce[wv][j] = my_e;
+    cg[wv][j] = my_g;
+  }
+  wave_lds_fence();
+  my_e = l < nc ? ce[wv][l] : 0;
+  my_g = l < nc ? cg[wv][l] : 0.f;
+  RowFrag<uint16_t, EPL> xf;
+  xf.template fetch<NT>(x + static_cast<size_t>(tok) * d, l);
+  RowFrag<uint16_t, EPL> f[kGfRing];
+  const float h = token_dots<uint16_t, EPL, NT, kGfRing>(xf, W, my_e, nc, d, l, f);
+  const float my_c = my_g * (h / (1.f + __expf(-h)));
+  float acc[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
+  token_gather<uint16_t, EPL, NT, kGfRing>(V, my_e, my_c, nc, d, l, f, acc);
+  store_row<uint16_t, EPL, kStorePlain>(acc, yrow, accumulate);
+}
+
+// A tile of TT = 16, 32 or 64 tokens per workgroup of 8 waves.
+template <int EPL, int TT>
+__global__ __launch_bounds__(512) void gf_tile_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ fe,
+    const float* __restrict__ fg, int L, int K, int d, const int32_t* __restrict__ misc,
     const int32_t* __restrict__ hot_ids, const uint16_t* __restrict__ whf,
-    const uint16_t* __restrict__ vtf, float* __restrict__ y, int accumulate) {
+    const uint16_t* __restrict__ vtf, float* __restrict__ y) {
   constexpr int MT = TT / 16;
   __shared__ __attribute__((aligned(16))) GfTileLds<TT> S;
   const int tid = threadIdx.x, wv = tid >> 6, l = lane();
   const int t0 = blockIdx.x * TT;
   const int H = min(max(misc[1], 0), kGfHot);
+  if (H == 0) return;  // nothing hot: gf_cold_kernel has written y (uniform over the grid)
   const int Hp = (H + 63) & ~63;
   const int fr = l & 15, fq = l >> 4;
 
@@ -519,11 +579,11 @@ __global__ __launch_bounds__(512) void gf_tile_kernel(
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int i = tid + 512 * r;
-    tv[r] = (H > 0 && i < ntask) ? fe[static_cast<size_t>(t0) * K + i] : -1;
-    gv[r] = (H > 0 && i < ntask) ? fg[static_cast<size_t>(t0) * K + i] : 0.f;
+    tv[r] = i < ntask ? fe[static_cast<size_t>(t0) * K + i] : -1;
+    gv[r] = i < ntask ? fg[static_cast<size_t>(t0) * K + i] : 0.f;
   }
   for (int i = tid; i < H; i += 512) S.hot[i] = hot_ids[i];
-  if (H > 0) {
+  {
     float4* g4 = reinterpret_cast<float4*>(&S.u.g[0][0]);
     for (int i = tid; i < TT * kGfHot / 4; i += 512) g4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -540,13 +600,13 @@ __global__ __launch_bounds__(512) void gf_tile_kernel(
 
   // ---- 2. S = x_tile . W_H^T and 3. C = bf16(G * silu(S))
   const int ntiles = Hp / 16;
-  const int nj = H > 0 ? max(0, min(4, (ntiles - wv + 7) / 8)) : 0;
+  const int nj = max(0, min(4, (ntiles - wv + 7) / 8));
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (H > 0) {  // uniform over the workgroup: every wave stages its share of x
+  {  // every wave stages its share of x, nj = 0 included
     switch (nj) {
       case 0: gf_gemm1<EPL, TT, 0>(x, t0, L, whf, wv, l, tid, S.xs, acc); break;
       case 1: gf_gemm1<EPL, TT, 1>(x, t0, L, whf, wv, l, tid, S.xs, acc); break;
@@ -578,54 +638,11 @@ __global__ __launch_bounds__(512) void gf_tile_kernel(
       if (j < nj)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          S.u.p.c[mt * 16 + 4 * fq + q][(wv + 8 * j) * 16 + fr] = gf_bf16(cv[mt][j][q]);
+          S.u.c[mt * 16 + 4 * fq + q][(wv + 8 * j) * 16 + fr] = gf_bf16(cv[mt][j][q]);
 
-  // ---- 4. cold tasks, one token at a time per wave, as the token-centric form
-  // runs them: y_t = sum over the token's cold tasks of g silu(x_t . W[e]) V[e]
-  for (int tl = wv; tl < TT; tl += 8) {
-    const int tok = t0 + tl;
-    int nc = 0;
-    if (tok < L) {  // uniform over the wave
-      int my_e = 0;
-      float my_g = 0.f;
-      bool cold = false;
-      if (l < K) {
-        const size_t m = static_cast<size_t>(tok) * K + l;
-        const int e = fe[m];
-        my_e = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : 0;
-        my_g = fg[m];
-        cold = H == 0 || gf_find_hot(S.hot, H, e) < 0;
-      }
-      const uint64_t cm = __ballot(cold);
-      nc = __popcll(cm);
-      if (nc > 0) {
-        if (cold) {  // the cold tasks into lanes 0 .. nc - 1, in k order
-          const int j = mbcnt(cm);
-          S.u.p.ce[wv][j] = my_e;
-          S.u.p.cc[wv][j] = my_g;
-        }
-        wave_lds_fence();
-        my_e = l < nc ? S.u.p.ce[wv][l] : 0;
-        my_g = l < nc ? S.u.p.cc[wv][l] : 0.f;
-        wave_lds_fence();  // read before the wave's next token overwrites them
-        RowFrag<uint16_t, EPL> xf;
-        xf.load(x + static_cast<size_t>(tok) * d, l);
-        RowFrag<uint16_t, EPL> f[kGfRing];
-        const float h = token_dots<uint16_t, EPL, false, kGfRing>(xf, W, my_e, nc, d, l, f);
-        const float my_c = my_g * (h / (1.f + __expf(-h)));
-        float acc[EPL];
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
-        token_gather<uint16_t, EPL, false, kGfRing>(V, my_e, my_c, nc, d, l, f, acc);
-        store_row<uint16_t, EPL, kStorePlain>(acc, y + static_cast<size_t>(tok) * d, accumulate);
-      }
-    }
-    if (l == 0) S.ncold[tl] = nc;
-  }
-  if (H == 0) return;  // every task was cold: y is complete
-  __syncthreads();      // step 4's y rows and cold counts before step 5 adds to them
+  __syncthreads();  // the C tile complete before the second product reads it
 
-  // ---- 5. y_tile^T = V_H^T . C^T, 64 output columns per pass, added to y
+  // ---- 4. y_tile^T = V_H^T . C^T, 64 output columns per pass, added to y
   const int ncb = d / 64;
   for (int b = wv; b < ncb; b += 8) {
     const int c0 = b * 64;
@@ -638,23 +655,20 @@ __global__ __launch_bounds__(512) void gf_tile_kernel(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
       vrow[mt] = vtf + (static_cast<size_t>(c0 / 16 + mt) * (kGfHot / 32) * 64 + l) * 8;
-    gf_gemm2<TT>(vrow, S.u.p.c, Hp, fr, fq, a2);
-    // accumulator layout: column c0 + mt * 16 + 4 * fq + q, token nt * 16 + fr
+    gf_gemm2<TT>(vrow, S.u.c, Hp, fr, fq, a2);
+    // accumulator layout: column c0 + mt * 16 + 4 * fq + q, token nt * 16 + fr;
+    // the rows gf_cold_kernel wrote already hold y0 (with accumulate) plus the
+    // token's cold tasks
 #pragma unroll
     for (int nt = 0; nt < MT; ++nt) {
-      const int tl = nt * 16 + fr;
-      const int tok = t0 + tl;
+      const int tok = t0 + nt * 16 + fr;
       if (tok >= L) continue;
-      // rows step 4 wrote already hold y0 (with accumulate) plus the cold tasks
-      const bool add = accumulate || S.ncold[tl] > 0;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         float* p = y + static_cast<size_t>(tok) * d + c0 + mt * 16 + 4 * fq;
         float4 v = make_float4(a2[mt][nt][0], a2[mt][nt][1], a2[mt][nt][2], a2[mt][nt][3]);
-        if (add) {
-          const float4 o = *reinterpret_cast<const float4*>(p);
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-        }
+        const float4 o = *reinterpret_cast<const float4*>(p);
+        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
         *reinterpret_cast<float4*>(p) = v;
       }
     }
@@ -688,16 +702,26 @@ hipError_t launch_grouped(const uint16_t* x, const uint16_t* w, const uint16_t* 
   hipLaunchKernelGGL(gf_select_kernel, dim3(1), dim3(256), 0, s, L, misc, lvl, hot);
   hipLaunchKernelGGL(gf_pack_kernel, dim3(static_cast<unsigned>(d / 64), kGfHot / 64),
                      dim3(256), 0, s, w, v, d, misc, hot, whf, vtf);
+  // the cold tasks of every token first (they write every row of y), then the
+  // hot product of every tile added onto those rows
+  const bool nt = stream_rows(M, N);
+  const dim3 cgrid(static_cast<unsigned>((L + 3) / 4));
   // tokens per tile: 64 where that still gives a tile per CU (the hot rows are
   // read once per tile), fewer for smaller batches
   const int tt = L >= 256 * 64 ? 64 : (L >= 256 * 32 ? 32 : 16);
   const dim3 grid(static_cast<unsigned>((L + tt - 1) / tt));
-#define OMNI_GF_TT(EPL_, TT_)                                                                  \
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(gf_tile_kernel<EPL_, TT_>), grid, dim3(512), 0, s, x, w, v, \
-                     fe, fg, L, K, d, N, misc, hot, whf, vtf, y, accumulate)
-#define OMNI_GF(EPL_)                    \
-  if (tt == 64) OMNI_GF_TT(EPL_, 64);    \
-  else if (tt == 32) OMNI_GF_TT(EPL_, 32); \
+#define OMNI_GF_TT(EPL_, TT_)                                                                   \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(gf_tile_kernel<EPL_, TT_>), grid, dim3(512), 0, s, x, fe,   \
+                     fg, L, K, d, misc, hot, whf, vtf, y)
+#define OMNI_GF(EPL_)                                                                           \
+  if (nt)                                                                                       \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(gf_cold_kernel<EPL_, true>), cgrid, dim3(256), 0, s, x, w,  \
+                       v, fe, fg, L, K, d, N, misc, hot, y, accumulate);                         \
+  else                                                                                          \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(gf_cold_kernel<EPL_, false>), cgrid, dim3(256), 0, s, x, w, \
+                       v, fe, fg, L, K, d, N, misc, hot, y, accumulate);                         \
+  if (tt == 64) OMNI_GF_TT(EPL_, 64);                                                           \
+  else if (tt == 32) OMNI_GF_TT(EPL_, 32);                                                      \
   else OMNI_GF_TT(EPL_, 16)
   switch (d) {
     case 64: OMNI_GF(1); break;

@@ -380,32 +380,62 @@ __global__ __launch_bounds__(512) void router_gemm_bf16_big_kernel(
     }
     return;
   }
+  // The logits go through LDS so that every store to HBM is part of a
+  // contiguous row: in four rounds, the waves write the accumulators of 64
+  // tile rows (row tiles 2r and 2r + 1 of both wave rows) into a 64 x 256
+  // float tile, then the workgroup stores the tile row by row, 16 bytes per
+  // thread, with the bias (and, with acc_out, the old values) added.
+  // Storing straight from the accumulator layout wrote 4-byte pieces of 16
+  // rows per instruction (18 us of the 80 us call at L = 8192, N = 2^20).
+  constexpr int kCtLd = GBN + 4;  // floats per LDS row (16-byte pad)
+  float* ct = reinterpret_cast<float*>(smem);
+  const bool vec4 = (Nr & 3) == 0 && (Nc & 3) == 0;
+  __syncthreads();  // the ring's last reads are done: smem is free
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + j * 16 + fr;
-    if (n >= NT) continue;
-    const bool is_row = n < Nr;
-    const float bias = is_row ? (rb ? rb[n] : 0.f) : (cb ? cb[n - Nr] : 0.f);
-    float* col = is_row ? zr + n : zc + (n - Nr);
-    const size_t ld = is_row ? Nr : Nc;
-    // accumulate: read this column's old values first, all loads in flight
-    float old[8][4];
+  for (int r = 0; r < 4; ++r) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
-        old[i][q] = (acc_out && t < L) ? col[static_cast<size_t>(t) * ld] : 0.f;
-      }
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+        for (int q = 0; q < 4; ++q)
+          ct[(wm * 32 + h * 16 + fc * 4 + q) * kCtLd + wn * 64 + j * 16 + fr] =
+              acc[2 * r + h][j][q];
+    __syncthreads();
+    for (int e = tid; e < 64 * (GBN / 4); e += 512) {
+      const int rr = e / (GBN / 4), c = (e % (GBN / 4)) * 4;
+      const int t = m0 + (rr >> 5) * 128 + r * 32 + (rr & 31);
+      const int n = n0 + c;
+      if (t >= L || n >= NT) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&ct[rr * kCtLd + c]);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      if (vec4 && (n + 3 < Nr || (n >= Nr && n + 3 < NT))) {
+        const bool is_row = n < Nr;
+        const float* bias = is_row ? rb : cb;
+        const int nb = is_row ? n : n - Nr;
+        float* dst = (is_row ? zr + static_cast<size_t>(t) * Nr : zc + static_cast<size_t>(t) * Nc) + nb;
+        float4 o = bias ? *reinterpret_cast<const float4*>(bias + nb)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (acc_out) {
+          const float4 p = *reinterpret_cast<const float4*>(dst);
+          o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
+        }
+        *reinterpret_cast<float4*>(dst) = make_float4(vv[0] + o.x, vv[1] + o.y, vv[2] + o.z,
+                                                      vv[3] + o.w);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = m0 + wm * 128 + i * 16 + fc * 4 + q;
-        if (t >= L) continue;
-        col[static_cast<size_t>(t) * ld] = acc[i][j][q] + bias + old[i][q];
+        for (int u = 0; u < 4; ++u) {
+          const int nu = n + u;
+          if (nu >= NT) break;
+          const bool is_row = nu < Nr;
+          const float bias = is_row ? (rb ? rb[nu] : 0.f) : (cb ? cb[nu - Nr] : 0.f);
+          float* dst = is_row ? zr + static_cast<size_t>(t) * Nr + nu
+                              : zc + static_cast<size_t>(t) * Nc + (nu - Nr);
+          *dst = vv[u] + bias + (acc_out ? *dst : 0.f);
+        }
       }
     }
+    __syncthreads();  // the tile is read before the next round overwrites it
   }
 }
 

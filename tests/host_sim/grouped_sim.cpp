@@ -3,7 +3,7 @@
 // input file and writes y, the hot-set summary and the hot ids, for
 // tests/test_host_sim_grouped.py.
 //
-//   grouped_sim IN OUT LDS_FILL
+//   grouped_sim IN OUT LDS_FILL [NT]
 //   IN:  int32 L, K, d, N, accumulate;
 //        uint16 x [L, d], W [N, d], V [N, d] (bf16 bits);
 //        int32 flat_expert [L*K]; float32 flat_gate [L*K];
@@ -19,6 +19,11 @@
 #include "hip/hip_runtime.h"
 #include "grouped.hip"
 
+// stream_rows lives in execute.hip (whose kernels the wave model does not
+// compile); here it is the run's NT argument, so both cold-kernel variants run.
+static bool g_nt = false;
+bool omni::stream_rows(long long, long long) { return g_nt; }
+
 template <class T> static void rd(FILE* f, std::vector<T>& v) {
   if (std::fread(v.data(), sizeof(T), v.size(), f) != v.size()) sim::fail("short input file");
 }
@@ -27,11 +32,12 @@ template <class T> static void wr(FILE* f, const T* p, size_t n) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 4) {
-    std::fprintf(stderr, "usage: grouped_sim IN OUT LDS_FILL\n");
+  if (argc != 4 && argc != 5) {
+    std::fprintf(stderr, "usage: grouped_sim IN OUT LDS_FILL [NT]\n");
     return 2;
   }
   sim::g_lds_fill = static_cast<unsigned char>(std::atoi(argv[3]));
+  g_nt = argc == 5 && std::atoi(argv[4]) != 0;
   FILE* f = std::fopen(argv[1], "rb");
   if (!f) sim::fail("cannot open input");
   std::vector<int32_t> hdr(5);

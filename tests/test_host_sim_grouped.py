@@ -64,7 +64,7 @@ def _hot_rule(idx, L, N):
     return np.flatnonzero(cnt >= tau).astype(np.int32), tau
 
 
-def _run(sim, tag, L, K, d, N, s, seed, accumulate=False, fill=0):
+def _run(sim, tag, L, K, d, N, s, seed, accumulate=False, fill=0, nt=False):
     x = normal((L, d), seed, 1.0, "bf16")
     w = normal((N, d), seed + 1, d ** -0.5, "bf16")
     v = normal((N, d), seed + 2, d ** -0.5, "bf16")
@@ -83,8 +83,8 @@ def _run(sim, tag, L, K, d, N, s, seed, accumulate=False, fill=0):
         sched["task_expert"].astype(np.int32).tofile(f)
         y0.tofile(f)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
-    r = subprocess.run([sim["exe"], fin, fout, str(fill)], capture_output=True, text=True,
-                       env=env, timeout=900)
+    r = subprocess.run([sim["exe"], fin, fout, str(fill), str(int(nt))], capture_output=True,
+                       text=True, env=env, timeout=900)
     assert r.returncode == 0, f"{tag}: exit {r.returncode}\n{r.stderr[-4000:]}"
     b = np.fromfile(fout, np.uint8)
     y = b[:L * d * 4].view(np.float32).reshape(L, d)
@@ -131,3 +131,6 @@ def test_grouped_form_does_not_read_unwritten_lds(sim):
     a = _run(sim, "fill0", 150, 16, 128, 2048, 1.1, 11, fill=0)
     b = _run(sim, "fill255", 150, 16, 128, 2048, 1.1, 11, fill=255)
     np.testing.assert_array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
+    # the cold kernel with the nontemporal hint on its rows: the same bits
+    c = _run(sim, "nt", 150, 16, 128, 2048, 1.1, 11, nt=True)
+    np.testing.assert_array_equal(a["y"].view(np.uint32), c["y"].view(np.uint32))
