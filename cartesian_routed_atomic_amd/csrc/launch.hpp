@@ -40,6 +40,7 @@ struct ScheduleWs {
   size_t bytes;
   size_t flags, tile_cnt, rank, key0, val0, key1, val1, hist, dtot;  // byte offsets
   int n_ftiles, n_ttiles, passes, max_groups;
+  int dbits;  // digit bits per radix pass
 };
 // window = 0: groups of B active experts in id order; window != 0: group g
 // is the id window [g B, (g + 1) B), every window a group.

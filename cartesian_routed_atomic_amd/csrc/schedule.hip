@@ -12,15 +12,20 @@
 //      tiles before it, scans its own flags and writes rank[e] (position
 //      among active experts) and the ascending active list;
 //   3. stable LSD radix sort of the tasks by group g = rank[e] / B (or, in
-//      the fixed-window variant, g = e / B: the id window), 8 bits
-//      per pass.  Tasks enter in flatten order m = t*K + k, which is already
-//      token-major, so a stable sort by group alone yields (group, token)
-//      order with ties in flatten order.  Each pass: per-tile digit
+//      the fixed-window variant, g = e / B: the id window), as few passes of
+//      at most 11 bits as the largest possible group id needs (one pass up to
+//      2048 groups).  Tasks enter in flatten order m = t*K + k, which is
+//      already token-major, so a stable sort by group alone yields (group,
+//      token) order with ties in flatten order.  Each pass: per-tile digit
 //      histograms (the first pass computes the group keys on the way), a
-//      parallel scan of each digit's row of tile counts, then a stable
-//      scatter ranked with 8 ballots per element.  Passes beyond the digits
-//      that n_groups actually needs return at once;
-//   4. CSR group offsets from the group boundaries of the sorted keys.
+//      parallel scan of each digit's row of tile counts (with at most 32
+//      tiles the scatter kernel sums its rows itself), then a stable scatter
+//      ranked with one ballot per digit bit.  When several passes are
+//      possible, passes beyond the digits that n_groups actually needs
+//      return at once;
+//   4. CSR group offsets: a single pass writes them from its digit bases
+//      (the digit is the group); several passes take them from the group
+//      boundaries of the sorted keys.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -28,11 +33,13 @@ namespace omni {
 
 constexpr int kTile = 4096;   // experts per flag tile (256 threads x 16)
 constexpr int kInlineCountTiles = 8;  // up to 32,768 experts: no separate tile-count launch
-constexpr int kSTile = 2048;  // tasks per sort tile (512 threads x 4)
-// Up to this many sort tiles (65,536 tasks) the down-sweep reads its digit
-// rows of tile counts itself, one round of loads; measured: decode (8 tiles)
-// 31 -> 27 us per schedule, tiny 30 -> 25 us; at 64 tiles (two rounds) it
-// lost 3 us to the separate scan.
+constexpr int kMaxDigitBits = 11;
+constexpr int kMaxDigits = 1 << kMaxDigitBits;
+constexpr int kSortWaves = 8;  // waves of a sort block (512 threads)
+constexpr int kSortR = 4;  // tasks per lane: a sort tile is 2048 tasks
+constexpr int kSTile = 512 * kSortR;
+// Up to this many sort tiles the scatter kernel sums its digit rows of tile
+// counts itself (no row-scan launch).
 constexpr int kFuseTiles = 32;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -44,10 +51,16 @@ ScheduleWs schedule_ws_layout(int L, int K, int N, int B, int window) {
   w.n_ttiles = static_cast<int>((M + kSTile - 1) / kSTile);
   const long long mn = window ? N : (M < N ? M : N);  // every id window is a group
   w.max_groups = static_cast<int>((mn + B - 1) / B);
-  int bits = 0;
+  int bits = 1;
   while (bits < 31 && (1ll << bits) < w.max_groups) ++bits;  // groups are < max_groups
-  w.passes = bits <= 8 ? 1 : (bits + 7) / 8;
+  // One pass of up to 11 bits; beyond that passes of at most 8 bits, which
+  // measured faster than fewer wider ones (the per-tile work grows with the
+  // digit count: 3 x 7 bits 87 us, 2 x 10 bits 99 us for the B = 1 sort of
+  // 524,288 tasks; 1 x 11 bits 56 us, 2 x 8 bits 65 us for B = 256).
+  w.passes = bits <= kMaxDigitBits ? 1 : (bits + 7) / 8;
+  w.dbits = (bits + w.passes - 1) / w.passes;
   const size_t nt = static_cast<size_t>(w.n_ttiles > 0 ? w.n_ttiles : 1);
+  const size_t nd = static_cast<size_t>(1) << w.dbits;
   size_t o = 0;
   w.flags = o;    o = align256(o + static_cast<size_t>(w.n_ftiles) * kTile);
   w.tile_cnt = o; o = align256(o + static_cast<size_t>(w.n_ftiles) * 4);
@@ -56,21 +69,31 @@ ScheduleWs schedule_ws_layout(int L, int K, int N, int B, int window) {
   w.val0 = o;     o = align256(o + static_cast<size_t>(M) * 4);
   w.key1 = o;     o = align256(o + static_cast<size_t>(M) * 4);
   w.val1 = o;     o = align256(o + static_cast<size_t>(M) * 4);
-  w.hist = o;     o = align256(o + 256 * nt * 4);
-  w.dtot = o;     o = align256(o + 256 * 4);
+  w.hist = o;     o = align256(o + nd * nt * 4);
+  w.dtot = o;     o = align256(o + nd * 4);
   w.bytes = o;
   return w;
 }
 
-// Passes that n_groups actually needs: max group id n_groups - 1 < 256^eff.
-__device__ __forceinline__ int effective_passes(int n_groups) {
+// Passes that n_groups actually needs: max group id n_groups - 1 < 2^(db eff).
+// counts == NULL: a single pass is all the layout has.
+__device__ __forceinline__ int effective_passes(const int* counts, int db) {
+  if (!counts) return 1;
+  const long long n_groups = counts[1];
   int eff = 1;
-  long long lim = 256;
-  while (static_cast<long long>(n_groups) > lim && eff < 4) {
+  long long lim = 1ll << db;
+  while (n_groups > lim && eff < 3) {
     ++eff;
-    lim <<= 8;
+    lim <<= db;
   }
   return eff;
+}
+
+// Group of a task whose expert is e.  Ids outside [0, N) go to group 0: the
+// result is then unspecified but every access stays in bounds.
+__device__ __forceinline__ int group_key(int e, const int* __restrict__ rank, int N, int B,
+                                         int window) {
+  return static_cast<unsigned>(e) < static_cast<unsigned>(N) ? (window ? e : rank[e]) / B : 0;
 }
 
 __global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, size_t n16) {
@@ -78,8 +101,7 @@ __global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, size
   if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
 }
 
-// Ids outside [0, N) are ignored here and sent to group 0 below: the result is
-// then unspecified but every access stays in bounds.
+// Ids outside [0, N) are ignored here and sent to group 0 below.
 __global__ __launch_bounds__(256) void mark_kernel(const int32_t* __restrict__ idx, int M, int N,
                                                    uint8_t* __restrict__ flags) {
   const int m = blockIdx.x * 256 + threadIdx.x;
@@ -156,43 +178,101 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ f
   }
 }
 
-// Per-tile digit histogram, digit-major: hist[d * n_tt + tile].  The first
-// pass computes the group key of each task (kout) on the way.
+// Exclusive scan of up to kMaxDigits values that a 512-thread block holds
+// four per thread (thread t: digits 4t .. 4t + 3 in v, 0 past the digit
+// count).  ex[j] = sum of the digits below digit 4t + j.  red: kSortWaves
+// words of LDS.
+__device__ __forceinline__ void block_scan_digits(const uint32_t (&v)[4], uint32_t (&ex)[4],
+                                                  uint32_t* red) {
+  const uint32_t s = v[0] + v[1] + v[2] + v[3];
+  const uint32_t inc = wave_inclusive_scan(s);
+  const int w = threadIdx.x >> 6;
+  if (lane() == 63) red[w] = inc;
+  __syncthreads();
+  uint32_t run = inc - s;
+  for (int q = 0; q < kSortWaves; ++q) run += q < w ? red[q] : 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ex[j] = run;
+    run += v[j];
+  }
+}
+
+// Stable rank of one wave's 64 elements among the elements of the same digit
+// (db bits) this wave has ranked so far: lanes with equal digits find each
+// other with db ballots, and the lowest of them advances the wave's count of
+// that digit (whw: the wave's row of counts in LDS).
+__device__ __forceinline__ uint32_t wave_rank_digit(uint32_t d, bool valid, int db,
+                                                    uint16_t* whw) {
+  const int l = lane();
+  const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < kMaxDigitBits; ++bit) {
+    if (bit < db) {
+      const bool on = (d >> bit) & 1;
+      const uint64_t bm = __ballot(valid && on);
+      peers &= on ? bm : ~bm;
+    }
+  }
+  const uint64_t below = peers & lt;
+  const uint32_t before = whw[d];
+  wave_lds_fence();
+  if (valid && below == 0) whw[d] = static_cast<uint16_t>(before + __popcll(peers));
+  wave_lds_fence();
+  return before + static_cast<uint32_t>(__popcll(below));
+}
+
+// Per-tile digit histogram, digit-major: hist[digit * n_tt + tile].  The
+// first pass computes the group key of each task (kout) on the way.
 __global__ __launch_bounds__(512) void radix_up_kernel(
     const int* __restrict__ kin, const int32_t* __restrict__ idx, const int* __restrict__ rank,
-    int* __restrict__ kout, int M, int N, int B, int window, int pass, int n_tt,
+    int* __restrict__ kout, int M, int N, int B, int window, int pass, int db, int n_tt,
     const int* __restrict__ counts, int* __restrict__ hist) {
-  if (pass >= effective_passes(counts[1])) return;
-  __shared__ uint32_t h[256];
-  if (threadIdx.x < 256) h[threadIdx.x] = 0;
-  __syncthreads();
-  const int shift = 8 * pass;
+  if (pass >= effective_passes(counts, db)) return;
+  __shared__ uint32_t h[kMaxDigits];
+  const int nd = 1 << db;
+  for (int i = threadIdx.x; i < nd; i += 512) h[i] = 0;
+  const int shift = db * pass;
   const int base = blockIdx.x * kSTile;
+  int key[kSortR];
+  if (pass == 0) {
+    int e[kSortR];
 #pragma unroll
-  for (int r = 0; r < kSTile / 512; ++r) {
-    const int i = base + r * 512 + threadIdx.x;
-    if (i >= M) continue;
-    int key;
-    if (pass == 0) {
-      const int e = idx[i];
-      key = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? (window ? e : rank[e]) / B : 0;
-      kout[i] = key;
-    } else {
-      key = kin[i];
+    for (int r = 0; r < kSortR; ++r) {
+      const int i = base + r * 512 + threadIdx.x;
+      e[r] = i < M ? idx[i] : 0;
     }
-    atomicAdd(&h[(static_cast<uint32_t>(key) >> shift) & 255], 1u);
+#pragma unroll
+    for (int r = 0; r < kSortR; ++r) key[r] = group_key(e[r], rank, N, B, window);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kSortR; ++r) {
+      const int i = base + r * 512 + threadIdx.x;
+      key[r] = i < M ? kin[i] : 0;
+    }
   }
   __syncthreads();
-  if (threadIdx.x < 256) hist[threadIdx.x * n_tt + blockIdx.x] = static_cast<int>(h[threadIdx.x]);
+#pragma unroll
+  for (int r = 0; r < kSortR; ++r) {
+    const int i = base + r * 512 + threadIdx.x;
+    if (i >= M) continue;
+    if (pass == 0) kout[i] = key[r];
+    atomicAdd(&h[(static_cast<uint32_t>(key[r]) >> shift) & (nd - 1)], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nd; i += 512)
+    hist[static_cast<size_t>(i) * n_tt + blockIdx.x] = static_cast<int>(h[i]);
 }
 
 // Exclusive scan of each digit's row of tile counts; the row total goes to
 // dtot[d].  One wave per digit.
 __global__ __launch_bounds__(64) void radix_rowscan_kernel(int* __restrict__ hist, int n_tt,
-                                                           int pass,
+                                                           int pass, int db,
                                                            const int* __restrict__ counts,
                                                            int* __restrict__ dtot) {
-  if (pass >= effective_passes(counts[1])) return;
+  if (pass >= effective_passes(counts, db)) return;
   int* row = hist + static_cast<size_t>(blockIdx.x) * n_tt;
   const int l = lane();
   uint32_t carry = 0;
@@ -207,128 +287,123 @@ __global__ __launch_bounds__(64) void radix_rowscan_kernel(int* __restrict__ his
 }
 
 // Stable scatter of one pass.  Wave w of a tile ranks its 256 consecutive
-// elements 64 at a time: lanes with the same digit find each other with 8
-// ballots, the lowest of them bumps the wave's running count.  The last
-// effective pass also writes the task arrays.
-// fused != 0 (few tiles): hist holds the raw tile counts and each block sums
-// its digit rows itself (no radix_rowscan_kernel launch); a single-pass sort
-// then also writes the group offsets (G + 1 entries, spread over the blocks:
-// off[g] = tasks in groups below g), so no offsets_kernel launch either.
+// elements 64 at a time.  The last effective pass writes the task arrays
+// (and the keys only when write_keys: several passes, whose offsets come
+// from the sorted keys); a single effective pass also writes the group
+// offsets from its digit bases: off[g] = tasks in groups below g for
+// g <= G (an empty group gets the start of the next non-empty one, groups
+// past the last get M), spread over the blocks.
+// fused != 0 (at most kFuseTiles tiles): hist holds the raw tile counts and
+// each block sums its digit rows itself; else hist holds the row-scanned
+// counts and dtot the row totals.
 __global__ __launch_bounds__(512) void radix_down_kernel(
-    const int* __restrict__ kin, const int* __restrict__ vin, int M, int pass, int n_tt,
-    const int* __restrict__ hist, const int* __restrict__ dtot, const int* __restrict__ counts,
-    int* __restrict__ kout, int* __restrict__ vout, int K,
-    const int32_t* __restrict__ expert_idx, const float* __restrict__ gate,
-    int32_t* __restrict__ task_token, int32_t* __restrict__ task_expert,
-    float* __restrict__ task_gate, int32_t* __restrict__ task_index, int fused, int G,
-    int32_t* __restrict__ group_offsets) {
-  const int eff = effective_passes(counts[1]);
+    const int* __restrict__ kin, const int* __restrict__ vin, int M, int pass, int db, int n_tt,
+    const int* __restrict__ hist, const int* __restrict__ dtot, int fused,
+    const int* __restrict__ counts, int* __restrict__ kout, int* __restrict__ vout,
+    int write_keys, int K, const int32_t* __restrict__ expert_idx,
+    const float* __restrict__ gate, int32_t* __restrict__ task_token,
+    int32_t* __restrict__ task_expert, float* __restrict__ task_gate,
+    int32_t* __restrict__ task_index, int G, int32_t* __restrict__ group_offsets) {
+  const int eff = effective_passes(counts, db);
   if (pass >= eff) return;
   const bool last = pass == eff - 1;
-  constexpr int kW = 8, kR = kSTile / (kW * 64);
-  __shared__ uint32_t wh[kW][256];
-  __shared__ uint32_t goff[256];
-  __shared__ uint32_t tpre[256];
-  __shared__ uint32_t red[4];
+  __shared__ uint16_t wh[kSortWaves][kMaxDigits];
+  __shared__ uint32_t goff[kMaxDigits];
+  __shared__ uint32_t red[kSortWaves];
   const int tid = threadIdx.x, w = tid >> 6, l = lane();
-  for (int q = 0; q < kW; ++q)
-    if (tid < 256) wh[q][tid] = 0;
-  // digit base: exclusive scan of the digit totals (first 4 waves, 64 each)
-  if (tid < 256) {
-    uint32_t v, before;
-    if (fused) {  // this digit's tiles before this block, and all of them
-      const int* row = hist + static_cast<size_t>(tid) * n_tt;
-      uint32_t all = 0;
-      before = 0;
-      for (int b0 = 0; b0 < n_tt; b0 += 32) {  // 32 loads in flight per round
-        uint32_t c[32];
+  const int nd = 1 << db;
+  const int b = blockIdx.x;
+  // this wave's elements, with their task data on the last pass (m = i on a
+  // first pass, so those loads need not wait for vin)
+  const int base = b * kSTile + w * (kSortR * 64);
+  int kv[kSortR], vv[kSortR], ev[kSortR];
+  float gv[kSortR];
 #pragma unroll
-        for (int j = 0; j < 32; ++j)
-          c[j] = b0 + j < n_tt ? static_cast<uint32_t>(row[b0 + j]) : 0u;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          before += b0 + j < static_cast<int>(blockIdx.x) ? c[j] : 0u;
-          all += c[j];
-        }
-      }
-      v = all;
-    } else {
-      v = static_cast<uint32_t>(dtot[tid]);
-      before = static_cast<uint32_t>(hist[tid * n_tt + blockIdx.x]);
-    }
-    tpre[tid] = before;
-    const uint32_t inc = wave_inclusive_scan(v);
-    if (l == 63) red[w] = inc;
-    goff[tid] = inc - v;
-  }
-  __syncthreads();
-  if (tid < 256) {
-    uint32_t add = 0;
-    for (int q = 0; q < w; ++q) add += red[q];
-    goff[tid] += add;
-  }
-  __syncthreads();
-  if (fused && eff == 1) {  // single pass: the digit is the group
-    for (long long g = static_cast<long long>(blockIdx.x) * 512 + tid; g <= G;
-         g += static_cast<long long>(gridDim.x) * 512)
-      group_offsets[g] = g < 256 ? static_cast<int>(goff[g]) : M;
-  }
-  if (tid < 256) goff[tid] += tpre[tid];
-  __syncthreads();
-  const int shift = 8 * pass;
-  const int base = blockIdx.x * kSTile + w * (kR * 64);
-  const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  uint32_t dg[kR], lr[kR];
-  int kv[kR], vv[kR];
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
+  for (int r = 0; r < kSortR; ++r) {
     const int i = base + r * 64 + l;
     const bool valid = i < M;
-    const int k = valid ? kin[i] : 0;
-    const int v = valid ? (vin ? vin[i] : i) : 0;
-    const uint32_t d = (static_cast<uint32_t>(k) >> shift) & 255;
-    uint64_t peers = __ballot(valid);
+    kv[r] = valid ? kin[i] : 0;
+    vv[r] = valid ? (vin ? vin[i] : i) : 0;
+  }
+  if (last) {
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool on = (d >> bit) & 1;
-      const uint64_t bm = __ballot(valid && on);
-      peers &= on ? bm : ~bm;
+    for (int r = 0; r < kSortR; ++r) {
+      const bool valid = base + r * 64 + l < M;
+      ev[r] = valid ? expert_idx[vv[r]] : 0;
+      gv[r] = valid ? gate[vv[r]] : 0.f;
     }
-    const uint64_t below = peers & lt;
-    const uint32_t before = wh[w][d];
-    wave_lds_fence();
-    if (valid && below == 0) wh[w][d] = before + static_cast<uint32_t>(__popcll(peers));
-    wave_lds_fence();
-    dg[r] = d;
-    lr[r] = before + static_cast<uint32_t>(__popcll(below));
-    kv[r] = k;
-    vv[r] = v;
+  }
+  for (int i = tid; i < kSortWaves * nd; i += 512) wh[i >> db][i & (nd - 1)] = 0;
+  uint32_t v[4], ex[4], before[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int dj = 4 * tid + j;
+    v[j] = 0u;
+    before[j] = 0u;
+    if (dj < nd) {
+      const int* row = hist + static_cast<size_t>(dj) * n_tt;
+      if (fused) {
+        for (int t = 0; t < n_tt; ++t) {
+          const uint32_t c = static_cast<uint32_t>(row[t]);
+          v[j] += c;
+          before[j] += t < b ? c : 0u;
+        }
+      } else {
+        v[j] = static_cast<uint32_t>(dtot[dj]);
+        before[j] = static_cast<uint32_t>(row[b]);
+      }
+    }
+  }
+  block_scan_digits(v, ex, red);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * tid + j < nd) goff[4 * tid + j] = ex[j];
+  __syncthreads();
+  if (eff == 1) {
+    for (long long g = static_cast<long long>(b) * 512 + tid; g <= G;
+         g += static_cast<long long>(gridDim.x) * 512)
+      group_offsets[g] = g < nd ? static_cast<int>(goff[g]) : M;
   }
   __syncthreads();
-  if (tid < 256) {  // exclusive prefix of the per-wave counts of each digit
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * tid + j < nd) goff[4 * tid + j] = ex[j] + before[j];
+  __syncthreads();
+  const int shift = db * pass;
+  uint32_t dg[kSortR], lr[kSortR];
+#pragma unroll
+  for (int r = 0; r < kSortR; ++r) {
+    const bool valid = base + r * 64 + l < M;
+    dg[r] = (static_cast<uint32_t>(kv[r]) >> shift) & (nd - 1);
+    lr[r] = wave_rank_digit(dg[r], valid, db, wh[w]);
+  }
+  __syncthreads();
+  // each digit's per-wave counts -> counts in the waves before
+  for (int i = tid; i < nd; i += 512) {
     uint32_t run = 0;
 #pragma unroll
-    for (int q = 0; q < kW; ++q) {
-      const uint32_t c = wh[q][tid];
-      wh[q][tid] = run;
+    for (int q = 0; q < kSortWaves; ++q) {
+      const uint32_t c = wh[q][i];
+      wh[q][i] = static_cast<uint16_t>(run);
       run += c;
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
+  for (int r = 0; r < kSortR; ++r) {
     const int i = base + r * 64 + l;
     if (i >= M) continue;
     const uint32_t pos = goff[dg[r]] + wh[w][dg[r]] + lr[r];
     if (pos >= static_cast<uint32_t>(M)) continue;  // unreachable when counts agree
-    kout[pos] = kv[r];
-    vout[pos] = vv[r];
-    if (last) {
-      const int m = vv[r];
-      task_token[pos] = m / K;
-      task_expert[pos] = expert_idx[m];
-      task_gate[pos] = gate[m];
-      if (task_index) task_index[pos] = m;
+    if (!last) {
+      kout[pos] = kv[r];
+      vout[pos] = vv[r];
+    } else {
+      if (write_keys) kout[pos] = kv[r];
+      task_token[pos] = vv[r] / K;
+      task_expert[pos] = ev[r];
+      task_gate[pos] = gv[r];
+      if (task_index) task_index[pos] = vv[r];
     }
   }
 }
@@ -339,10 +414,11 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
 // are those of the last effective pass.
 __global__ __launch_bounds__(256) void offsets_kernel(const int* __restrict__ skey_even,
                                                       const int* __restrict__ skey_odd, int M,
-                                                      int G, const int* __restrict__ counts,
+                                                      int G, int db,
+                                                      const int* __restrict__ counts,
                                                       int* __restrict__ off) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  const int eff = effective_passes(counts[1]);
+  const int eff = effective_passes(counts, db);
   const int* skey = ((eff - 1) & 1) ? skey_odd : skey_even;
   if (i < M) {
     const int g = min(skey[i], G - 1);
@@ -368,6 +444,48 @@ static inline unsigned blocks_for(long long n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }
 
+static void launch_sort(const ScheduleWs& lay, int M, int N, int B, int window, int K,
+                        const int32_t* expert_idx, const float* gate, const int* rank,
+                        int32_t* counts, int32_t* group_offsets, int32_t* task_token,
+                        int32_t* task_expert, float* task_gate, int32_t* task_index, char* base,
+                        hipStream_t s) {
+  int* key0 = reinterpret_cast<int*>(base + lay.key0);
+  int* val0 = reinterpret_cast<int*>(base + lay.val0);
+  int* key1 = reinterpret_cast<int*>(base + lay.key1);
+  int* val1 = reinterpret_cast<int*>(base + lay.val1);
+  int* hist = reinterpret_cast<int*>(base + lay.hist);
+  int* dtot = reinterpret_cast<int*>(base + lay.dtot);
+  // a single pass needs no device-side pass count
+  const int* cnt = lay.passes > 1 ? counts : nullptr;
+  const int fused = lay.n_ttiles <= kFuseTiles ? 1 : 0;
+  // pass p reads (key, val) from buffer p & 1 and writes buffer (p + 1) & 1;
+  // pass 0 reads the group keys it computes itself (key0) and identity values
+  int* kb[2] = {key0, key1};
+  int* vb[2] = {val0, val1};
+  const int write_keys = lay.passes > 1 ? 1 : 0;
+  for (int p = 0; p < lay.passes; ++p) {
+    int* kin = kb[p & 1];
+    const int* vin = p == 0 ? nullptr : vb[p & 1];
+    hipLaunchKernelGGL(radix_up_kernel, dim3(lay.n_ttiles), dim3(512), 0, s, kin, expert_idx,
+                       rank, key0, M, N, B, window, p, lay.dbits, lay.n_ttiles, cnt, hist);
+    if (!fused)
+      hipLaunchKernelGGL(radix_rowscan_kernel, dim3(1u << lay.dbits), dim3(64), 0, s, hist,
+                         lay.n_ttiles, p, lay.dbits, cnt, dtot);
+    hipLaunchKernelGGL(radix_down_kernel, dim3(lay.n_ttiles), dim3(512), 0, s, kin, vin, M, p,
+                       lay.dbits, lay.n_ttiles, hist, dtot, fused, cnt, kb[(p + 1) & 1],
+                       vb[(p + 1) & 1], write_keys, K, expert_idx, gate, task_token, task_expert,
+                       task_gate, task_index, lay.max_groups, group_offsets);
+  }
+  // Several possible passes: the offsets come from the sorted keys (the last
+  // effective pass p leaves them in kb[(p + 1) & 1]); a single effective
+  // pass has written the same offsets already.
+  if (lay.passes > 1) {
+    const long long nthr = M > lay.max_groups + 1 ? M : lay.max_groups + 1;
+    hipLaunchKernelGGL(offsets_kernel, dim3(blocks_for(nthr, 256)), dim3(256), 0, s, key1, key0,
+                       M, lay.max_groups, lay.dbits, cnt, group_offsets);
+  }
+}
+
 hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t* expert_idx,
                            const float* gate, int32_t* counts, int32_t* active,
                            int32_t* group_offsets, int32_t* task_token, int32_t* task_expert,
@@ -376,55 +494,30 @@ hipError_t launch_schedule(int L, int K, int N, int B, int window, const int32_t
   const ScheduleWs lay = schedule_ws_layout(L, K, N, B, window);
   if (M == 0) {
     const int ng = window ? lay.max_groups : 0;
-    empty_schedule_kernel<<<blocks_for(static_cast<long long>(lay.max_groups) + 1, 256), 256, 0,
-                            s>>>(counts, group_offsets, ng, lay.max_groups);
+    hipLaunchKernelGGL(empty_schedule_kernel,
+                       dim3(blocks_for(static_cast<long long>(lay.max_groups) + 1, 256)),
+                       dim3(256), 0, s, counts, group_offsets, ng, lay.max_groups);
     return hipGetLastError();
   }
   char* base = static_cast<char*>(ws);
   uint8_t* flags = reinterpret_cast<uint8_t*>(base + lay.flags);
   int* tile_cnt = reinterpret_cast<int*>(base + lay.tile_cnt);
   int* rank = reinterpret_cast<int*>(base + lay.rank);
-  int* key0 = reinterpret_cast<int*>(base + lay.key0);
-  int* val0 = reinterpret_cast<int*>(base + lay.val0);
-  int* key1 = reinterpret_cast<int*>(base + lay.key1);
-  int* val1 = reinterpret_cast<int*>(base + lay.val1);
-  int* hist = reinterpret_cast<int*>(base + lay.hist);
-  int* dtot = reinterpret_cast<int*>(base + lay.dtot);
 
   const size_t n16 = static_cast<size_t>(lay.n_ftiles) * kTile / 16;
-  zero16_kernel<<<blocks_for(static_cast<long long>(n16), 256), 256, 0, s>>>(
-      reinterpret_cast<uint4*>(flags), n16);
-  mark_kernel<<<blocks_for(M, 256), 256, 0, s>>>(expert_idx, M, N, flags);
+  hipLaunchKernelGGL(zero16_kernel, dim3(blocks_for(static_cast<long long>(n16), 256)),
+                     dim3(256), 0, s, reinterpret_cast<uint4*>(flags), n16);
+  hipLaunchKernelGGL(mark_kernel, dim3(blocks_for(M, 256)), dim3(256), 0, s, expert_idx, M, N,
+                     flags);
   // few expert tiles: rank_kernel counts the flags before its tile itself
   const bool count_inline = lay.n_ftiles <= kInlineCountTiles;
-  if (!count_inline) tile_count_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, tile_cnt);
-  rank_kernel<<<lay.n_ftiles, 256, 0, s>>>(flags, N, count_inline ? nullptr : tile_cnt,
-                                           lay.n_ftiles, B, window, rank, active, counts);
-  // pass p reads (key, val) from buffer p & 1 and writes buffer (p + 1) & 1;
-  // pass 0 reads the group keys it computes itself (key0) and identity values
-  int* kb[2] = {key0, key1};
-  int* vb[2] = {val0, val1};
-  // few sort tiles: the down-sweep scans the tile counts itself
-  const int fused = lay.n_ttiles <= kFuseTiles ? 1 : 0;
-  for (int p = 0; p < lay.passes; ++p) {
-    int* kin = kb[p & 1];
-    const int* vin = p == 0 ? nullptr : vb[p & 1];
-    radix_up_kernel<<<lay.n_ttiles, 512, 0, s>>>(kin, expert_idx, rank, key0, M, N, B, window,
-                                                 p, lay.n_ttiles, counts, hist);
-    if (!fused) radix_rowscan_kernel<<<256, 64, 0, s>>>(hist, lay.n_ttiles, p, counts, dtot);
-    radix_down_kernel<<<lay.n_ttiles, 512, 0, s>>>(
-        kin, vin, M, p, lay.n_ttiles, hist, dtot, counts, kb[(p + 1) & 1], vb[(p + 1) & 1], K,
-        expert_idx, gate, task_token, task_expert, task_gate, task_index, fused,
-        lay.max_groups, group_offsets);
-  }
-  // A fused single-pass sort has written the offsets; with more possible
-  // passes the offsets come from the sorted keys (the last effective pass p
-  // leaves them in kb[(p + 1) & 1]).
-  if (!fused || lay.passes > 1) {
-    const long long nthr = M > lay.max_groups + 1 ? M : lay.max_groups + 1;
-    offsets_kernel<<<blocks_for(nthr, 256), 256, 0, s>>>(key1, key0, M, lay.max_groups, counts,
-                                                         group_offsets);
-  }
+  if (!count_inline)
+    hipLaunchKernelGGL(tile_count_kernel, dim3(lay.n_ftiles), dim3(256), 0, s, flags, tile_cnt);
+  hipLaunchKernelGGL(rank_kernel, dim3(lay.n_ftiles), dim3(256), 0, s, flags, N,
+                     count_inline ? static_cast<const int*>(nullptr) : tile_cnt, lay.n_ftiles, B,
+                     window, rank, active, counts);
+  launch_sort(lay, M, N, B, window, K, expert_idx, gate, rank, counts, group_offsets, task_token,
+              task_expert, task_gate, task_index, base, s);
   return hipGetLastError();
 }
 

@@ -332,6 +332,7 @@ inline void __threadfence() { std::atomic_thread_fence(std::memory_order_seq_cst
 #define __HIP_MEMORY_SCOPE_AGENT 3
 #define __hip_atomic_load(p, order, scope) __atomic_load_n((p), __ATOMIC_RELAXED)
 template <class T> inline T atomicAdd(T* p, T v) { T o = *p; *p = o + v; return o; }
+template <class T> inline T atomicOr(T* p, T v) { T o = *p; *p = o | v; return o; }
 
 template <class T> inline T __shfl(T v, int src, int width = 64) {
   const int base = OMNI_SIM_LANE & ~(width - 1);
