@@ -24,7 +24,8 @@
 // kernel therefore selects the top K of P (|P| <= 280 for K, k' <= 64) and
 // checks, per row, the first cell past the staircase: if none reaches tau
 // the answer is exact.  Otherwise (a float32 tie at tau) the token is
-// flagged and a second, plain kernel redoes its top K over all k'^2 cells.
+// flagged and its wave redoes its top K over all k'^2 cells, plainly: K
+// rounds, each taking the largest cell key below the previous round's.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -264,9 +265,9 @@ struct TopkLds {
 
 constexpr int kStairItems = 5;  // ceil(280 / 64): |P| <= 280 for K, k' <= 64
 
-// Main pass.  tie_flag[t] = 1 marks a token whose K-th score ties a cell past
-// the staircase; its outputs are then written by product_topk_fixup_kernel.
-// lse[2t], lse[2t+1] keep the row / column normalisers for that kernel.
+// tie_flag[t] = 1 marks a token whose K-th score ties a cell past the
+// staircase (its outputs then come from the exact walk over all cells);
+// lse[2t], lse[2t+1] keep the row / column normalisers.
 template <int NI>
 __global__ __launch_bounds__(256) void product_topk_kernel(
     const float* __restrict__ Zr, const float* __restrict__ Zc, int L, int Nr, int Nc, int kp,
@@ -408,49 +409,32 @@ __global__ __launch_bounds__(256) void product_topk_kernel(
   if (l < kp && len < kp) extra = fkey(S.av[l] + S.bv[len]) >= tau;
   const bool tie = __ballot(extra) != 0ull;
   if (l == 0) tie_flag[t] = tie ? 1 : 0;
-  if (!tie) write_outputs(best, t, K, expert_idx, score, gate);
-}
-
-// Exact top-K for the flagged tokens: K rounds, each taking the largest cell
-// key below the previous round's, over all k' x k' cells.  Lane r owns row r
-// (k' <= 64); columns are walked one at a time.  The axis values are rebuilt
-// as z - lse with the main pass's float32 normalisers, so they are the same
-// numbers the main pass selected on.
-__global__ __launch_bounds__(256) void product_topk_fixup_kernel(
-    const float* __restrict__ Zr, const float* __restrict__ Zc, int L, int Nr, int Nc, int kp,
-    int K, const int32_t* __restrict__ row_sel, const int32_t* __restrict__ col_sel,
-    const int32_t* __restrict__ tie_flag, const float* __restrict__ lse,
-    int32_t* __restrict__ expert_idx, float* __restrict__ score, float* __restrict__ gate) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), l = lane();
-  if (t >= L || tie_flag[t] == 0) return;
-  int ri = 0, ci = 0;
-  float av = 0.f, bv = 0.f;
-  if (l < kp) {
-    ri = row_sel[static_cast<size_t>(t) * kp + l];
-    ci = col_sel[static_cast<size_t>(t) * kp + l];
-    ri = min(max(ri, 0), Nr - 1);
-    ci = min(max(ci, 0), Nc - 1);
-    av = Zr[static_cast<size_t>(t) * Nr + ri] - lse[2 * static_cast<size_t>(t)];
-    bv = Zc[static_cast<size_t>(t) * Nc + ci] - lse[2 * static_cast<size_t>(t) + 1];
-  }
-  uint64_t prev = ~0ull, mine = 0;
-  for (int k = 0; k < K; ++k) {
-    uint64_t cur = 0;
-    for (int c = 0; c < kp; ++c) {
-      const float bc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), c));
-      const uint32_t cc = static_cast<uint32_t>(__builtin_amdgcn_readlane(ci, c));
-      const uint64_t key = sel_key(av + bc, static_cast<uint32_t>(ri) * Nc + cc);
-      if (l < kp && key < prev && key > cur) cur = key;
-    }
+  uint64_t out = best;
+  if (tie) {
+    // Exact top K over all k' x k' cells: K rounds, each taking the largest
+    // cell key below the previous round's.  Lane r owns row r; the columns
+    // are walked one at a time from LDS.  The axis values are the ones the
+    // selection above used.
+    const float av = (l < kp) ? S.av[l] : 0.f;
+    const uint32_t rbase = (l < kp) ? S.R[l] * static_cast<uint32_t>(Nc) : 0u;
+    uint64_t prev = ~0ull;
+    out = 0ull;
+    for (int k = 0; k < K; ++k) {
+      uint64_t cur = 0ull;
+      for (int c = 0; c < kp; ++c) {
+        const uint64_t key = sel_key(av + S.bv[c], rbase + S.C[c]);
+        if (l < kp && key < prev && key > cur) cur = key;
+      }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t u = __shfl_xor(cur, o);
-      cur = cur > u ? cur : u;
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(cur, o);
+        cur = cur > u ? cur : u;
+      }
+      if (l == k) out = cur;
+      prev = cur;
     }
-    if (l == k) mine = cur;
-    prev = cur;
   }
-  write_outputs(mine, t, K, expert_idx, score, gate);
+  write_outputs(out, t, K, expert_idx, score, gate);
 }
 
 hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, int Nc, int kp,
@@ -472,10 +456,6 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
   else if (n <= 1024) OMNI_TOPK(16);
   else OMNI_TOPK(32);
 #undef OMNI_TOPK
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(product_topk_fixup_kernel, dim3(grid), dim3(256), 0, s, zr, zc, L, Nr, Nc,
-                     kp, K, row_sel, col_sel, tie_flag, lse, expert_idx, score, gate);
   return hipGetLastError();
 }
 

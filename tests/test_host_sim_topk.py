@@ -16,7 +16,7 @@ live lanes at once, as the hardware does in lockstep.  Two builds:
 
 The main case is the tie-heavy 64 x 64 grid, k' = 16, K = 12, logits in
 steps of 0.25 over 97 tokens, where 28 tokens tie at the staircase threshold
-and take product_topk_fixup_kernel.
+and take the exact walk over all k'^2 cells.
 """
 import concurrent.futures as cf
 import os
