@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void chunk_gather_kernel(
       my_c = coef[o];
     }
     // the rows' chunk: the base pointer moved to the chunk's first column
-    token_gather<T, VEC, NT, kChRing>(V + col0, my_e, my_c, n, d, l, f, acc);
+    token_gather<T, VEC, NT, kChRing, false>(V + col0, my_e, my_c, n, d, l, f, acc);
   }
   store_row<T, VEC, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
                                                   accumulate);

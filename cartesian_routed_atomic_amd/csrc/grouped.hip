@@ -545,12 +545,12 @@ __global__ __launch_bounds__(256, 3) void gf_cold_kernel(
   RowFrag<uint16_t, EPL> xf;
   xf.template fetch<NT>(x + static_cast<size_t>(tok) * d, l);
   RowFrag<uint16_t, EPL> f[kGfRing];
-  const float h = token_dots<uint16_t, EPL, NT, kGfRing>(xf, W, my_e, nc, d, l, f);
+  const float h = token_dots<uint16_t, EPL, NT, kGfRing, false>(xf, W, my_e, nc, d, l, f);
   const float my_c = my_g * (h / (1.f + __expf(-h)));
   float acc[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
-  token_gather<uint16_t, EPL, NT, kGfRing>(V, my_e, my_c, nc, d, l, f, acc);
+  token_gather<uint16_t, EPL, NT, kGfRing, false>(V, my_e, my_c, nc, d, l, f, acc);
   store_row<uint16_t, EPL, kStorePlain>(acc, yrow, accumulate);
 }
 

@@ -177,31 +177,42 @@ __device__ __forceinline__ void store_row(const float (&acc)[EPL], float* __rest
 // Wave-level row streaming shared by the token-centric kernels and the grouped
 // form's cold tasks: the n (1 <= n <= 64) tasks of a chunk have their expert
 // ids in lanes 0..n-1 (my_e), and rows stream through a ring of RING register
-// slots with RING - 1 rows in flight.  Every load is issued unconditionally:
-// positions past the chunk re-read its last row (then in cache).  With a load
-// under a condition the compiler's wait counts must assume the path that
-// skipped it, and every step would wait for the row it had just requested.
-// The steps past the chunk (fewer than RING) compute on such a row into a lane
-// past n (token_dots) or with a zero coefficient (token_gather), so they
-// change nothing.
+// slots with RING - 1 rows in flight.  Two ways to end the ring:
+//   EXACT   loads and steps stop at task n - 1 (the loads past the chunk are
+//           skipped under a condition, so the compiler's wait counts assume
+//           the skipping path near the end);
+//   !EXACT  every load is issued: positions past the chunk re-read its last
+//           row (then in cache), and the steps past it compute on that row
+//           into a lane past n (token_dots) or with a zero coefficient
+//           (token_gather), so they change nothing.
+// Measured (us per executor call): the token-centric kernels at 64 tasks per
+// token run faster EXACT (large 665 against 682, mid 393 against 398, decode
+// 23.1 against 23.6: the re-read rows cost more than the looser waits); the
+// grouped form's cold tasks, about 13 per token, run faster !EXACT (its call
+// at mid 357 against 365, at decode 73 against 80).  The chunked gather keeps
+// !EXACT, the form it was built and measured with.
 
 // h_k = x_t . M[e_k] for the n tasks of a chunk (expert e_k in lane k); h_k
 // ends in lane k (lanes from n on hold unspecified finite values).
-template <typename T, int EPL, bool NT, int RING>
+template <typename T, int EPL, bool NT, int RING, bool EXACT = true>
 __device__ __forceinline__ float token_dots(const RowFrag<T, EPL>& xf, const T* __restrict__ M,
                                             int my_e, int n, int d, int l,
                                             RowFrag<T, EPL> (&f)[RING]) {
   float my_h = 0.f;
   const int last = n - 1;
 #pragma unroll
-  for (int s = 0; s < RING - 1; ++s)
+  for (int s = 0; s < RING - 1; ++s) {
+    if (EXACT && s >= n) break;
     f[s].template fetch<NT>(M + static_cast<size_t>(rdlane(my_e, min(s, last))) * d, l);
+  }
   for (int i = 0; i < n; i += RING) {
 #pragma unroll
     for (int s = 0; s < RING; ++s) {
       const int ii = i + s;
-      f[(s + RING - 1) % RING].template fetch<NT>(
-          M + static_cast<size_t>(rdlane(my_e, min(ii + RING - 1, last))) * d, l);
+      if (EXACT && ii >= n) break;
+      if (!EXACT || ii + RING - 1 < n)
+        f[(s + RING - 1) % RING].template fetch<NT>(
+            M + static_cast<size_t>(rdlane(my_e, min(ii + RING - 1, last))) * d, l);
       const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
       if (l == ii) my_h = h;
     }
@@ -211,20 +222,24 @@ __device__ __forceinline__ float token_dots(const RowFrag<T, EPL>& xf, const T* 
 
 // y_t (+)= sum_k c_k V[e_k] over the n tasks of a chunk (c_k, e_k in lane k),
 // the V rows streamed through the ring, fp32 accumulation in k order.
-template <typename T, int EPL, bool NT, int RING>
+template <typename T, int EPL, bool NT, int RING, bool EXACT = true>
 __device__ __forceinline__ void token_gather(const T* __restrict__ V, int my_e, float my_c, int n,
                                              int d, int l, RowFrag<T, EPL> (&f)[RING],
                                              float (&acc)[EPL]) {
   const int last = n - 1;
 #pragma unroll
-  for (int s = 0; s < RING - 1; ++s)
+  for (int s = 0; s < RING - 1; ++s) {
+    if (EXACT && s >= n) break;
     f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, min(s, last))) * d, l);
+  }
   for (int i = 0; i < n; i += RING) {
 #pragma unroll
     for (int s = 0; s < RING; ++s) {
       const int ii = i + s;
-      f[(s + RING - 1) % RING].template fetch<NT>(
-          V + static_cast<size_t>(rdlane(my_e, min(ii + RING - 1, last))) * d, l);
+      if (EXACT && ii >= n) break;
+      if (!EXACT || ii + RING - 1 < n)
+        f[(s + RING - 1) % RING].template fetch<NT>(
+            V + static_cast<size_t>(rdlane(my_e, min(ii + RING - 1, last))) * d, l);
       const float c = ii < n ? rdlane(my_c, min(ii, 63)) : 0.f;
 #pragma unroll
       for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
