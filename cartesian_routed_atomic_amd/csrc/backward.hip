@@ -94,22 +94,19 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
   xf.load(x + static_cast<size_t>(t) * d, l);
   Frag f[kBwdRing];
 
-  // The ring loads are unconditional (positions past the last task re-read
-  // it; their results land in no lane below K and add zero), so the
-  // compiler's wait counts keep kBwdRing - 1 rows in flight on every path.
-  // K <= 64 and the steps go four at a time, so every position is below 64.
-  const int lastk = K - 1;
   // pass 1: u_k = dy_t . V[e_k]
   float my_u = 0.f;
 #pragma unroll
   for (int s = 0; s < kBwdRing - 1; ++s)
-    f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, min(s, lastk))) * d, l);
+    if (s < K) f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, s)) * d, l);
   for (int i = 0; i < K; i += kBwdRing) {
 #pragma unroll
     for (int s = 0; s < kBwdRing; ++s) {
       const int k = i + s;
-      f[(s + kBwdRing - 1) % kBwdRing].template fetch<NT>(
-          V + static_cast<size_t>(rdlane(my_e, min(k + kBwdRing - 1, lastk))) * d, l);
+      if (k >= K) break;
+      if (k + kBwdRing - 1 < K)
+        f[(s + kBwdRing - 1) % kBwdRing].template fetch<NT>(
+            V + static_cast<size_t>(rdlane(my_e, k + kBwdRing - 1)) * d, l);
       float p = 0.f;
 #pragma unroll
       for (int q = 0; q < EPL; ++q) p = fmaf(dyr[q], f[s].get(q), p);
@@ -125,16 +122,17 @@ __global__ __launch_bounds__(256, 3) void bwd_token_kernel(
   float my_dh = 0.f, my_dg = 0.f, my_c = 0.f;
 #pragma unroll
   for (int s = 0; s < kBwdRing - 1; ++s)
-    f[s].template fetch<NT>(W + static_cast<size_t>(rdlane(my_e, min(s, lastk))) * d, l);
+    if (s < K) f[s].template fetch<NT>(W + static_cast<size_t>(rdlane(my_e, s)) * d, l);
   for (int i = 0; i < K; i += kBwdRing) {
 #pragma unroll
     for (int s = 0; s < kBwdRing; ++s) {
       const int k = i + s;
-      f[(s + kBwdRing - 1) % kBwdRing].template fetch<NT>(
-          W + static_cast<size_t>(rdlane(my_e, min(k + kBwdRing - 1, lastk))) * d, l);
+      if (k >= K) break;
+      if (k + kBwdRing - 1 < K)
+        f[(s + kBwdRing - 1) % kBwdRing].template fetch<NT>(
+            W + static_cast<size_t>(rdlane(my_e, k + kBwdRing - 1)) * d, l);
       const float h = wave_sum(frag_dot<EPL>(xf, f[s]));
-      // past the last task: g = 0 (lanes from K on), so dh = 0 and acc is unchanged
-      const float g = k < K ? rdlane(my_g, k) : 0.f, u = rdlane(my_u, k);
+      const float g = rdlane(my_g, k), u = rdlane(my_u, k);
       const float sg = 1.f / (1.f + __expf(-h));
       const float sv = h * sg;
       const float dh = g * (sg * (1.f + h * (1.f - sg))) * u;
@@ -329,26 +327,24 @@ __global__ __launch_bounds__(256) void seg_reduce_kernel(
 #pragma unroll
   for (int q = 0; q < EPL; ++q) av[q] = aw[q] = 0.f;
   int seg_start = 0;
-  // unconditional ring loads (positions past the chunk re-read its last task,
-  // and only positions below n are summed), so the compiler's wait counts
-  // keep R - 1 tasks in flight; n <= 64 and R divides 64, so k < 64
-  const int last = n - 1;
 #pragma unroll
   for (int s = 0; s < R - 1; ++s) {
-    const size_t o = static_cast<size_t>(rdlane(my_t, min(s, last))) * d;
-    fy[s].load(dyc + o, l);
-    fx[s].load(xc + o, l);
+    if (s < n) {
+      const size_t o = static_cast<size_t>(rdlane(my_t, s)) * d;
+      fy[s].load(dyc + o, l);
+      fx[s].load(xc + o, l);
+    }
   }
   for (int i = 0; i < n; i += R) {
 #pragma unroll
     for (int s = 0; s < R; ++s) {
       const int k = i + s;
-      {
-        const size_t o = static_cast<size_t>(rdlane(my_t, min(k + R - 1, last))) * d;
+      if (k >= n) break;
+      if (k + R - 1 < n) {
+        const size_t o = static_cast<size_t>(rdlane(my_t, k + R - 1)) * d;
         fy[(s + R - 1) % R].load(dyc + o, l);
         fx[(s + R - 1) % R].load(xc + o, l);
       }
-      if (k >= n) continue;
       const float ck = rdlane(my_c, k), hk = rdlane(my_h, k);
 #pragma unroll
       for (int q = 0; q < EPL; ++q) {
