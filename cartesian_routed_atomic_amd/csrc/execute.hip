@@ -141,22 +141,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     my_e = static_cast<unsigned>(my_e) < static_cast<unsigned>(N) ? my_e : 0;
     const float my_c = (l < n) ? coef[base + l] : 0.f;
     Frag f[kRing];
-    // loads unconditional (see token_gather): positions past n re-read row n - 1
-    const int last = n - 1;
-#pragma unroll
-    for (int s = 0; s < kRing - 1; ++s)
-      f[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, min(s, last))) * d + col0, l);
-    for (int i = 0; i < n; i += kRing) {
-#pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        const int ii = i + s;
-        f[(s + kRing - 1) % kRing].template fetch<NT>(
-            V + static_cast<size_t>(rdlane(my_e, min(ii + kRing - 1, last))) * d + col0, l);
-        const float c = ii < n ? rdlane(my_c, min(ii, 63)) : 0.f;
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) acc[q] = fmaf(c, f[s].get(q), acc[q]);
-      }
-    }
+    token_gather<T, EPL, NT, kRing>(V + col0, my_e, my_c, n, d, l, f, acc);
   }
   store_row<T, EPL, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
                                                   accumulate);
@@ -399,22 +384,7 @@ __global__ __launch_bounds__(64 * WS) void token_split_kernel(
     const int my_e = l < n ? se[l] : 0;
     const float my_c = l < n ? sc[l] : 0.f;
     FragB g[kSplitRing];
-    // loads unconditional (see token_gather): positions past n re-read row n - 1
-    const int last = n - 1;
-#pragma unroll
-    for (int s = 0; s < kSplitRing - 1; ++s)
-      g[s].template fetch<NT>(V + static_cast<size_t>(rdlane(my_e, min(s, last))) * d + col0, l);
-    for (int i = 0; i < n; i += kSplitRing) {
-#pragma unroll
-      for (int s = 0; s < kSplitRing; ++s) {
-        const int ii = i + s;
-        g[(s + kSplitRing - 1) % kSplitRing].template fetch<NT>(
-            V + static_cast<size_t>(rdlane(my_e, min(ii + kSplitRing - 1, last))) * d + col0, l);
-        const float c = ii < n ? rdlane(my_c, min(ii, 63)) : 0.f;
-#pragma unroll
-        for (int q = 0; q < EPLB; ++q) acc[q] = fmaf(c, g[s].get(q), acc[q]);
-      }
-    }
+    token_gather<T, EPLB, NT, kSplitRing>(V + col0, my_e, my_c, n, d, l, g, acc);
     __syncthreads();  // the next chunk's coefficients overwrite sc / se
   }
   store_row<T, EPLB, NT ? kStoreDevice : kStoreNT>(acc, y + static_cast<size_t>(t) * d + col0,
