@@ -342,8 +342,12 @@ def main():
         graph_ms = timed(graph.replay)
         say(f"[bench] graph replay: {args.steps} replays, {graph_ms:.3f} ms/step")
 
-    # per-stage times (HIP events on the stream the kernels run on)
-    def ev_time(fn, reps=10):
+    # per-stage times (HIP events on the stream the kernels run on), after two
+    # untimed calls (a form's first calls in a process run measurably slower)
+    def ev_time(fn, reps=10, warmup=2):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
