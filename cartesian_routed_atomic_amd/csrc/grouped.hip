@@ -38,7 +38,9 @@
 // tasks, tau = max(2, ceil(L / 64)) doubled until at most kGfHot remain.
 // gf_level_kernel finds it in one parallel pass over the counts: for every
 // level tau0 * 2^j how many experts reach it and the first kGfHot of them;
-// gf_select_kernel (one workgroup) then picks the level and sorts that list.  gf_pack_kernel gathers the hot rows of W into one contiguous block
+// gf_select_kernel (one workgroup) then picks the level and sorts that list
+// (each id placed at the count of smaller ids).  gf_pack_kernel gathers the
+// hot rows of W into one contiguous block
 // (W_H, [kGfHot, d]) and those of V transposed (V_H^T, [d, kGfHot]), so both
 // MFMA operands are K-contiguous and the tiles' loads touch a few pages
 // instead of one per hot expert.
@@ -132,14 +134,17 @@ struct GfCntLds {
 __global__ __launch_bounds__(256) void gf_count_kernel(const int32_t* __restrict__ texp, int M,
                                                        int N, int32_t* __restrict__ cnt) {
   __shared__ GfCntLds S;
+  constexpr int R = kGfCntChunk / 256;  // tasks per thread, held in registers
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * kGfCntChunk;
-  const int m1 = min(M, m0 + kGfCntChunk);
-
+  int ev[R];
   int emin = INT_MAX, emax = INT_MIN;
-  for (int m = m0 + tid; m < m1; m += 256) {
-    const int e = texp[m];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int m = m0 + r * 256 + tid;
+    const int e = m < M ? texp[m] : -1;
+    ev[r] = static_cast<unsigned>(e) < static_cast<unsigned>(N) ? e : -1;
+    if (ev[r] >= 0) {
       emin = min(emin, e);
       emax = max(emax, e);
     }
@@ -170,18 +175,16 @@ __global__ __launch_bounds__(256) void gf_count_kernel(const int32_t* __restrict
     const int ns = static_cast<int>(span);
     for (int i = tid; i < ns; i += 256) S.cnt[i] = 0;
     __syncthreads();
-    for (int m = m0 + tid; m < m1; m += 256) {
-      const int e = texp[m];
-      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) atomicAdd(&S.cnt[e - emin], 1);
-    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (ev[r] >= 0) atomicAdd(&S.cnt[ev[r] - emin], 1);
     __syncthreads();
     for (int i = tid; i < ns; i += 256)
       if (S.cnt[i]) atomicAdd(&cnt[emin + i], S.cnt[i]);
   } else {
-    for (int m = m0 + tid; m < m1; m += 256) {
-      const int e = texp[m];
-      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) atomicAdd(&cnt[e], 1);
-    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (ev[r] >= 0) atomicAdd(&cnt[ev[r]], 1);
   }
 }
 
@@ -242,31 +245,34 @@ __global__ __launch_bounds__(256) void gf_level_kernel(const int32_t* __restrict
 __global__ __launch_bounds__(256) void gf_select_kernel(int L, int32_t* __restrict__ misc,
                                                         const int32_t* __restrict__ lvl,
                                                         int32_t* __restrict__ hot_ids) {
-  __shared__ int32_t srt[kGfHot];
+  __shared__ int32_t ids[kGfHot];
+  __shared__ int32_t pick[2];
   const int tid = threadIdx.x;
   const long long tau0 = max(2, (L + kGfHotDiv - 1) / kGfHotDiv);
-  int js = kGfLevels - 1;
-  for (int j = kGfLevels - 1; j >= 0; --j)
-    if (misc[kGfLvl + j] <= kGfHot) js = j;
-  const int H = min(misc[kGfLvl + js], kGfHot);
-  for (int i = tid; i < kGfHot; i += 256) srt[i] = i < H ? lvl[js * kGfHot + i] : INT_MAX;
-  __syncthreads();
-  for (int k = 2; k <= kGfHot; k <<= 1) {  // bitonic sort, ascending
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < kGfHot; i += 256) {
-        const int p = i ^ j;
-        if (p > i) {
-          const int a = srt[i], b = srt[p];
-          if ((a > b) == ((i & k) == 0)) {
-            srt[i] = b;
-            srt[p] = a;
-          }
-        }
-      }
-      __syncthreads();
+  if (tid < 64) {  // the lowest level at most kGfHot experts reach (the last if none)
+    const int c = tid < kGfLevels ? misc[kGfLvl + tid] : 0;
+    const uint64_t ok = __ballot(tid < kGfLevels && c <= kGfHot);
+    const int js = ok ? __builtin_ctzll(ok) : kGfLevels - 1;
+    if (tid == js) {
+      pick[0] = js;
+      pick[1] = min(c, kGfHot);
     }
   }
-  for (int i = tid; i < H; i += 256) hot_ids[i] = srt[i];
+  __syncthreads();
+  const int js = pick[0], H = pick[1];
+  for (int i = tid; i < kGfHot; i += 256) ids[i] = i < H ? lvl[js * kGfHot + i] : INT_MAX;
+  __syncthreads();
+  // ascending by id: each id's position is the number of smaller ids (the ids
+  // are distinct; the slots past H hold INT_MAX and count for none)
+  for (int i = tid; i < H; i += 256) {
+    const int mine = ids[i];
+    int r = 0;
+    for (int j = 0; j < H; j += 4) {
+      const int4 q = *reinterpret_cast<const int4*>(&ids[j]);
+      r += (q.x < mine) + (q.y < mine) + (q.z < mine) + (q.w < mine);
+    }
+    hot_ids[r] = mine;
+  }
   if (tid == 0) {
     misc[1] = H;
     misc[2] = static_cast<int>(tau0 << js);
