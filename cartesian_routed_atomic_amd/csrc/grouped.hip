@@ -661,10 +661,20 @@ __global__ __launch_bounds__(512) void gf_tile_kernel(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
       vrow[mt] = vtf + (static_cast<size_t>(c0 / 16 + mt) * (kGfHot / 32) * 64 + l) * 8;
-    gf_gemm2<TT>(vrow, S.u.c, Hp, fr, fq, a2);
     // accumulator layout: column c0 + mt * 16 + 4 * fq + q, token nt * 16 + fr;
     // the rows gf_cold_kernel wrote already hold y0 (with accumulate) plus the
-    // token's cold tasks
+    // token's cold tasks.  Their old values are loaded before the product, so
+    // the loads run under it (rows past L re-read the tile's first row).
+    float4 yo[MT][4];
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt) {
+      const int tok = min(t0 + nt * 16 + fr, L - 1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        yo[nt][mt] = *reinterpret_cast<const float4*>(y + static_cast<size_t>(tok) * d + c0 +
+                                                      mt * 16 + 4 * fq);
+    }
+    gf_gemm2<TT>(vrow, S.u.c, Hp, fr, fq, a2);
 #pragma unroll
     for (int nt = 0; nt < MT; ++nt) {
       const int tok = t0 + nt * 16 + fr;
@@ -672,9 +682,9 @@ __global__ __launch_bounds__(512) void gf_tile_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         float* p = y + static_cast<size_t>(tok) * d + c0 + mt * 16 + 4 * fq;
-        float4 v = make_float4(a2[mt][nt][0], a2[mt][nt][1], a2[mt][nt][2], a2[mt][nt][3]);
-        const float4 o = *reinterpret_cast<const float4*>(p);
-        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        const float4 o = yo[nt][mt];
+        const float4 v = make_float4(a2[mt][nt][0] + o.x, a2[mt][nt][1] + o.y,
+                                     a2[mt][nt][2] + o.z, a2[mt][nt][3] + o.w);
         *reinterpret_cast<float4*>(p) = v;
       }
     }
