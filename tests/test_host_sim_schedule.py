@@ -99,10 +99,8 @@ CASES = [
     ("window2", 20, 4, 10000, 2, True, 0.0, 7),
     # 35 tiles of 2048: the separate row scan, offsets from the digit bases
     ("wide", 1100, 64, 1 << 17, 64, False, 0.0, 8),
-    # 132 tiles (268,800 tasks), one 11-bit pass
-    ("tile8k", 4200, 64, 1 << 18, 128, False, 0.0, 9),
-    # three 6-bit passes (262,400 possible groups), Zipf routing
-    ("tile8k2", 4100, 64, 1 << 20, 1, False, 0.8, 10),
+    # three 6-bit passes (70,400 possible groups), Zipf routing
+    ("threepass", 1100, 64, 1 << 17, 1, False, 0.8, 10),
 ]
 
 
