@@ -12,15 +12,15 @@
 //      tiles before it, scans its own flags and writes rank[e] (position
 //      among active experts) and the ascending active list;
 //   3. stable LSD radix sort of the tasks by group g = rank[e] / B (or, in
-//      the fixed-window variant, g = e / B: the id window), as few passes of
-//      at most 11 bits as the largest possible group id needs (one pass up to
-//      2048 groups).  Tasks enter in flatten order m = t*K + k, which is
-//      already token-major, so a stable sort by group alone yields (group,
-//      token) order with ties in flatten order.  Each pass: per-tile digit
-//      histograms (the first pass computes the group keys on the way), a
-//      parallel scan of each digit's row of tile counts (with at most 32
-//      tiles the scatter kernel sums its rows itself), then a stable scatter
-//      ranked with one ballot per digit bit.  When several passes are
+//      the fixed-window variant, g = e / B: the id window): one pass of up
+//      to 11 bits (up to 2048 groups), else passes of at most 8 bits.  Tasks
+//      enter in flatten order m = t*K + k, which is already token-major, so
+//      a stable sort by group alone yields (group, token) order with ties in
+//      flatten order.  Each pass: per-tile digit histograms (the first pass
+//      computes the group keys on the way), a parallel scan of each digit's
+//      tile counts (with at most 32 tiles the scatter kernel sums them
+//      itself), then a stable scatter ranked with one ballot per digit bit.
+//      When several passes are
 //      possible, passes beyond the digits that n_groups actually needs
 //      return at once;
 //   4. CSR group offsets: a single pass writes them from its digit bases
@@ -224,12 +224,14 @@ __device__ __forceinline__ uint32_t wave_rank_digit(uint32_t d, bool valid, int 
   return before + static_cast<uint32_t>(__popcll(below));
 }
 
-// Per-tile digit histogram, digit-major: hist[digit * n_tt + tile].  The
-// first pass computes the group key of each task (kout) on the way.
+// Per-tile digit histogram, digit-major (hist[digit * n_tt + tile]) or, with
+// tmaj, tile-major (hist[tile * nd + digit]: each block writes its row
+// whole, which pays with 2048 digits).  The first pass computes the group key
+// of each task (kout) on the way.
 __global__ __launch_bounds__(512) void radix_up_kernel(
     const int* __restrict__ kin, const int32_t* __restrict__ idx, const int* __restrict__ rank,
     int* __restrict__ kout, int M, int N, int B, int window, int pass, int db, int n_tt,
-    const int* __restrict__ counts, int* __restrict__ hist) {
+    int tmaj, const int* __restrict__ counts, int* __restrict__ hist) {
   if (pass >= effective_passes(counts, db)) return;
   __shared__ uint32_t h[kMaxDigits];
   const int nd = 1 << db;
@@ -263,7 +265,8 @@ __global__ __launch_bounds__(512) void radix_up_kernel(
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nd; i += 512)
-    hist[static_cast<size_t>(i) * n_tt + blockIdx.x] = static_cast<int>(h[i]);
+    hist[tmaj ? static_cast<size_t>(blockIdx.x) * nd + i
+              : static_cast<size_t>(i) * n_tt + blockIdx.x] = static_cast<int>(h[i]);
 }
 
 // Exclusive scan of each digit's row of tile counts; the row total goes to
@@ -286,6 +289,52 @@ __global__ __launch_bounds__(64) void radix_rowscan_kernel(int* __restrict__ his
   if (l == 0) dtot[blockIdx.x] = static_cast<int>(carry);
 }
 
+// Exclusive scan over the tiles of each digit's counts (a column of the
+// tile-major histogram); the column total goes to dtot[d].  A workgroup takes
+// 64 digits, one per lane, and its 16 waves a sixteenth of the tiles each:
+// every load reads 64 consecutive counts of one tile row.
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(1024) void radix_colscan_kernel(int* __restrict__ hist, int n_tt,
+                                                             int pass, int db,
+                                                             const int* __restrict__ counts,
+                                                             int* __restrict__ dtot) {
+  if (pass >= effective_passes(counts, db)) return;
+  __shared__ uint32_t wsum[kScanWaves][64];
+  const int nd = 1 << db;
+  const int w = threadIdx.x >> 6, l = lane();
+  const int dg = blockIdx.x * 64 + l;
+  const bool ok = dg < nd;
+  const int per = (n_tt + kScanWaves - 1) / kScanWaves;
+  const int t0 = min(n_tt, w * per), t1 = min(n_tt, t0 + per);
+  int* col = hist + (ok ? dg : 0);  // element t of this digit's column: col[t * nd]
+  constexpr int U = 8;
+  uint32_t s = 0;
+  for (int t = t0; t < t1; t += U) {
+    uint32_t c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      c[u] = (ok && t + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t + u) * nd]) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += c[u];
+  }
+  wsum[w][l] = s;
+  __syncthreads();
+  uint32_t run = 0;
+  for (int q = 0; q < w; ++q) run += wsum[q][l];
+  for (int t = t0; t < t1; t += U) {
+    uint32_t c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      c[u] = (ok && t + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t + u) * nd]) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ok && t + u < t1) col[static_cast<size_t>(t + u) * nd] = static_cast<int>(run);
+      run += c[u];
+    }
+  }
+  if (w == kScanWaves - 1 && ok) dtot[dg] = static_cast<int>(run);
+}
+
 // Stable scatter of one pass.  Wave w of a tile ranks its 256 consecutive
 // elements 64 at a time.  The last effective pass writes the task arrays
 // (and the keys only when write_keys: several passes, whose offsets come
@@ -294,11 +343,12 @@ __global__ __launch_bounds__(64) void radix_rowscan_kernel(int* __restrict__ his
 // g <= G (an empty group gets the start of the next non-empty one, groups
 // past the last get M), spread over the blocks.
 // fused != 0 (at most kFuseTiles tiles): hist holds the raw tile counts and
-// each block sums its digit rows itself; else hist holds the row-scanned
-// counts and dtot the row totals.
+// each block sums its digits' counts itself; else hist holds the scanned
+// counts and dtot the totals.  tmaj: the histogram's layout (as in
+// radix_up_kernel).
 __global__ __launch_bounds__(512) void radix_down_kernel(
     const int* __restrict__ kin, const int* __restrict__ vin, int M, int pass, int db, int n_tt,
-    const int* __restrict__ hist, const int* __restrict__ dtot, int fused,
+    int tmaj, const int* __restrict__ hist, const int* __restrict__ dtot, int fused,
     const int* __restrict__ counts, int* __restrict__ kout, int* __restrict__ vout,
     int write_keys, int K, const int32_t* __restrict__ expert_idx,
     const float* __restrict__ gate, int32_t* __restrict__ task_token,
@@ -341,16 +391,18 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
     v[j] = 0u;
     before[j] = 0u;
     if (dj < nd) {
-      const int* row = hist + static_cast<size_t>(dj) * n_tt;
+      // element t of this digit's counts: hist[base + t * step]
+      const size_t base = tmaj ? static_cast<size_t>(dj) : static_cast<size_t>(dj) * n_tt;
+      const size_t step = tmaj ? static_cast<size_t>(nd) : 1;
       if (fused) {
         for (int t = 0; t < n_tt; ++t) {
-          const uint32_t c = static_cast<uint32_t>(row[t]);
+          const uint32_t c = static_cast<uint32_t>(hist[base + t * step]);
           v[j] += c;
           before[j] += t < b ? c : 0u;
         }
       } else {
         v[j] = static_cast<uint32_t>(dtot[dj]);
-        before[j] = static_cast<uint32_t>(row[b]);
+        before[j] = static_cast<uint32_t>(hist[base + b * step]);
       }
     }
   }
@@ -463,16 +515,25 @@ static void launch_sort(const ScheduleWs& lay, int M, int N, int B, int window, 
   int* kb[2] = {key0, key1};
   int* vb[2] = {val0, val1};
   const int write_keys = lay.passes > 1 ? 1 : 0;
+  // 2048-digit histograms are kept tile-major (rows written and read whole by
+  // the blocks, columns scanned); narrower ones digit-major (measured: large
+  // 56.1 -> 52.9 us and mid 52.5 -> 46.4 us tile-major at 11 bits, but the
+  // 7-bit passes of the B = 1 sort 83 -> 87 us)
+  const int tmaj = lay.dbits >= 10 ? 1 : 0;
   for (int p = 0; p < lay.passes; ++p) {
     int* kin = kb[p & 1];
     const int* vin = p == 0 ? nullptr : vb[p & 1];
     hipLaunchKernelGGL(radix_up_kernel, dim3(lay.n_ttiles), dim3(512), 0, s, kin, expert_idx,
-                       rank, key0, M, N, B, window, p, lay.dbits, lay.n_ttiles, cnt, hist);
-    if (!fused)
+                       rank, key0, M, N, B, window, p, lay.dbits, lay.n_ttiles, tmaj, cnt, hist);
+    if (!fused && tmaj)
+      hipLaunchKernelGGL(radix_colscan_kernel, dim3(((1u << lay.dbits) + 63) / 64),
+                         dim3(64 * kScanWaves), 0, s, hist, lay.n_ttiles, p, lay.dbits, cnt,
+                         dtot);
+    else if (!fused)
       hipLaunchKernelGGL(radix_rowscan_kernel, dim3(1u << lay.dbits), dim3(64), 0, s, hist,
                          lay.n_ttiles, p, lay.dbits, cnt, dtot);
     hipLaunchKernelGGL(radix_down_kernel, dim3(lay.n_ttiles), dim3(512), 0, s, kin, vin, M, p,
-                       lay.dbits, lay.n_ttiles, hist, dtot, fused, cnt, kb[(p + 1) & 1],
+                       lay.dbits, lay.n_ttiles, tmaj, hist, dtot, fused, cnt, kb[(p + 1) & 1],
                        vb[(p + 1) & 1], write_keys, K, expert_idx, gate, task_token, task_expert,
                        task_gate, task_index, lay.max_groups, group_offsets);
   }
