@@ -7,7 +7,8 @@
 // Device pipeline, no host synchronisation (n_active and n_groups stay on
 // the device):
 //   1. clear a byte flag per expert, then mark every expert some task uses
-//      (read-before-write, so hot experts cause few stores);
+//      (plain byte stores of 1: without a read first the marking runs 3 us
+//      faster at large and no slower under Zipf routing);
 //   2. count flags per 4096-expert tile; each tile sums the counts of the
 //      tiles before it, scans its own flags and writes rank[e] (position
 //      among active experts) and the ascending active list;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void mark_kernel(const int32_t* __restrict__ i
   const int m = blockIdx.x * 256 + threadIdx.x;
   if (m >= M) return;
   const int e = idx[m];
-  if (static_cast<unsigned>(e) < static_cast<unsigned>(N) && flags[e] == 0) flags[e] = 1;
+  if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) flags[e] = 1;
 }
 
 // block-wide sum over 256 threads (4 waves); red: 4 ints of LDS
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
   const int eff = effective_passes(counts, db);
   if (pass >= eff) return;
   const bool last = pass == eff - 1;
-  __shared__ uint16_t wh[kSortWaves][kMaxDigits];
+  __shared__ __attribute__((aligned(16))) uint16_t wh[kSortWaves][kMaxDigits];
   __shared__ uint32_t goff[kMaxDigits];
   __shared__ uint32_t red[kSortWaves];
   const int tid = threadIdx.x, w = tid >> 6, l = lane();
@@ -383,8 +384,26 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
       gv[r] = valid ? gate[vv[r]] : 0.f;
     }
   }
-  for (int i = tid; i < kSortWaves * nd; i += 512) wh[i >> db][i & (nd - 1)] = 0;
+  if (nd >= 8) {  // 16-byte stores: nd / 8 per row of counts
+    const int n8 = nd >> 3;
+    for (int i = tid; i < kSortWaves * n8; i += 512)
+      reinterpret_cast<uint4*>(wh[i / n8])[i % n8] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    for (int i = tid; i < kSortWaves * nd; i += 512) wh[i >> db][i & (nd - 1)] = 0;
+  }
   uint32_t v[4], ex[4], before[4];
+  if (!fused && nd >= 4 && 4 * tid < nd) {  // four consecutive digits: 16-byte loads
+    const int4 t4 = *reinterpret_cast<const int4*>(dtot + 4 * tid);
+    v[0] = t4.x; v[1] = t4.y; v[2] = t4.z; v[3] = t4.w;
+    if (tmaj) {
+      const int4 h4 = *reinterpret_cast<const int4*>(hist + static_cast<size_t>(b) * nd + 4 * tid);
+      before[0] = h4.x; before[1] = h4.y; before[2] = h4.z; before[3] = h4.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        before[j] = static_cast<uint32_t>(hist[static_cast<size_t>(4 * tid + j) * n_tt + b]);
+    }
+  } else {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int dj = 4 * tid + j;
@@ -405,6 +424,7 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
         before[j] = static_cast<uint32_t>(hist[base + b * step]);
       }
     }
+  }
   }
   block_scan_digits(v, ex, red);
 #pragma unroll
