@@ -145,6 +145,8 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ f
   __shared__ int red[4];
   __shared__ int wpre[4];
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = lane();
+  // this tile's flags, loaded before the counts of the tiles before it
+  const uint4 v = reinterpret_cast<const uint4*>(flags + static_cast<size_t>(b) * kTile)[tid];
   int part = 0;
   if (tile_cnt) {
     for (int i = tid; i < b; i += 256) part += tile_cnt[i];
@@ -154,7 +156,6 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint8_t* __restrict__ f
           reinterpret_cast<const uint4*>(flags + static_cast<size_t>(i) * kTile)[tid]);
   }
   const int off = block_sum256(part, red);
-  const uint4 v = reinterpret_cast<const uint4*>(flags + static_cast<size_t>(b) * kTile)[tid];
   const int c = flag_count(v);
   const int inc = wave_prefix_sum(c);
   if (l == 63) wpre[w] = inc;
@@ -308,29 +309,47 @@ __global__ __launch_bounds__(1024) void radix_colscan_kernel(int* __restrict__ h
   const int per = (n_tt + kScanWaves - 1) / kScanWaves;
   const int t0 = min(n_tt, w * per), t1 = min(n_tt, t0 + per);
   int* col = hist + (ok ? dg : 0);  // element t of this digit's column: col[t * nd]
-  constexpr int U = 8;
-  uint32_t s = 0;
-  for (int t = t0; t < t1; t += U) {
-    uint32_t c[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      c[u] = (ok && t + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t + u) * nd]) : 0u;
-#pragma unroll
-    for (int u = 0; u < U; ++u) s += c[u];
-  }
-  wsum[w][l] = s;
-  __syncthreads();
+  constexpr int U = 8, KEEP = 32;
   uint32_t run = 0;
-  for (int q = 0; q < w; ++q) run += wsum[q][l];
-  for (int t = t0; t < t1; t += U) {
-    uint32_t c[U];
+  if (per <= KEEP) {  // the wave's counts stay in registers between the two steps
+    uint32_t c[KEEP];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      c[u] = (ok && t + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t + u) * nd]) : 0u;
+    for (int u = 0; u < KEEP; ++u)
+      c[u] = (ok && t0 + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t0 + u) * nd]) : 0u;
+    uint32_t s = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ok && t + u < t1) col[static_cast<size_t>(t + u) * nd] = static_cast<int>(run);
+    for (int u = 0; u < KEEP; ++u) s += c[u];
+    wsum[w][l] = s;
+    __syncthreads();
+    for (int q = 0; q < w; ++q) run += wsum[q][l];
+#pragma unroll
+    for (int u = 0; u < KEEP; ++u) {
+      if (ok && t0 + u < t1) col[static_cast<size_t>(t0 + u) * nd] = static_cast<int>(run);
       run += c[u];
+    }
+  } else {
+    uint32_t s = 0;
+    for (int t = t0; t < t1; t += U) {
+      uint32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        c[u] = (ok && t + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t + u) * nd]) : 0u;
+#pragma unroll
+      for (int u = 0; u < U; ++u) s += c[u];
+    }
+    wsum[w][l] = s;
+    __syncthreads();
+    for (int q = 0; q < w; ++q) run += wsum[q][l];
+    for (int t = t0; t < t1; t += U) {
+      uint32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        c[u] = (ok && t + u < t1) ? static_cast<uint32_t>(col[static_cast<size_t>(t + u) * nd]) : 0u;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ok && t + u < t1) col[static_cast<size_t>(t + u) * nd] = static_cast<int>(run);
+        run += c[u];
+      }
     }
   }
   if (w == kScanWaves - 1 && ok) dtot[dg] = static_cast<int>(run);
