@@ -469,22 +469,14 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
     lr[r] = wave_rank_digit(dg[r], valid, db, wh[w]);
   }
   __syncthreads();
-  // each digit's per-wave counts -> counts in the waves before
-  for (int i = tid; i < nd; i += 512) {
-    uint32_t run = 0;
-#pragma unroll
-    for (int q = 0; q < kSortWaves; ++q) {
-      const uint32_t c = wh[q][i];
-      wh[q][i] = static_cast<uint16_t>(run);
-      run += c;
-    }
-  }
-  __syncthreads();
 #pragma unroll
   for (int r = 0; r < kSortR; ++r) {
     const int i = base + r * 64 + l;
     if (i >= M) continue;
-    const uint32_t pos = goff[dg[r]] + wh[w][dg[r]] + lr[r];
+    // the element's digit in the waves before this one
+    uint32_t wb = 0;
+    for (int q = 0; q < w; ++q) wb += wh[q][dg[r]];
+    const uint32_t pos = goff[dg[r]] + wb + lr[r];
     if (pos >= static_cast<uint32_t>(M)) continue;  // unreachable when counts agree
     if (!last) {
       kout[pos] = kv[r];
