@@ -42,9 +42,10 @@ EXEC_KERNELS = {  # what one omni_atomic_forward call launches, per form
     "token": "omni_atomic_forward, token-centric: one kernel (token_multi_kernel from 8192 "
              "tokens, four tokens per wave; token lists read from the flattened selection the "
              "schedule carries)",
-    "grouped": "omni_atomic_forward, grouped: gf_count_kernel (hot set from the schedule), "
-               "gf_vt_kernel, gf_tile_kernel (per 64-token tile the hot experts as two MFMA "
-               "products, the cold tasks per task, y written once)",
+    "grouped": "omni_atomic_forward, grouped: gf_zero, gf_count, gf_level, gf_select (the hot "
+               "set from the sorted schedule), gf_pack (W_H, V_H^T in fragment order), "
+               "gf_cold_kernel (tasks outside the hot set, token by token; writes y), "
+               "gf_tile_kernel (per token tile the hot experts as two MFMA products, y += )",
 }
 
 
