@@ -7,7 +7,8 @@
 // the gate is the softmax over the K selected scores).
 //
 // One wave (64 lanes) serves one token end to end; four tokens per
-// workgroup, no cross-wave synchronisation.
+// workgroup, no cross-wave synchronisation.  For few tokens a second form
+// gives each token two waves (rows and columns), then one merges.
 //
 // Per axis the wave reads the logit row once, forms a = z - (m + ln sum
 // exp(z - m)) in float32, optionally stores it, and selects the k' largest a
@@ -263,7 +264,84 @@ struct TopkLds {
   int poff[68];
 };
 
+constexpr int kTopkPairTokens = 8192;  // below this many tokens, two waves per token
 constexpr int kStairItems = 5;  // ceil(280 / 64): |P| <= 280 for K, k' <= 64
+
+// The product merge of one token, by one wave, from the rank-ordered axis
+// lists in S (av, R: rows; bv, C: columns): the staircase cells, their top K,
+// the tie check against the first cell past the staircase in each row, the
+// exact walk for a tied token, then gates and outputs.
+__device__ __forceinline__ void product_merge(TopkLds& S, int kp, int K, int Nc, int t,
+                                              int32_t* __restrict__ expert_idx,
+                                              float* __restrict__ score,
+                                              float* __restrict__ gate,
+                                              int32_t* __restrict__ tie_flag) {
+  const int l = lane();
+  // ---- staircase P: row r contributes columns c < len_r = min(k', K / (r + 1))
+  const int len = (l < kp) ? min(kp, K / (l + 1)) : 0;
+  const int inc = wave_prefix_sum(len);
+  if (l < kp) S.poff[l + 1] = inc;
+  if (l == 0) S.poff[0] = 0;
+  const int P = __builtin_amdgcn_readlane(inc, 63);
+  wave_lds_fence();
+  uint32_t phi[kStairItems], plo[kStairItems];  // cell key = value key << 32 | ~expert
+#pragma unroll
+  for (int j = 0; j < kStairItems; ++j) {
+    const int p = l + 64 * j;
+    phi[j] = 0u;
+    plo[j] = 0u;
+    if (p < P) {
+      int lo = 0, hi = kp;  // largest r with poff[r] <= p
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (S.poff[mid] <= p) lo = mid; else hi = mid;
+      }
+      const int r = lo, c = p - S.poff[r];
+      phi[j] = fkey(S.av[r] + S.bv[c]);
+      plo[j] = ~(S.R[r] * static_cast<uint32_t>(Nc) + S.C[c]);
+    }
+  }
+  // K best cells by (value desc, expert asc): value threshold first; cells
+  // tied at it are split by a second search on ~expert among them.
+  KthSearch qm = kth_begin<kStairItems>(phi, K);
+  while (qm.bit >= 0) kth_step<kStairItems>(qm, phi, K);
+  uint64_t (&mb)[64] = S.buf[0];
+  top64_collect<kStairItems>(phi, plo, top64_finish<kStairItems>(phi, plo, K, qm), mb);
+  const uint64_t best = rank_sort64(mb, S.srt[0], K);
+  const uint32_t tau = static_cast<uint32_t>(__shfl(best, K - 1) >> 32);
+
+  // ---- a cell past the staircase can only tie at tau; check each row's first
+  bool extra = false;
+  if (l < kp && len < kp) extra = fkey(S.av[l] + S.bv[len]) >= tau;
+  const bool tie = __ballot(extra) != 0ull;
+  if (l == 0) tie_flag[t] = tie ? 1 : 0;
+  uint64_t out = best;
+  if (tie) {
+    // Exact top K over all k' x k' cells: K rounds, each taking the largest
+    // cell key below the previous round's.  Lane r owns row r; the columns
+    // are walked one at a time from LDS.  The axis values are the ones the
+    // selection above used.
+    const float av = (l < kp) ? S.av[l] : 0.f;
+    const uint32_t rbase = (l < kp) ? S.R[l] * static_cast<uint32_t>(Nc) : 0u;
+    uint64_t prev = ~0ull;
+    out = 0ull;
+    for (int k = 0; k < K; ++k) {
+      uint64_t cur = 0ull;
+      for (int c = 0; c < kp; ++c) {
+        const uint64_t key = sel_key(av + S.bv[c], rbase + S.C[c]);
+        if (l < kp && key < prev && key > cur) cur = key;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(cur, o);
+        cur = cur > u ? cur : u;
+      }
+      if (l == k) out = cur;
+      prev = cur;
+    }
+  }
+  write_outputs(out, t, K, expert_idx, score, gate);
+}
 
 // tie_flag[t] = 1 marks a token whose K-th score ties a cell past the
 // staircase (its outputs then come from the exact walk over all cells);
@@ -371,84 +449,104 @@ __global__ __launch_bounds__(256) void product_topk_kernel(
     col_sel[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(ck));
   }
 
-  // ---- staircase P: row r contributes columns c < len_r = min(k', K / (r + 1))
-  const int len = (l < kp) ? min(kp, K / (l + 1)) : 0;
-  const int inc = wave_prefix_sum(len);
-  if (l < kp) S.poff[l + 1] = inc;
-  if (l == 0) S.poff[0] = 0;
-  const int P = __builtin_amdgcn_readlane(inc, 63);
-  wave_lds_fence();
-  uint32_t phi[kStairItems], plo[kStairItems];  // cell key = value key << 32 | ~expert
-#pragma unroll
-  for (int j = 0; j < kStairItems; ++j) {
-    const int p = l + 64 * j;
-    phi[j] = 0u;
-    plo[j] = 0u;
-    if (p < P) {
-      int lo = 0, hi = kp;  // largest r with poff[r] <= p
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (S.poff[mid] <= p) lo = mid; else hi = mid;
-      }
-      const int r = lo, c = p - S.poff[r];
-      phi[j] = fkey(S.av[r] + S.bv[c]);
-      plo[j] = ~(S.R[r] * static_cast<uint32_t>(Nc) + S.C[c]);
-    }
-  }
-  // K best cells by (value desc, expert asc): value threshold first; cells
-  // tied at it are split by a second search on ~expert among them.
-  KthSearch qm = kth_begin<kStairItems>(phi, K);
-  while (qm.bit >= 0) kth_step<kStairItems>(qm, phi, K);
-  uint64_t (&mb)[64] = S.buf[0];
-  top64_collect<kStairItems>(phi, plo, top64_finish<kStairItems>(phi, plo, K, qm), mb);
-  const uint64_t best = rank_sort64(mb, S.srt[0], K);
-  const uint32_t tau = static_cast<uint32_t>(__shfl(best, K - 1) >> 32);
+  product_merge(S, kp, K, Nc, t, expert_idx, score, gate, tie_flag);
+}
 
-  // ---- a cell past the staircase can only tie at tau; check each row's first
-  bool extra = false;
-  if (l < kp && len < kp) extra = fkey(S.av[l] + S.bv[len]) >= tau;
-  const bool tie = __ballot(extra) != 0ull;
-  if (l == 0) tie_flag[t] = tie ? 1 : 0;
-  uint64_t out = best;
-  if (tie) {
-    // Exact top K over all k' x k' cells: K rounds, each taking the largest
-    // cell key below the previous round's.  Lane r owns row r; the columns
-    // are walked one at a time from LDS.  The axis values are the ones the
-    // selection above used.
-    const float av = (l < kp) ? S.av[l] : 0.f;
-    const uint32_t rbase = (l < kp) ? S.R[l] * static_cast<uint32_t>(Nc) : 0u;
-    uint64_t prev = ~0ull;
-    out = 0ull;
-    for (int k = 0; k < K; ++k) {
-      uint64_t cur = 0ull;
-      for (int c = 0; c < kp; ++c) {
-        const uint64_t key = sel_key(av + S.bv[c], rbase + S.C[c]);
-        if (l < kp && key < prev && key > cur) cur = key;
-      }
+// The same top-K with two waves per token, for few tokens: there the chain
+// of dependent steps of each token sets the time and most CUs are idle.
+// Wave 0 takes the rows, wave 1 the columns, each with the operations the
+// one-wave kernel applies to that axis, in the same order; then wave 0 merges.
+// The outputs are bit-identical to the one-wave kernel's (an axis whose
+// pre-filter overflows searches all its slots there only when the other axis
+// does too; both searches are exact and the rank sort orders distinct keys,
+// so the axis lists do not depend on it).
+template <int NI>
+__global__ __launch_bounds__(128) void product_topk_pair_kernel(
+    const float* __restrict__ Zr, const float* __restrict__ Zc, int L, int Nr, int Nc, int kp,
+    int K, int32_t* __restrict__ expert_idx, float* __restrict__ score,
+    float* __restrict__ gate, float* __restrict__ row_logp, float* __restrict__ col_logp,
+    int32_t* __restrict__ row_sel, int32_t* __restrict__ col_sel,
+    int32_t* __restrict__ tie_flag, float* __restrict__ lse_out) {
+  static_assert(NI <= 32, "32 slots per lane at most");
+  __shared__ TopkLds S;
+  const int w = threadIdx.x >> 6, l = lane();
+  const int t = blockIdx.x;
+  if (t >= L) return;  // the whole workgroup leaves together
+  const int n = w ? Nc : Nr;
+  const float* zrow = (w ? Zc : Zr) + static_cast<size_t>(t) * n;
+  float z[NI];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t u = __shfl_xor(cur, o);
-        cur = cur > u ? cur : u;
-      }
-      if (l == k) out = cur;
-      prev = cur;
-    }
+  for (int j = 0; j < NI; ++j) {
+    const int i = j * 64 + l;
+    z[j] = (i < n) ? zrow[i] : -INFINITY;
   }
-  write_outputs(out, t, K, expert_idx, score, gate);
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) m = fmaxf(m, z[j]);
+  m = wave_max(m);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    if (j * 64 + l < n) sum += __expf(z[j] - m);
+  sum = wave_sum(sum);
+  const float lse = m + __logf(sum);
+  if (l == 0) lse_out[2 * static_cast<size_t>(t) + w] = lse;
+  float* logp = w ? col_logp : row_logp;
+  uint32_t k[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = j * 64 + l;
+    const float a = z[j] - lse;
+    k[j] = (i < n) ? fkey(a) : 0u;
+    if (logp && i < n) logp[static_cast<size_t>(t) * n + i] = a;
+  }
+  uint32_t tp[2];
+  lane_top2<NI>(k, tp);
+  KthSearch f = kth_begin<2>(tp, kp);
+  while (f.bit >= 0) kth_step<2>(f, tp, kp);
+  if (wave_count_ge<NI>(k, f.prefix) <= 128) {
+    uint32_t h[2], lo[2];
+    axis_compact<NI>(k, f.prefix, S.cand[w], h, lo);
+    KthSearch q = kth_begin<2>(h, kp);
+    while (q.bit >= 0) kth_step<2>(q, h, kp);
+    top64_collect<2>(h, lo, top64_finish<2>(h, lo, kp, q), S.buf[w]);
+  } else {
+    KthSearch q = kth_begin<NI>(k, kp);
+    while (q.bit >= 0) kth_step<NI>(q, k, kp);
+    axis_collect<NI>(k, q, kp, S.buf[w]);
+  }
+  const uint64_t rk = rank_sort64(S.buf[w], S.srt[w], kp);
+  if (l < kp) {
+    (w ? S.bv : S.av)[l] = sel_val(rk);
+    (w ? S.C : S.R)[l] = sel_idx(rk);
+    (w ? col_sel : row_sel)[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(rk));
+  }
+  __syncthreads();
+  if (w != 0) return;
+  product_merge(S, kp, K, Nc, t, expert_idx, score, gate, tie_flag);
 }
 
 hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, int Nc, int kp,
                                int K, int32_t* expert_idx, float* score, float* gate,
                                float* row_logp, float* col_logp, int32_t* row_sel,
                                int32_t* col_sel, int32_t* tie_flag, float* lse,
-                               hipStream_t s) {
+                               hipStream_t s, int pair_below) {
   if (L == 0) return hipSuccess;
   const int n = Nr > Nc ? Nr : Nc;
-  const int grid = (L + 3) / 4;
-#define OMNI_TOPK(NI_)                                                                       \
-  hipLaunchKernelGGL(product_topk_kernel<NI_>, dim3(grid), dim3(256), 0, s, zr, zc, L, Nr, Nc, \
-                     kp, K, expert_idx, score, gate, row_logp, col_logp, row_sel, col_sel,     \
-                     tie_flag, lse)
+  // two waves per token below pair_below tokens (kTopkPairTokens unless the
+  // caller, a test, picks the form), four tokens per workgroup above
+  const bool pair = L < (pair_below < 0 ? kTopkPairTokens : pair_below);
+#define OMNI_TOPK(NI_)                                                                        \
+  do {                                                                                        \
+    if (pair)                                                                                 \
+      hipLaunchKernelGGL(product_topk_pair_kernel<NI_>, dim3(L), dim3(128), 0, s, zr, zc, L,  \
+                         Nr, Nc, kp, K, expert_idx, score, gate, row_logp, col_logp, row_sel, \
+                         col_sel, tie_flag, lse);                                             \
+    else                                                                                      \
+      hipLaunchKernelGGL(product_topk_kernel<NI_>, dim3((L + 3) / 4), dim3(256), 0, s, zr,    \
+                         zc, L, Nr, Nc, kp, K, expert_idx, score, gate, row_logp, col_logp,   \
+                         row_sel, col_sel, tie_flag, lse);                                    \
+  } while (0)
   if (n <= 64) OMNI_TOPK(1);
   else if (n <= 128) OMNI_TOPK(2);
   else if (n <= 256) OMNI_TOPK(4);
