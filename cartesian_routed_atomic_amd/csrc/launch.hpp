@@ -33,7 +33,7 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
                                int K, int32_t* expert_idx, float* score, float* gate,
                                float* row_logp, float* col_logp, int32_t* row_sel,
                                int32_t* col_sel, int32_t* tie_flag, float* lse,
-                               hipStream_t s, int pair_below = -1);  // -1: the library's rule
+                               hipStream_t s);
 
 // schedule.hip
 struct ScheduleWs {

@@ -6,16 +6,15 @@
 // formed) and "Expert-Centric Scheduling" (every decision carries a weight;
 // the gate is the softmax over the K selected scores).
 //
-// One wave (64 lanes) serves one token end to end; four tokens per
-// workgroup, no cross-wave synchronisation.  For few tokens a second form
-// gives each token two waves (rows and columns), then one merges.
+// Two waves (64 lanes each) serve one token: one per axis, then one merges.
 //
 // Per axis the wave reads the logit row once, forms a = z - (m + ln sum
 // exp(z - m)) in float32, optionally stores it, and selects the k' largest a
 // with an MSB-first radix select over 32-bit order-preserving value keys
 // (bits shared by all candidates are skipped; ties at the threshold value
 // are taken in index order, which is the lane/slot order of the row).  The
-// winners are sorted by a 64-lane bitonic sort on (value key << 32 | ~index).
+// winners are put in (value key << 32 | ~index) order by a rank sort: each
+// lane counts the keys above its own.
 //
 // Product merge.  With rank-ordered axis lists R (rows) and C (columns),
 // S(r, c) = fl32(a[R_r] + b[C_c]) is non-increasing in r and in c (float
@@ -264,7 +263,6 @@ struct TopkLds {
   int poff[68];
 };
 
-constexpr int kTopkPairTokens = 8192;  // below this many tokens, two waves per token
 constexpr int kStairItems = 5;  // ceil(280 / 64): |P| <= 280 for K, k' <= 64
 
 // The product merge of one token, by one wave, from the rank-ordered axis
@@ -343,125 +341,16 @@ __device__ __forceinline__ void product_merge(TopkLds& S, int kp, int K, int Nc,
   write_outputs(out, t, K, expert_idx, score, gate);
 }
 
+// Two waves per token: wave 0 takes the rows, wave 1 the columns (log-sum-exp,
+// value keys, pre-filter, exact top-k', rank order), then wave 0 merges.  Per
+// token the work is a chain of dependent steps (wave reductions, ballots, LDS
+// round trips); splitting the two axes over two waves halves the axis part of
+// that chain and doubles the waves that hide each other's latency.
 // tie_flag[t] = 1 marks a token whose K-th score ties a cell past the
 // staircase (its outputs then come from the exact walk over all cells);
 // lse[2t], lse[2t+1] keep the row / column normalisers.
 template <int NI>
-__global__ __launch_bounds__(256) void product_topk_kernel(
-    const float* __restrict__ Zr, const float* __restrict__ Zc, int L, int Nr, int Nc, int kp,
-    int K, int32_t* __restrict__ expert_idx, float* __restrict__ score,
-    float* __restrict__ gate, float* __restrict__ row_logp, float* __restrict__ col_logp,
-    int32_t* __restrict__ row_sel, int32_t* __restrict__ col_sel,
-    int32_t* __restrict__ tie_flag, float* __restrict__ lse_out) {
-  static_assert(NI <= 32, "32 slots per lane at most");
-  __shared__ TopkLds smem[4];
-  const int w = threadIdx.x >> 6, l = lane();
-  const int t = blockIdx.x * 4 + w;
-  if (t >= L) return;  // the whole wave leaves together
-  TopkLds& S = smem[w];
-
-  // ---- both logit rows, then both log-softmax normalisers
-  const float* zr_row = Zr + static_cast<size_t>(t) * Nr;
-  const float* zc_row = Zc + static_cast<size_t>(t) * Nc;
-  float zr[NI], zc[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int i = j * 64 + l;
-    zr[j] = (i < Nr) ? zr_row[i] : -INFINITY;
-    zc[j] = (i < Nc) ? zc_row[i] : -INFINITY;
-  }
-  float mr = -INFINITY, mc = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    mr = fmaxf(mr, zr[j]);
-    mc = fmaxf(mc, zc[j]);
-  }
-  mr = wave_max(mr);
-  mc = wave_max(mc);
-  float sr = 0.f, sc = 0.f;
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    if (j * 64 + l < Nr) sr += __expf(zr[j] - mr);
-    if (j * 64 + l < Nc) sc += __expf(zc[j] - mc);
-  }
-  sr = wave_sum(sr);
-  sc = wave_sum(sc);
-  const float lse_r = mr + __logf(sr), lse_c = mc + __logf(sc);
-  if (l == 0) {
-    lse_out[2 * static_cast<size_t>(t)] = lse_r;
-    lse_out[2 * static_cast<size_t>(t) + 1] = lse_c;
-  }
-  // value keys of a = z - lse (0 = no item); optional log-probability rows
-  uint32_t kr[NI], kc[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int i = j * 64 + l;
-    const float ar = zr[j] - lse_r, ac = zc[j] - lse_c;
-    kr[j] = (i < Nr) ? fkey(ar) : 0u;
-    kc[j] = (i < Nc) ? fkey(ac) : 0u;
-    if (row_logp && i < Nr) row_logp[static_cast<size_t>(t) * Nr + i] = ar;
-    if (col_logp && i < Nc) col_logp[static_cast<size_t>(t) * Nc + i] = ac;
-  }
-
-  // ---- the k' best rows and columns.  Pre-filter: v = the k'-th largest of
-  // the per-lane top-2 keys is a lower bound of the k'-th largest key (k' keys
-  // are >= v), and for Gaussian-like rows only ~70 keys reach it.  Those are
-  // compacted two per lane and searched exactly; more than 128 falls back to
-  // the search over all slots.  Both axes advance together.
-  uint32_t tr[2], tc[2];
-  lane_top2<NI>(kr, tr);
-  lane_top2<NI>(kc, tc);
-  KthSearch fr = kth_begin<2>(tr, kp), fc = kth_begin<2>(tc, kp);
-  while (fr.bit >= 0 || fc.bit >= 0) {
-    kth_step<2>(fr, tr, kp);
-    kth_step<2>(fc, tc, kp);
-  }
-  const bool cr = wave_count_ge<NI>(kr, fr.prefix) <= 128;
-  const bool cc = wave_count_ge<NI>(kc, fc.prefix) <= 128;
-  if (cr && cc) {
-    uint32_t hr[2], lr[2], hc[2], lc[2];
-    axis_compact<NI>(kr, fr.prefix, S.cand[0], hr, lr);
-    axis_compact<NI>(kc, fc.prefix, S.cand[1], hc, lc);
-    KthSearch qr = kth_begin<2>(hr, kp), qc = kth_begin<2>(hc, kp);
-    while (qr.bit >= 0 || qc.bit >= 0) {
-      kth_step<2>(qr, hr, kp);
-      kth_step<2>(qc, hc, kp);
-    }
-    top64_collect<2>(hr, lr, top64_finish<2>(hr, lr, kp, qr), S.buf[0]);
-    top64_collect<2>(hc, lc, top64_finish<2>(hc, lc, kp, qc), S.buf[1]);
-  } else {  // rare: search all slots
-    KthSearch qr = kth_begin<NI>(kr, kp), qc = kth_begin<NI>(kc, kp);
-    while (qr.bit >= 0 || qc.bit >= 0) {
-      kth_step<NI>(qr, kr, kp);
-      kth_step<NI>(qc, kc, kp);
-    }
-    axis_collect<NI>(kr, qr, kp, S.buf[0]);
-    axis_collect<NI>(kc, qc, kp, S.buf[1]);
-  }
-  const uint64_t rk = rank_sort64(S.buf[0], S.srt[0], kp);
-  const uint64_t ck = rank_sort64(S.buf[1], S.srt[1], kp);
-  if (l < kp) {
-    S.av[l] = sel_val(rk);
-    S.R[l] = sel_idx(rk);
-    S.bv[l] = sel_val(ck);
-    S.C[l] = sel_idx(ck);
-    row_sel[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(rk));
-    col_sel[static_cast<size_t>(t) * kp + l] = static_cast<int32_t>(sel_idx(ck));
-  }
-
-  product_merge(S, kp, K, Nc, t, expert_idx, score, gate, tie_flag);
-}
-
-// The same top-K with two waves per token, for few tokens: there the chain
-// of dependent steps of each token sets the time and most CUs are idle.
-// Wave 0 takes the rows, wave 1 the columns, each with the operations the
-// one-wave kernel applies to that axis, in the same order; then wave 0 merges.
-// The outputs are bit-identical to the one-wave kernel's (an axis whose
-// pre-filter overflows searches all its slots there only when the other axis
-// does too; both searches are exact and the rank sort orders distinct keys,
-// so the axis lists do not depend on it).
-template <int NI>
-__global__ __launch_bounds__(128) void product_topk_pair_kernel(
+__global__ __launch_bounds__(128) void product_topk_kernel(
     const float* __restrict__ Zr, const float* __restrict__ Zc, int L, int Nr, int Nc, int kp,
     int K, int32_t* __restrict__ expert_idx, float* __restrict__ score,
     float* __restrict__ gate, float* __restrict__ row_logp, float* __restrict__ col_logp,
@@ -500,6 +389,11 @@ __global__ __launch_bounds__(128) void product_topk_pair_kernel(
     k[j] = (i < n) ? fkey(a) : 0u;
     if (logp && i < n) logp[static_cast<size_t>(t) * n + i] = a;
   }
+  // The k' best lines of this axis.  Pre-filter: v = the k'-th largest of the
+  // per-lane top-2 keys is a lower bound of the k'-th largest key (k' keys
+  // are >= v), and for Gaussian-like rows only ~70 keys reach it.  Those are
+  // compacted two per lane and searched exactly; more than 128 fall back to
+  // the search over all slots (both searches are exact).
   uint32_t tp[2];
   lane_top2<NI>(k, tp);
   KthSearch f = kth_begin<2>(tp, kp);
@@ -530,23 +424,13 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
                                int K, int32_t* expert_idx, float* score, float* gate,
                                float* row_logp, float* col_logp, int32_t* row_sel,
                                int32_t* col_sel, int32_t* tie_flag, float* lse,
-                               hipStream_t s, int pair_below) {
+                               hipStream_t s) {
   if (L == 0) return hipSuccess;
   const int n = Nr > Nc ? Nr : Nc;
-  // two waves per token below pair_below tokens (kTopkPairTokens unless the
-  // caller, a test, picks the form), four tokens per workgroup above
-  const bool pair = L < (pair_below < 0 ? kTopkPairTokens : pair_below);
-#define OMNI_TOPK(NI_)                                                                        \
-  do {                                                                                        \
-    if (pair)                                                                                 \
-      hipLaunchKernelGGL(product_topk_pair_kernel<NI_>, dim3(L), dim3(128), 0, s, zr, zc, L,  \
-                         Nr, Nc, kp, K, expert_idx, score, gate, row_logp, col_logp, row_sel, \
-                         col_sel, tie_flag, lse);                                             \
-    else                                                                                      \
-      hipLaunchKernelGGL(product_topk_kernel<NI_>, dim3((L + 3) / 4), dim3(256), 0, s, zr,    \
-                         zc, L, Nr, Nc, kp, K, expert_idx, score, gate, row_logp, col_logp,   \
-                         row_sel, col_sel, tie_flag, lse);                                    \
-  } while (0)
+#define OMNI_TOPK(NI_)                                                                      \
+  hipLaunchKernelGGL(product_topk_kernel<NI_>, dim3(L), dim3(128), 0, s, zr, zc, L, Nr, Nc, \
+                     kp, K, expert_idx, score, gate, row_logp, col_logp, row_sel, col_sel,   \
+                     tie_flag, lse)
   if (n <= 64) OMNI_TOPK(1);
   else if (n <= 128) OMNI_TOPK(2);
   else if (n <= 256) OMNI_TOPK(4);

@@ -2,8 +2,7 @@
 // compiled for the host against the wave model in hip/hip_runtime.h) on one
 // input file and writes every output, for tests/test_host_sim_topk.py.
 //
-//   topk_sim IN OUT LDS_FILL LOG_ULPS FORM
-//   FORM: 1 = one wave per token (four per workgroup), 2 = two waves per token
+//   topk_sim IN OUT LDS_FILL LOG_ULPS
 //   IN:  int32 L, Nr, Nc, kprime, K; float32 row_logits [L, Nr]; col_logits [L, Nc]
 //   OUT: int32 expert_idx [L, K]; float32 score, gate [L, K];
 //        float32 row_logp [L, Nr], col_logp [L, Nc]; int32 row_sel, col_sel [L, k'];
@@ -25,12 +24,10 @@ template <class T> static void wr(FILE* f, const std::vector<T>& v) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 6) {
-    std::fprintf(stderr, "usage: topk_sim IN OUT LDS_FILL LOG_ULPS FORM\n");
+  if (argc != 5) {
+    std::fprintf(stderr, "usage: topk_sim IN OUT LDS_FILL LOG_ULPS\n");
     return 2;
   }
-  const int form = std::atoi(argv[5]);
-  if (form != 1 && form != 2) sim::fail("FORM must be 1 or 2");
   sim::g_lds_fill = static_cast<unsigned char>(std::atoi(argv[3]));
   sim::g_log_ulps = std::atoi(argv[4]);
   FILE* f = std::fopen(argv[1], "rb");
@@ -50,8 +47,7 @@ int main(int argc, char** argv) {
   const hipError_t e = omni::launch_product_topk(zr.data(), zc.data(), L, Nr, Nc, kp, K,
                                                  idx.data(), score.data(), gate.data(), ra.data(),
                                                  cb.data(), rsel.data(), csel.data(), tie.data(),
-                                                 lse.data(), nullptr,
-                                                 form == 2 ? 1 << 30 : 0);
+                                                 lse.data(), nullptr);
   if (e != hipSuccess) sim::fail("launch_product_topk returned an error");
   FILE* o = std::fopen(argv[2], "wb");
   if (!o) sim::fail("cannot open output");
