@@ -261,9 +261,11 @@ struct TopkLds {
   uint32_t R[64];
   uint32_t C[64];
   int poff[68];
+  uint8_t rowstart[320];  // 1 at the first staircase cell of each row
 };
 
 constexpr int kStairItems = 5;  // ceil(280 / 64): |P| <= 280 for K, k' <= 64
+static_assert(kStairItems * 64 <= 320, "one rowstart byte per staircase slot");
 
 // The product merge of one token, by one wave, from the rank-ordered axis
 // lists in S (av, R: rows; bv, C: columns): the staircase cells, their top K,
@@ -281,20 +283,29 @@ __device__ __forceinline__ void product_merge(TopkLds& S, int kp, int K, int Nc,
   if (l < kp) S.poff[l + 1] = inc;
   if (l == 0) S.poff[0] = 0;
   const int P = __builtin_amdgcn_readlane(inc, 63);
+  // The row of cell p is the number of rows that begin at or before p, less
+  // one (rows with cells begin at distinct offsets; empty rows come last):
+  // each row marks its first cell, and the lanes of a block of 64 cells count
+  // the marks with one ballot.
+  uint32_t* rs = reinterpret_cast<uint32_t*>(S.rowstart);
+  rs[l] = 0u;
+  if (l < 320 / 4 - 64) rs[64 + l] = 0u;
+  wave_lds_fence();
+  if (len > 0) S.rowstart[inc - len] = 1;
   wave_lds_fence();
   uint32_t phi[kStairItems], plo[kStairItems];  // cell key = value key << 32 | ~expert
+  int rows_before = 0;  // rows that begin in the blocks before this one
 #pragma unroll
   for (int j = 0; j < kStairItems; ++j) {
     const int p = l + 64 * j;
+    const bool first = p < P && S.rowstart[p] != 0;
+    const uint64_t m = __ballot(first);
+    const int r = rows_before + mbcnt(m) + (first ? 1 : 0) - 1;
+    rows_before += __popcll(m);
     phi[j] = 0u;
     plo[j] = 0u;
     if (p < P) {
-      int lo = 0, hi = kp;  // largest r with poff[r] <= p
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (S.poff[mid] <= p) lo = mid; else hi = mid;
-      }
-      const int r = lo, c = p - S.poff[r];
+      const int c = p - S.poff[r];
       phi[j] = fkey(S.av[r] + S.bv[c]);
       plo[j] = ~(S.R[r] * static_cast<uint32_t>(Nc) + S.C[c]);
     }
