@@ -193,9 +193,10 @@ __device__ __forceinline__ void top64_collect(const uint32_t (&hi)[NI], const ui
 
 // Items of one axis with value key >= v, compacted in index order into
 // cand[0..128) as (key << 32 | ~index), zero-padded; returns them two per
-// lane (cand[l], cand[64 + l]).  Requires at most 128 such items.
+// lane (cand[l], cand[64 + l]) and true, or false (hi, lo unset) when more
+// than 128 items pass (then only the first 128 are written).
 template <int NI>
-__device__ __forceinline__ void axis_compact(const uint32_t (&vk)[NI], uint32_t v,
+__device__ __forceinline__ bool axis_compact(const uint32_t (&vk)[NI], uint32_t v,
                                              uint64_t (&cand)[128],
                                              uint32_t (&hi)[2], uint32_t (&lo)[2]) {
   const int l = lane();
@@ -207,17 +208,20 @@ __device__ __forceinline__ void axis_compact(const uint32_t (&vk)[NI], uint32_t 
   for (int j = 0; j < NI; ++j) {
     const bool in = vk[j] >= v && vk[j] != 0u;
     const uint64_t m = __ballot(in);
-    if (in) cand[base + mbcnt(m)] = (static_cast<uint64_t>(vk[j]) << 32) |
-                                    static_cast<uint32_t>(~(j * 64 + l));
+    const int at = base + mbcnt(m);
+    if (in && at < 128)
+      cand[at] = (static_cast<uint64_t>(vk[j]) << 32) | static_cast<uint32_t>(~(j * 64 + l));
     base += __popcll(m);
   }
   wave_lds_fence();
+  if (base > 128) return false;
   const uint64_t a = cand[l], b = cand[64 + l];
   hi[0] = static_cast<uint32_t>(a >> 32);
   lo[0] = static_cast<uint32_t>(a);
   hi[1] = static_cast<uint32_t>(b >> 32);
   lo[1] = static_cast<uint32_t>(b);
   wave_lds_fence();
+  return true;
 }
 
 // Per-lane two largest keys (0 = empty).
@@ -359,8 +363,9 @@ __device__ __forceinline__ void product_merge(TopkLds& S, int kp, int K, int Nc,
 // that chain and doubles the waves that hide each other's latency.
 // tie_flag[t] = 1 marks a token whose K-th score ties a cell past the
 // staircase (its outputs then come from the exact walk over all cells);
-// lse[2t], lse[2t+1] keep the row / column normalisers.
-template <int NI>
+// lse[2t], lse[2t+1] keep the row / column normalisers.  FULL: both axes
+// have exactly NI * 64 lines (every slot holds a line; no per-slot guards).
+template <int NI, bool FULL>
 __global__ __launch_bounds__(128) void product_topk_kernel(
     const float* __restrict__ Zr, const float* __restrict__ Zc, int L, int Nr, int Nc, int kp,
     int K, int32_t* __restrict__ expert_idx, float* __restrict__ score,
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(128) void product_topk_kernel(
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int i = j * 64 + l;
-    z[j] = (i < n) ? zrow[i] : -INFINITY;
+    z[j] = (FULL || i < n) ? zrow[i] : -INFINITY;
   }
   float m = -INFINITY;
 #pragma unroll
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(128) void product_topk_kernel(
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < NI; ++j)
-    if (j * 64 + l < n) sum += __expf(z[j] - m);
+    if (FULL || j * 64 + l < n) sum += __expf(z[j] - m);
   sum = wave_sum(sum);
   const float lse = m + __logf(sum);
   if (l == 0) lse_out[2 * static_cast<size_t>(t) + w] = lse;
@@ -397,8 +402,8 @@ __global__ __launch_bounds__(128) void product_topk_kernel(
   for (int j = 0; j < NI; ++j) {
     const int i = j * 64 + l;
     const float a = z[j] - lse;
-    k[j] = (i < n) ? fkey(a) : 0u;
-    if (logp && i < n) logp[static_cast<size_t>(t) * n + i] = a;
+    k[j] = (FULL || i < n) ? fkey(a) : 0u;
+    if (logp && (FULL || i < n)) logp[static_cast<size_t>(t) * n + i] = a;
   }
   // The k' best lines of this axis.  Pre-filter: v = the k'-th largest of the
   // per-lane top-2 keys is a lower bound of the k'-th largest key (k' keys
@@ -409,9 +414,8 @@ __global__ __launch_bounds__(128) void product_topk_kernel(
   lane_top2<NI>(k, tp);
   KthSearch f = kth_begin<2>(tp, kp);
   while (f.bit >= 0) kth_step<2>(f, tp, kp);
-  if (wave_count_ge<NI>(k, f.prefix) <= 128) {
-    uint32_t h[2], lo[2];
-    axis_compact<NI>(k, f.prefix, S.cand[w], h, lo);
+  uint32_t h[2], lo[2];
+  if (axis_compact<NI>(k, f.prefix, S.cand[w], h, lo)) {
     KthSearch q = kth_begin<2>(h, kp);
     while (q.bit >= 0) kth_step<2>(q, h, kp);
     top64_collect<2>(h, lo, top64_finish<2>(h, lo, kp, q), S.buf[w]);
@@ -438,10 +442,17 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
                                hipStream_t s) {
   if (L == 0) return hipSuccess;
   const int n = Nr > Nc ? Nr : Nc;
-#define OMNI_TOPK(NI_)                                                                      \
-  hipLaunchKernelGGL(product_topk_kernel<NI_>, dim3(L), dim3(128), 0, s, zr, zc, L, Nr, Nc, \
-                     kp, K, expert_idx, score, gate, row_logp, col_logp, row_sel, col_sel,   \
-                     tie_flag, lse)
+#define OMNI_TOPK_F(NI_, F_)                                                                   \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(product_topk_kernel<NI_, F_>), dim3(L), dim3(128), 0, s,  \
+                     zr, zc, L, Nr, Nc, kp, K, expert_idx, score, gate, row_logp, col_logp,    \
+                     row_sel, col_sel, tie_flag, lse)
+#define OMNI_TOPK(NI_)                                 \
+  do {                                                 \
+    if (Nr == (NI_) * 64 && Nc == (NI_) * 64)          \
+      OMNI_TOPK_F(NI_, true);                          \
+    else                                               \
+      OMNI_TOPK_F(NI_, false);                         \
+  } while (0)
   if (n <= 64) OMNI_TOPK(1);
   else if (n <= 128) OMNI_TOPK(2);
   else if (n <= 256) OMNI_TOPK(4);
@@ -449,6 +460,7 @@ hipError_t launch_product_topk(const float* zr, const float* zc, int L, int Nr, 
   else if (n <= 1024) OMNI_TOPK(16);
   else OMNI_TOPK(32);
 #undef OMNI_TOPK
+#undef OMNI_TOPK_F
   return hipGetLastError();
 }
 
