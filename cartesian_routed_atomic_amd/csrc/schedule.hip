@@ -422,6 +422,37 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
       for (int j = 0; j < 4; ++j)
         before[j] = static_cast<uint32_t>(hist[static_cast<size_t>(4 * tid + j) * n_tt + b]);
     }
+  } else if (fused) {
+    // every tile's count of this thread's four digits (element t of digit
+    // dj's counts is hist[base + t * step]), four tiles' loads in flight
+    // before they are summed: a loop that summed each load as it came took
+    // one memory latency per tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = 0u;
+      before[j] = 0u;
+    }
+    for (int t0 = 0; t0 < n_tt; t0 += 4) {
+      uint32_t c[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dj = 4 * tid + j;
+        const size_t base = tmaj ? static_cast<size_t>(dj) : static_cast<size_t>(dj) * n_tt;
+        const size_t step = tmaj ? static_cast<size_t>(nd) : 1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = t0 + u;
+          c[j][u] = (dj < nd && t < n_tt) ? static_cast<uint32_t>(hist[base + t * step]) : 0u;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[j] += c[j][u];
+          before[j] += t0 + u < b ? c[j][u] : 0u;
+        }
+    }
   } else {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -429,19 +460,10 @@ __global__ __launch_bounds__(512) void radix_down_kernel(
     v[j] = 0u;
     before[j] = 0u;
     if (dj < nd) {
-      // element t of this digit's counts: hist[base + t * step]
       const size_t base = tmaj ? static_cast<size_t>(dj) : static_cast<size_t>(dj) * n_tt;
       const size_t step = tmaj ? static_cast<size_t>(nd) : 1;
-      if (fused) {
-        for (int t = 0; t < n_tt; ++t) {
-          const uint32_t c = static_cast<uint32_t>(hist[base + t * step]);
-          v[j] += c;
-          before[j] += t < b ? c : 0u;
-        }
-      } else {
-        v[j] = static_cast<uint32_t>(dtot[dj]);
-        before[j] = static_cast<uint32_t>(hist[base + b * step]);
-      }
+      v[j] = static_cast<uint32_t>(dtot[dj]);
+      before[j] = static_cast<uint32_t>(hist[base + b * step]);
     }
   }
   }
